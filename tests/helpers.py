@@ -1,0 +1,63 @@
+"""Glue between the synthetic inputs, the oracle and the comparisons.
+
+Tolerances (from the workload definition): ids bit-exact, routing weights to
+1e-6 relative, every BF16 output row within 2e-2 x the RMS of the oracle's
+row (max |err| <= 2e-2 * rms).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+
+ROW_RTOL = 2e-2
+WEIGHT_RTOL = 1e-6
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    """float64 host copy of a tensor of any dtype (bf16/f32 values exact)."""
+    if t.dtype == torch.uint8:
+        return t.cpu().numpy()
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def expert_fn(inp):
+    """Lazily copies one expert's weights and scales to the host."""
+    def get(e: int):
+        return (inp.w13[e].cpu().numpy(), host(inp.w13_scale[e]),
+                inp.w2[e].cpu().numpy(), host(inp.w2_scale[e]))
+    return get
+
+
+def oracle_layer(inp, **over):
+    s = inp.shape
+    kw = dict(top_k=s.top_k, routed_scale=s.routed_scale, limit=s.limit,
+              ue8m0_act=s.ue8m0_act, inter=s.inter)
+    kw.update(over)
+    return oracle.moe_decode(host(inp.x), host(inp.logits), host(inp.bias), expert_fn(inp), **kw)
+
+
+def oracle_shared(inp):
+    s = inp.shape
+    return oracle.shared_expert(host(inp.x), inp.sw13.cpu().numpy(), host(inp.sw13_scale),
+                                inp.sw2.cpu().numpy(), host(inp.sw2_scale),
+                                limit=s.shared_limit, ue8m0_act=True)
+
+
+def row_errors(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """max |got - ref| / rms(ref) per row (rows of all-zero ref compare to 0)."""
+    got = np.asarray(got, np.float64).reshape(ref.shape[0], -1)
+    ref = np.asarray(ref, np.float64).reshape(ref.shape[0], -1)
+    rms = np.sqrt(np.mean(ref * ref, axis=1))
+    err = np.max(np.abs(got - ref), axis=1)
+    out = np.where(rms > 0, err / np.where(rms > 0, rms, 1), np.where(err > 0, np.inf, 0.0))
+    return out
+
+
+def assert_rows_close(got, ref, rtol=ROW_RTOL, what="rows"):
+    e = row_errors(got, ref)
+    bad = np.nonzero(e > rtol)[0]
+    assert bad.size == 0, f"{what}: {bad.size} rows over {rtol} x rms (worst {e.max():.3g} at row {int(e.argmax())})"
+    return float(e.max()) if e.size else 0.0
