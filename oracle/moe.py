@@ -88,8 +88,8 @@ def ue8m0_round_up(s: np.ndarray) -> np.ndarray:
 def quantize_blocks(v, ue8m0: bool, reciprocal: bool):
     """FP8 per 128-element block of each row of v (binary32 values).
 
-    amax = max(1e-10, max |v|); s = FP32(amax / 448); with ue8m0, s rounds up
-    to a power of two; then either q = e4m3(FP32(v * FP32(1 / s)))
+    amax = max(1e-10, max |v|); s = FP32(amax / 448); with ue8m0, s is floored
+    at 1e-10 and then rounded up to a power of two; then either q = e4m3(FP32(v * FP32(1 / s)))
     (reciprocal=True: the activation quantiser of the "mega_moe" epilogue and
     of "shared_expert" _GateUpKernel/_DownKernel, via _group_scale) or
     q = e4m3(FP32(v / s)) (reciprocal=False: "mega_moe" hidden_block).
@@ -103,7 +103,7 @@ def quantize_blocks(v, ue8m0: bool, reciprocal: bool):
     amax = np.maximum(np.abs(b).max(axis=2), AMAX_FLOOR)
     s = f32(amax / FP8_MAX)
     if ue8m0:
-        s = ue8m0_round_up(s)
+        s = ue8m0_round_up(np.maximum(s, AMAX_FLOOR))
     if reciprocal:
         scaled = f32(b * f32(1.0 / s)[..., None])
     else:

@@ -33,11 +33,18 @@ def test_quant_zero_rows():
     q, s = quantize_blocks(np.zeros((2, 256)), ue8m0=False, reciprocal=True)
     assert np.all(q == 0)
     assert np.all(s == f32(f32(1e-10) / 448.0))
+    # with UE8M0 the scale is floored at 1e-10 before rounding up to a power of
+    # two: 1e-10 lies in [2**-34, 2**-33), so the scale is 2**-33
     q, s = quantize_blocks(np.zeros((1, 128)), ue8m0=True, reciprocal=True)
     assert np.all(q == 0)
-    # the smallest power of two >= f32(1e-10)/448
-    t = float(f32(f32(1e-10) / 448.0))
-    assert s[0, 0] >= t and s[0, 0] / 2 < t
+    assert s[0, 0] == 2.0**-33
+    # a block with amax just under 448e-10 is floored too; one well above is not
+    x = np.zeros((2, 128))
+    x[0, 3] = 1e-9
+    x[1, 3] = 1e-3
+    q, s = quantize_blocks(x, ue8m0=True, reciprocal=True)
+    assert s[0, 0] == 2.0**-33
+    assert s[1, 0] == 2.0**-18   # 1e-3 / 448 = 2.23e-6 in [2**-19, 2**-18)
 
 
 def test_quant_error_bound_and_amax():
