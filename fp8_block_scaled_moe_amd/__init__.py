@@ -1,0 +1,16 @@
+"""Routed-expert FP8 block-scaled MoE decode for MI355X (gfx950).
+
+The compute path is the HIP library libmoe_decode.so (C ABI in
+include/moe_decode.h); this package is its thin Python binding. Build the
+library with `python -m fp8_block_scaled_moe_amd.build`.
+"""
+
+from ._capi import (  # noqa: F401
+    MoeDecode,
+    MoeDecodeConfig,
+    MoeDecodeError,
+    debug_codec,
+    error_string,
+    header_functions,
+    lib,
+)

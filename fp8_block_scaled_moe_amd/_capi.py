@@ -1,0 +1,256 @@
+"""ctypes binding of libmoe_decode.so (include/moe_decode.h).
+
+Argument marshalling only: every step of the routed-expert path runs in the
+library's HIP kernels. PyTorch provides device memory and the stream.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Sequence
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_decode.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "moe_decode.h")
+
+OK = 0
+ERR_INVALID_ARG = -1
+ERR_UNSUPPORTED = -2
+ERR_TOO_MANY_TOKENS = -3
+ERR_HIP = -4
+ERR_OUT_OF_MEMORY = -5
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+SCALES_F32 = 0
+SCALES_UE8M0_PACKED = 1
+GEMM_PATHS = {"auto": 0, "valu": 1, "mfma": 2}
+
+STAGES = {
+    "ctrl": 0, "uexp": 1, "uoff": 2, "ucnt": 3, "routes": 4, "x_q": 5, "x_s": 6,
+    "part1": 7, "h_q": 8, "h_s": 9, "part2": 10,
+}
+
+
+class MoeDecodeConfig(ctypes.Structure):
+    _fields_ = [
+        ("hidden", ctypes.c_int32),
+        ("inter", ctypes.c_int32),
+        ("experts", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("max_tokens", ctypes.c_int32),
+        ("logits_dtype", ctypes.c_int32),
+        ("ue8m0_act", ctypes.c_int32),
+        ("limit", ctypes.c_float),
+        ("routed_scale", ctypes.c_float),
+        ("w13", ctypes.c_void_p),
+        ("w13_scale", ctypes.c_void_p),
+        ("w2", ctypes.c_void_p),
+        ("w2_scale", ctypes.c_void_p),
+        ("shared_inter", ctypes.c_int32),
+        ("shared_scale_format", ctypes.c_int32),
+        ("shared_ue8m0_act", ctypes.c_int32),
+        ("shared_limit", ctypes.c_float),
+        ("sw13", ctypes.c_void_p),
+        ("sw13_scale", ctypes.c_void_p),
+        ("sw2", ctypes.c_void_p),
+        ("sw2_scale", ctypes.c_void_p),
+        ("gemm_path", ctypes.c_int32),
+        ("splits1", ctypes.c_int32),
+        ("splits2", ctypes.c_int32),
+    ]
+
+
+class MoeDecodeError(RuntimeError):
+    def __init__(self, code: int, what: str = ""):
+        self.code = code
+        super().__init__(f"{what}: {error_string(code)} ({code})" if what else error_string(code))
+
+
+_lib = None
+
+
+def header_functions() -> Sequence[str]:
+    """Names of the functions include/moe_decode.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(moe_decode_\w+)\s*\(", text, re.M)))
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library. Raises if it has not been built: there is no
+    fallback implementation."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m fp8_block_scaled_moe_amd.build` "
+            "(the routed-expert path has no implementation outside the HIP library)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    L.moe_decode_create.argtypes = [ctypes.POINTER(MoeDecodeConfig), ctypes.POINTER(vp)]
+    L.moe_decode_create.restype = ctypes.c_int
+    L.moe_decode_run.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_decode_run.restype = ctypes.c_int
+    L.moe_decode_destroy.argtypes = [vp]
+    L.moe_decode_destroy.restype = None
+    L.moe_decode_error_string.argtypes = [ctypes.c_int]
+    L.moe_decode_error_string.restype = ctypes.c_char_p
+    L.moe_decode_plan.argtypes = [vp, i32, ctypes.POINTER(i32), i32]
+    L.moe_decode_plan.restype = ctypes.c_int
+    L.moe_decode_debug_stage.argtypes = [vp, i32, vp, sz, vp]
+    L.moe_decode_debug_stage.restype = ctypes.c_int
+    L.moe_decode_set_timing.argtypes = [vp, i32]
+    L.moe_decode_set_timing.restype = ctypes.c_int
+    L.moe_decode_last_timing.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i32]
+    L.moe_decode_last_timing.restype = ctypes.c_int
+    L.moe_decode_debug_codec.argtypes = [vp, vp, vp, i32, vp]
+    L.moe_decode_debug_codec.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def error_string(code: int) -> str:
+    return lib().moe_decode_error_string(code).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _need(t: torch.Tensor, name: str, dtypes, dev) -> None:
+    if t.device != dev:
+        raise ValueError(f"{name} must be on {dev}, got {t.device}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_FP8 = (torch.uint8, torch.float8_e4m3fn)
+
+
+class MoeDecode:
+    """Handle over moe_decode_create / moe_decode_run / moe_decode_destroy.
+
+    Weight tensors are borrowed: the handle keeps references so they outlive
+    it. w13 [E, 2I, H] (up rows, then gate rows) and w2 [E, H, I] are e4m3
+    bytes (uint8 or float8_e4m3fn); scales are FP32 [E, N/128, K/128].
+    """
+
+    def __init__(self, w13, w13_scale, w2, w2_scale, *, top_k: int, limit: float,
+                 routed_scale: float, max_tokens: int, logits_dtype=torch.float32,
+                 ue8m0_act: bool = False, gemm_path: str = "auto", splits1: int = 0,
+                 splits2: int = 0):
+        self.device = w13.device
+        for t, n, d in ((w13, "w13", _FP8), (w2, "w2", _FP8), (w13_scale, "w13_scale", (torch.float32,)),
+                        (w2_scale, "w2_scale", (torch.float32,))):
+            _need(t, n, d, self.device)
+        E, N1, H = w13.shape
+        self.experts, self.hidden, self.inter, self.top_k = E, H, N1 // 2, top_k
+        self.max_tokens = max_tokens
+        self.logits_dtype = logits_dtype
+        self._keep = (w13, w13_scale, w2, w2_scale)
+        cfg = MoeDecodeConfig()
+        cfg.hidden, cfg.inter, cfg.experts, cfg.top_k = H, N1 // 2, E, top_k
+        cfg.max_tokens = max_tokens
+        cfg.logits_dtype = DTYPE_BF16 if logits_dtype == torch.bfloat16 else DTYPE_F32
+        cfg.ue8m0_act = int(bool(ue8m0_act))
+        cfg.limit, cfg.routed_scale = limit, routed_scale
+        cfg.w13, cfg.w13_scale, cfg.w2, cfg.w2_scale = (t.data_ptr() for t in self._keep)
+        cfg.gemm_path = GEMM_PATHS[gemm_path]
+        cfg.splits1, cfg.splits2 = splits1, splits2
+        self.cfg = cfg
+        h = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            rc = lib().moe_decode_create(ctypes.byref(cfg), ctypes.byref(h))
+        if rc != OK:
+            raise MoeDecodeError(rc, "moe_decode_create")
+        self._h = h
+
+    # -- calls --------------------------------------------------------------
+    def run_into(self, x, logits, bias, slots, ids, weights, combined, shared_out=None,
+                 stream=None) -> None:
+        M = x.shape[0]
+        rc = lib().moe_decode_run(self._h, M, _ptr(x), _ptr(logits), _ptr(bias), _ptr(slots),
+                                  _ptr(ids), _ptr(weights), _ptr(combined), _ptr(shared_out),
+                                  _stream(stream))
+        if rc != OK:
+            raise MoeDecodeError(rc, "moe_decode_run")
+
+    def outputs(self, M: int):
+        dev, H, k = self.device, self.hidden, self.top_k
+        return (torch.empty((M * k, H), dtype=torch.bfloat16, device=dev),
+                torch.empty((M, k), dtype=torch.int32, device=dev),
+                torch.empty((M, k), dtype=torch.float32, device=dev),
+                torch.empty((M, H), dtype=torch.bfloat16, device=dev))
+
+    def __call__(self, x, logits, bias, stream=None):
+        """(slots [M*k, H] bf16, ids [M, k] int32, weights [M, k] f32,
+        combined [M, H] bf16)."""
+        _need(x, "x", (torch.bfloat16,), self.device)
+        _need(logits, "logits", (self.logits_dtype,), self.device)
+        _need(bias, "bias", (torch.float32,), self.device)
+        out = self.outputs(x.shape[0])
+        self.run_into(x, logits, bias, *out, stream=stream)
+        return out
+
+    # -- introspection ------------------------------------------------------
+    def plan(self, M: int) -> dict:
+        buf = (ctypes.c_int32 * 7)()
+        rc = lib().moe_decode_plan(self._h, M, buf, 7)
+        if rc != OK:
+            raise MoeDecodeError(rc, "moe_decode_plan")
+        keys = ("path", "splits1", "splits2", "ks1", "ks2", "grid1", "grid2")
+        return dict(zip(keys, list(buf)))
+
+    def stage(self, name: str, dst: torch.Tensor, stream=None) -> torch.Tensor:
+        rc = lib().moe_decode_debug_stage(self._h, STAGES[name], dst.data_ptr(),
+                                          dst.numel() * dst.element_size(), _stream(stream))
+        if rc != OK:
+            raise MoeDecodeError(rc, "moe_decode_debug_stage")
+        return dst
+
+    def set_timing(self, enable: bool) -> None:
+        rc = lib().moe_decode_set_timing(self._h, int(enable))
+        if rc != OK:
+            raise MoeDecodeError(rc, "moe_decode_set_timing")
+
+    def last_timing(self):
+        ms = (ctypes.c_float * 7)()
+        rc = lib().moe_decode_last_timing(self._h, ms, 7)
+        if rc != OK:
+            raise MoeDecodeError(rc, "moe_decode_last_timing")
+        return list(ms)
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            lib().moe_decode_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def debug_codec(values: torch.Tensor):
+    """(codes, decoded) from the library's device quantiser and FP8 reader."""
+    n = values.numel()
+    q = torch.empty(n, dtype=torch.uint8, device=values.device)
+    dq = torch.empty(n, dtype=torch.float32, device=values.device)
+    rc = lib().moe_decode_debug_codec(values.data_ptr(), q.data_ptr(), dq.data_ptr(), n, _stream(None))
+    if rc != OK:
+        raise MoeDecodeError(rc, "moe_decode_debug_codec")
+    return q, dq

@@ -1,0 +1,58 @@
+"""Builds libmoe_decode.so (gfx950) in place, next to this file.
+
+    python -m fp8_block_scaled_moe_amd.build
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libmoe_decode.so")
+SOURCES = ["capi.hip", "route_quant.hip", "expert_gemm.hip", "epilogues.hip"]
+ARCH = "gfx950"
+
+FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-Wall",
+    # keep the compiler from forming packed FP32 instructions
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the library)")
+
+
+def build(verbose: bool = False) -> str:
+    """Compiles every source into libmoe_decode.so; returns its path."""
+    tmp = LIB + f".tmp{os.getpid()}"
+    cmd = [hipcc(), *FLAGS, "-o", tmp, *[os.path.join(CSRC, s) for s in SOURCES]]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "packed-fp32-ops"  # the host pass does not know the feature
+    msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
+    if res.returncode != 0:
+        if os.path.exists(tmp):
+            os.remove(tmp)
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
+    if verbose and msgs.strip():
+        print(msgs)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

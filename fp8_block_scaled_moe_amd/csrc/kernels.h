@@ -1,0 +1,86 @@
+// Kernel argument blocks and host-side launchers. Each kernel lives in its
+// own translation unit and is launched through the function declared here.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kTile = 128;  // block size of every FP8 scale (K and N)
+
+// Distinct-expert buckets built by the routing kernel (device memory).
+struct Buckets {
+  int32_t* ctrl;     // [0] arrival counter (self-resetting), [1] U = distinct experts
+  int32_t* uexp;     // [U] expert ids, ascending
+  int32_t* uoff;     // [U] first index of the expert's routes in `routes`
+  int32_t* ucnt;     // [U] number of routes of the expert
+  int32_t* routes;   // [M*k] route indices (t*k + j) grouped by expert, ascending t
+};
+
+struct RouteQuantArgs {
+  const void* logits;   // [M, E] f32 or bf16
+  int logits_bf16;
+  const float* bias;    // [E]
+  const uint16_t* x;    // [M, H] bf16
+  int M, E, k, H;
+  float routed_scale;
+  int ue8m0;
+  int words;            // 64-bit token-mask words per expert: ceil(M / 64)
+  int32_t* ids;         // [M, k]
+  float* weights;       // [M, k]
+  uint8_t* xq;          // [M, H]
+  float* xs;            // [M, H/128]
+  Buckets b;
+};
+
+// One block-scaled GEMM pass over the touched experts: for every route r of
+// distinct expert u and every weight row n,
+//   part[split, r, n] = sum_{b in split} ws[e, n/128, b] * as[row(r), b] *
+//                       sum_{i in block b} W[e, n, i] * A[row(r), i]
+// with row(r) = r / act_div.
+struct GemmArgs {
+  const uint8_t* w;     // [E, N, K] e4m3
+  const float* ws;      // [E, N/128, K/128]
+  const uint8_t* aq;    // [rows, K] e4m3
+  const float* as;      // [rows, K/128]
+  float* part;          // [splits, R, N]
+  Buckets b;
+  int N, K, nkb;        // nkb = K / 128
+  int tiles;            // N / 64
+  int splits, ks;       // K splits and 128-blocks per split
+  int R;                // routes (row stride of part)
+  int act_div;
+};
+
+struct SwigluArgs {
+  const float* part;    // [splits, R, 2I]
+  int splits, R, I;
+  float limit;
+  uint8_t* hq;          // [R, I]
+  float* hs;            // [R, I/128]
+};
+
+struct CombineArgs {
+  const float* part;    // [splits, R, H]
+  int splits, M, k, H;
+  const float* weights; // [M, k]
+  uint16_t* slots;      // [M*k, H] bf16
+  uint16_t* combined;   // [M, H] bf16
+};
+
+// Maximum 128-blocks of K per split (bounds the LDS staging of activations).
+constexpr int kMaxKs = 16;
+constexpr int kRowsPerWg = 64;
+constexpr int kValuRoutes = 8;   // routes per pass of the VALU inner product
+constexpr int kMfmaRoutes = 16;  // routes per pass of the MFMA inner product
+
+size_t route_quant_lds_bytes(int E, int words);
+hipError_t launch_route_quant(const RouteQuantArgs& a, hipStream_t s);
+hipError_t launch_gemm_valu(const GemmArgs& a, int grid, hipStream_t s);
+hipError_t launch_gemm_mfma(const GemmArgs& a, int grid, hipStream_t s);
+hipError_t launch_swiglu_requant(const SwigluArgs& a, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_codec_check(const float* in, uint8_t* q, float* dq, int n, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,196 @@
+/*
+ * moe_decode.h -- routed-expert FP8 block-scaled MoE decode on MI355X (gfx950).
+ *
+ * The operation (vLLM "mega_moe" page, module docstring and MegaExperts
+ * __call__; slot semantics from the nvfp4-megamoe-kernel README, "slot
+ * representation"): for each of M decode tokens
+ *   1. biased sigmoid top-k routing from router logits: s = sigmoid(z),
+ *      key = s + bias, top_k by key (ties to the lower expert), weights =
+ *      s / sum(picked s) * routed_scale ("mega_moe" page, top_k_pick);
+ *   2. the BF16 activation quantised to OCP FP8 e4m3 per 128 values with
+ *      scale max(amax, 1e-10) / 448 (optionally rounded up to a power of two)
+ *      ("mega_moe" page, epilogue);
+ *   3. GEMM1 against the expert's FP8 W13 (rows 0..I-1 up, I..2I-1 gate)
+ *      with FP32 128x128 block scales applied once per K block;
+ *   4. clamped SwiGLU: gate = min(g, L), up = clamp(u, -L, L),
+ *      act = gate / (1 + exp(-gate)) * up ("mega_moe" page, hidden_block);
+ *   5. the hidden requantised to FP8 per 128 (scale amax / 448);
+ *   6. GEMM2 against W2, written as an unweighted BF16 "slot" row per
+ *      (token, expert) route, row t * top_k + j;
+ *   7. combined[t] = BF16(sum_j weights[t, j] * slot[t * top_k + j]): the
+ *      routing weights applied exactly once (nvfp4-megamoe-kernel README,
+ *      bugs 6 and 7; FP32 sum rounded once as in the "kimi_k3 ... ep.comm"
+ *      page's combine).
+ * Optionally, the dense shared expert of the "shared_expert" page runs on the
+ * same stream (FP8 gate_up GEMV with gate rows first, BF16 gate/up, clamped
+ * SwiGLU rounded to BF16, FP8 per 128, down GEMV, BF16 out).
+ *
+ * Conventions
+ *  - All tensor pointers are DEVICE pointers on the device that was current
+ *    when moe_decode_create ran, row-major and contiguous, 16-byte aligned.
+ *  - FP8 is OCP e4m3 ("e4m3fn": bias 7, max 448, no infinities), one byte per
+ *    value; BF16 is a 16-bit brain float; FP32 is IEEE binary32.
+ *  - Everything is enqueued on the HIP stream passed in (a hipStream_t, given
+ *    as void* so that this header needs no HIP headers; NULL is the default
+ *    stream). No call synchronises the host, and moe_decode_run allocates
+ *    nothing, so it may be captured in a HIP graph.
+ *  - Return value: MOE_DECODE_OK (0) or a negative MOE_DECODE_ERR_* code.
+ *    An argument error leaves the handle valid and enqueues nothing.
+ *
+ * Thread safety: one handle owns one workspace. Calls of moe_decode_run on
+ * the same handle must be ordered (same stream, or synchronised); separate
+ * handles are independent.
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_DECODE_OK 0
+#define MOE_DECODE_ERR_INVALID_ARG (-1)     /* null or misaligned pointer, bad M, bad value */
+#define MOE_DECODE_ERR_UNSUPPORTED (-2)     /* shape or option outside what the kernels take */
+#define MOE_DECODE_ERR_TOO_MANY_TOKENS (-3) /* M > max_tokens of the handle */
+#define MOE_DECODE_ERR_HIP (-4)             /* a HIP call or kernel launch failed */
+#define MOE_DECODE_ERR_OUT_OF_MEMORY (-5)   /* workspace allocation failed */
+
+#define MOE_DTYPE_F32 0
+#define MOE_DTYPE_BF16 1
+
+#define MOE_SCALES_F32 0         /* FP32 [n/128, k/128] block scales */
+#define MOE_SCALES_UE8M0_PACKED 1 /* int32 [n, ceil(k/512)]: byte g%4 of word g/4 = biased exponent of K group g */
+
+#define MOE_GEMM_AUTO 0  /* choose the inner product per call */
+#define MOE_GEMM_VALU 1  /* packed FP8->F16 conversion + F16 dot2 into FP32 */
+#define MOE_GEMM_MFMA 2  /* v_mfma_f32_16x16x128_f8f6f4, one 128-K block per instruction */
+
+/* Limits of this implementation. */
+#define MOE_DECODE_MAX_EXPERTS 1024
+#define MOE_DECODE_MAX_TOP_K 32
+#define MOE_DECODE_MAX_TOKENS 256
+
+typedef struct moe_decode_config {
+  /* Shapes. hidden (H) and inter (I) are multiples of 128; 1 <= top_k <=
+   * min(experts, 32); experts <= 1024; 1 <= max_tokens <= 256. */
+  int32_t hidden;
+  int32_t inter;
+  int32_t experts;
+  int32_t top_k;
+  int32_t max_tokens;
+  int32_t logits_dtype; /* MOE_DTYPE_F32 or MOE_DTYPE_BF16 ([M, E] logits) */
+  int32_t ue8m0_act;    /* nonzero: activation scales rounded up to powers of two */
+  float limit;          /* SwiGLU clamp L > 0 */
+  float routed_scale;   /* multiplies the renormalised routing weights */
+
+  /* Routed expert weights (borrowed: they must outlive the handle).
+   * w13       [E, 2I, H] e4m3, rows 0..I-1 "up", rows I..2I-1 "gate"
+   * w13_scale [E, 2I/128, H/128] FP32, any positive values
+   * w2        [E, H, I] e4m3
+   * w2_scale  [E, H/128, I/128] FP32 */
+  const void* w13;
+  const float* w13_scale;
+  const void* w2;
+  const float* w2_scale;
+
+  /* Optional dense shared expert ("shared_expert" page); all zero/NULL when
+   * absent. shared_inter (Is) is a multiple of 128.
+   * sw13 [2Is, H] e4m3, rows 0..Is-1 gate, Is..2Is-1 up; sw2 [H, Is] e4m3.
+   * Scales per shared_scale_format: FP32 [2Is/128, H/128] / [H/128, Is/128],
+   * or MOE_SCALES_UE8M0_PACKED int32 [2Is, ceil(H/512)] / [H, ceil(Is/512)]
+   * (converted once, in create, to FP32 owned by the handle). */
+  int32_t shared_inter;
+  int32_t shared_scale_format;
+  int32_t shared_ue8m0_act; /* nonzero: the shared expert's activation scales are UE8M0 */
+  float shared_limit;
+  const void* sw13;
+  const void* sw13_scale;
+  const void* sw2;
+  const void* sw2_scale;
+
+  /* Tuning (0 = automatic). gemm_path: MOE_GEMM_*. splits1/splits2: K splits
+   * of GEMM1/GEMM2 (work units are 64 weight rows x one K split of one touched
+   * expert). */
+  int32_t gemm_path;
+  int32_t splits1;
+  int32_t splits2;
+} moe_decode_config;
+
+typedef struct moe_decode_handle* moe_decode_t;
+
+/* Validates cfg, allocates the handle's workspace for cfg->max_tokens on the
+ * current device, and converts packed shared-expert scales. Weight pointers
+ * are borrowed, not copied. On success *out receives the handle.
+ * Errors: INVALID_ARG (null cfg/out/weights, limit <= 0, max_tokens out of
+ * range), UNSUPPORTED (shape limits above), OUT_OF_MEMORY, HIP. */
+int moe_decode_create(const moe_decode_config* cfg, moe_decode_t* out);
+
+/* One routed-expert decode step for M tokens, 0 <= M <= max_tokens.
+ *   x          [M, H] BF16
+ *   logits     [M, E] FP32 or BF16 (per logits_dtype)
+ *   bias       [E] FP32 score-correction bias (selects, does not weigh)
+ *   slots      [M*top_k, H] BF16 out: unweighted expert output of route
+ *              t*top_k + j (token t, j-th pick)
+ *   ids        [M, top_k] int32 out: picked experts, highest biased score first
+ *   weights    [M, top_k] FP32 out: routing weights
+ *   combined   [M, H] BF16 out: sum_j weights[t, j] * slots[t*top_k + j]
+ *   shared_out [M, H] BF16 out of the shared expert, or NULL to skip it
+ *              (must be NULL if the handle has no shared expert)
+ *   stream     hipStream_t
+ * M == 0 enqueues nothing and returns OK. Errors: INVALID_ARG (null handle or
+ * pointer, misaligned pointer, M < 0), TOO_MANY_TOKENS, HIP (launch failure).
+ * Numerics: ids and weights follow the FP32 rules above exactly; slot,
+ * combined and shared rows carry FP32 accumulation-order differences. */
+int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
+                   const float* bias, void* slots, int32_t* ids, float* weights,
+                   void* combined, void* shared_out, void* stream);
+
+/* Frees the workspace (after synchronising the device). NULL is a no-op. */
+void moe_decode_destroy(moe_decode_t h);
+
+/* Static description of an error code. */
+const char* moe_decode_error_string(int code);
+
+/* ---- Introspection (tests and benchmarks) ------------------------------ */
+
+/* The launch plan run() uses for M tokens: out[0] = GEMM path used
+ * (MOE_GEMM_VALU or MOE_GEMM_MFMA), out[1] = splits1, out[2] = splits2,
+ * out[3] = blocks per split in GEMM1, out[4] = in GEMM2, out[5] = grid of
+ * GEMM1, out[6] = grid of GEMM2. n is the capacity of out (>= 7). */
+int moe_decode_plan(moe_decode_t h, int32_t M, int32_t* out, int32_t n);
+
+/* Stage read-back: copies workspace region `stage` of the last run into the
+ * device buffer dst (bytes = capacity of dst) on stream. Stages:
+ *  0 control words int32[2] (arrival counter, distinct experts U)
+ *  1 distinct experts, ascending int32[U]   2 their first index into stage 4
+ *  3 their route counts int32[U]            4 routes grouped by expert int32[M*k]
+ *  5 x_q [M, H] e4m3                        6 x_s [M, H/128] FP32
+ *  7 GEMM1 split partials FP32 [splits1, M*k, 2I]
+ *  8 h_q [M*k, I] e4m3                      9 h_s [M*k, I/128] FP32
+ * 10 GEMM2 split partials FP32 [splits2, M*k, H]
+ * The size copied is min(bytes, size of the stage for the handle's maximum). */
+int moe_decode_debug_stage(moe_decode_t h, int32_t stage, void* dst, size_t bytes,
+                           void* stream);
+
+/* Per-kernel timing of subsequent runs with HIP events recorded between the
+ * launches (enable != 0; not for use under graph capture). After a run has
+ * completed, moe_decode_last_timing writes the milliseconds of each launch
+ * in order: route+quant, GEMM1, SwiGLU+requant, GEMM2, combine, shared
+ * gate_up, shared down (0 when not run). n is the capacity of ms (>= 7). */
+int moe_decode_set_timing(moe_decode_t h, int32_t enable);
+int moe_decode_last_timing(moe_decode_t h, float* ms, int32_t n);
+
+/* Codec self-check of the device code: q[i] = e4m3 encoding of in[i] with the
+ * library's quantiser (nearest, ties to even, saturating), and dq[i] = the
+ * value the GEMM inner products read for code (i & 255) through the path's
+ * FP8 -> F16 conversion. in, q and dq are device buffers of n elements. */
+int moe_decode_debug_codec(const float* in, uint8_t* q, float* dq, int32_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DECODE_H */
