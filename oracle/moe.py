@@ -148,17 +148,28 @@ def block_scaled_gemm(wcodes, wscale, acodes, ascale) -> np.ndarray:
 # Clamped SwiGLU
 # --------------------------------------------------------------------------
 
+def silu_f32(gate) -> np.ndarray:
+    """gate / (1 + exp(-gate)) as the pages evaluate it in FP32: each of the
+    exp, the add and the divide rounded to binary32 in that order (the exp
+    correctly rounded, the reading taken for the pages' FP32 exp)."""
+    gate = np.asarray(gate, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        e = f32(np.exp(-gate))
+    return f32(gate / f32(1.0 + e))
+
+
 def swiglu(h1, inter: int, limit: float) -> np.ndarray:
     """Routed clamped SwiGLU ("mega_moe" page, hidden_block; the GEMM1 row
     order "up rows, then gate rows" of the module docstring).
 
     up = clamp(h1[:, :I], -L, L); gate = min(h1[:, I:], L) (the gate is not
-    clamped from below); act = FP32(gate / (1 + exp(-gate)) * up)."""
+    clamped from below); act = (gate / (1 + exp(-gate))) * up with every
+    operation rounded to FP32 in the page's order. The FP8 hidden codes are
+    decided from act, so the rounding points are kept exactly."""
     h1 = np.asarray(h1, dtype=np.float64)
     up = np.clip(h1[:, :inter], -limit, limit)
     gate = np.minimum(h1[:, inter:], limit)
-    with np.errstate(over="ignore"):
-        return f32(gate / (1.0 + np.exp(-gate)) * up)
+    return f32(silu_f32(gate) * up)
 
 
 # --------------------------------------------------------------------------
@@ -252,17 +263,16 @@ def shared_expert(x, sw13, sw13_scale, sw2, sw2_scale, *, limit: float,
     x quantised per 128 with the stock rule (UE8M0 scales when ue8m0_act,
     multiplying by the reciprocal, which is an exact power of two then);
     gate_up = BF16(FP32(GEMV)) with gate rows first; gate = min(gate, L),
-    up = clamp(up, -L, L); silu = FP32(gate / (1 + exp(-gate)));
-    act = BF16(silu * up); act quantised like x; out = BF16(FP32(GEMV))."""
+    up = clamp(up, -L, L); silu = gate / (1 + exp(-gate)) in FP32 steps
+    (_DownKernel: IEEE divide, accurate exp); act = BF16(silu * up); act
+    quantised like x; out = BF16(FP32(GEMV))."""
     x = np.asarray(x, dtype=np.float64)
     x_q, x_s = quantize_blocks(x, ue8m0=ue8m0_act, reciprocal=True)
     gu = bf16_round(block_scaled_gemm(sw13, sw13_scale, x_q, x_s))
     Is = gu.shape[1] // 2
     gate = np.minimum(gu[:, :Is], limit)
     up = np.clip(gu[:, Is:], -limit, limit)
-    with np.errstate(over="ignore"):
-        silu = f32(gate / (1.0 + np.exp(-gate)))
-    act = bf16_round(silu * up)
+    act = bf16_round(silu_f32(gate) * up)
     h_q, h_s = quantize_blocks(act, ue8m0=ue8m0_act, reciprocal=True)
     out = bf16_round(block_scaled_gemm(sw2, sw2_scale, h_q, h_s))
     return dict(x_q=x_q, x_s=x_s, gate_up=gu, act=act, h_q=h_q, h_s=h_s, out=out)
