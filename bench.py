@@ -1,0 +1,194 @@
+"""Routed-expert FP8 MoE decode benchmark: us per layer and achieved HBM GB/s.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3] [--M 4]
+
+One step = one moe_decode_run (routing, activation quant, GEMM1, SwiGLU +
+requant, GEMM2, combine) on resident synthetic inputs. Before every step a
+1 GiB buffer is overwritten so that the weights come from HBM, not from L2 or
+the 256 MB MALL; the flush is outside the per-layer events. Counted bytes =
+distinct experts touched x (W13 + W2 FP8 bytes + FP32 scales). Prints one JSON
+line. The default workload is the DeepSeek-V3-shaped decode at M=4.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+from fp8_block_scaled_moe_amd import MoeDecode  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "routed-MoE decode µs/layer + achieved HBM GB/s (% peak) at M=1..64 tokens"
+KERNELS = ["route_quant", "gemm1", "swiglu_requant", "gemm2", "combine"]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="dsv3", choices=sorted(synth.CONFIGS))
+    p.add_argument("--M", type=int, default=0, help="tokens (default: the workload's)")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--path", default="auto", choices=["auto", "valu", "mfma"])
+    p.add_argument("--splits1", type=int, default=0)
+    p.add_argument("--splits2", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--sweep", default="", help="comma-separated M values: one JSON line each")
+    return p.parse_args()
+
+
+def workload_name(shape) -> str:
+    return (f"{shape.name}: M={shape.M} H={shape.hidden} I={shape.inter} E={shape.experts} "
+            f"top_k={shape.top_k}")
+
+
+def cpu_baseline(inp, counted_bytes: int) -> dict:
+    """The oracle on the host cores, once, on the same inputs (the whole layer
+    for all M tokens: it reads only the touched experts)."""
+    from threadpoolctl import threadpool_info
+    from tests.helpers import oracle_layer
+
+    t0 = time.perf_counter()
+    oracle_layer(inp)
+    dt = time.perf_counter() - t0
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    return {"value": counted_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle", "seconds": dt, "host_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"one full layer of the same workload ({inp.shape.M} tokens, all touched "
+                      f"experts), float64 NumPy oracle, weights copied to host outside the timing"}
+
+
+def run_one(args, shape, inp, moe, flush):
+    dev = inp.x.device
+    k = shape.top_k
+    slots, ids, weights, combined = moe.outputs(shape.M)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        moe.run_into(inp.x, inp.logits, inp.bias, slots, ids, weights, combined, stream=stream)
+
+    for _ in range(args.warmup):
+        flush.zero_()
+        step()
+    torch.cuda.synchronize()
+    U = int(torch.unique(ids).numel())
+    counted = U * shape.expert_bytes()
+
+    # pass 1: whole layer, events on torch's current stream (the library's stream)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        flush.zero_()
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    layer_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+
+    # pass 2: per-kernel times from events the library records between launches
+    moe.set_timing(True)
+    per = []
+    for i in range(args.steps):
+        flush.zero_()
+        step()
+        per.append(moe.last_timing()[:len(KERNELS)])
+    moe.set_timing(False)
+    per = np.array(per)
+    torch.cuda.synchronize()
+    return dict(U=U, counted=counted, layer_ms=layer_ms, per_kernel_ms=per, wall_s=wall, ids=ids)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the routed-expert path "
+                          "has no multi-GPU form in this library (expert-parallel sharding is "
+                          "described in DESIGN.md)", "n_gpus": args.gpus}))
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    base = synth.CONFIGS[args.workload]
+    Ms = [int(m) for m in args.sweep.split(",")] if args.sweep else [args.M or base.M]
+    maxM = max(Ms)
+    shape = base.with_(M=maxM)
+    inp_all = synth.make_inputs(shape, seed=args.seed, device=dev)
+    moe = MoeDecode(inp_all.w13, inp_all.w13_scale, inp_all.w2, inp_all.w2_scale,
+                    top_k=shape.top_k, limit=shape.limit, routed_scale=shape.routed_scale,
+                    max_tokens=maxM, logits_dtype=inp_all.logits.dtype, ue8m0_act=shape.ue8m0_act,
+                    gemm_path=args.path, splits1=args.splits1, splits2=args.splits2)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    for M in Ms:
+        sh = base.with_(M=M)
+        inp = synth.MoeInputs(shape=sh, seed=args.seed, x=inp_all.x[:M].contiguous(),
+                              logits=inp_all.logits[:M].contiguous(), bias=inp_all.bias,
+                              w13=inp_all.w13, w13_scale=inp_all.w13_scale, w2=inp_all.w2,
+                              w2_scale=inp_all.w2_scale)
+        r = run_one(args, sh, inp, moe, flush)
+        ms = float(np.mean(r["layer_ms"]))
+        us = ms * 1e3
+        gbs = r["counted"] / (ms * 1e-3) / 1e9
+        per = r["per_kernel_ms"].mean(axis=0)
+        # dominant kernel: GEMM1 streams W13 (2/3 of the counted bytes)
+        g1_bytes = r["U"] * (2 * sh.inter * sh.hidden + (2 * sh.inter // 128) * (sh.hidden // 128) * 4)
+        g1_gbs = g1_bytes / (per[1] * 1e-3) / 1e9
+        plan = moe.plan(M)
+        line = {
+            "metric": METRIC,
+            "value": round(gbs, 1),
+            "unit": "GB/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(ms, 5),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "fp8",
+            "data": "synthetic",
+            "config": {
+                "workload": workload_name(sh),
+                "M": M, "hidden": sh.hidden, "inter": sh.inter, "experts": sh.experts,
+                "top_k": sh.top_k, "unique_experts": r["U"], "counted_bytes": r["counted"],
+                "us_per_layer": round(us, 2),
+                "us_per_layer_p10_p90": [round(float(np.quantile(r["layer_ms"], q)) * 1e3, 2)
+                                         for q in (0.1, 0.9)],
+                "pct_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
+                "kernel_us": {k: round(float(v) * 1e3, 2) for k, v in zip(KERNELS, per)},
+                "wall_ms_per_step_incl_flush": round(r["wall_s"] / args.steps * 1e3, 4),
+                "gemm_path": {1: "valu", 2: "mfma"}[plan["path"]],
+                "splits": [plan["splits1"], plan["splits2"]],
+                "l2_mall_flush": "1 GiB overwrite before every step, outside the timed layer",
+            },
+            "roofline": {
+                "kernel": "gemm1 (W13 up/gate GEMM over the touched experts)",
+                "bound": "hbm",
+                "achieved": round(g1_gbs, 1),
+                "peak": PEAK_HBM_GBS,
+                "unit": "GB/s",
+                "frac": round(g1_gbs / PEAK_HBM_GBS, 4),
+                "traffic": None,
+                "algorithmic_bytes_per_launch": g1_bytes,
+                "avg_launch_us": round(float(per[1]) * 1e3, 2),
+            },
+        }
+        if not args.no_cpu_baseline and M == Ms[0]:
+            line["cpu_baseline"] = cpu_baseline(inp, r["counted"])
+        print(json.dumps(line), flush=True)
+    moe.close()
+
+
+if __name__ == "__main__":
+    main()

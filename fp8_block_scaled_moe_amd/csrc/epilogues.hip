@@ -3,7 +3,7 @@
 // swiglu_requant: the fixed-order sum of GEMM1's split partials, the clamped
 // SwiGLU and the FP8 hidden of the vLLM "mega_moe" page's hidden_block:
 // up = clamp(u, -L, L), gate = min(g, L), act = gate / (1 + exp(-gate)) * up
-// in FP32, then per 128 values scale = max(amax, 1e-10) / 448 and
+// in FP32 operations (the exp correctly rounded), then per 128 values scale = max(amax, 1e-10) / 448 and
 // q = e4m3(act / scale). Rows 0..I-1 of GEMM1 are up, I..2I-1 gate.
 //
 // combine: the fixed-order sum of GEMM2's split partials rounded once to the
@@ -42,8 +42,11 @@ __global__ __launch_bounds__(kThreads) void swiglu_requant_kernel(SwigluArgs a) 
   up1 = fminf(fmaxf(up1, -L), L);
   g0 = fminf(g0, L);
   g1 = fminf(g1, L);
-  const float act0 = g0 / (1.f + expf(-g0)) * up0;
-  const float act1 = g1 / (1.f + expf(-g1)) * up1;
+  // exp rounded once to FP32 from FP64, then the add, divide and product in
+  // FP32 in this order: the FP8 codes below are decided from these values.
+  const float e0 = (float)exp(-(double)g0), e1 = (float)exp(-(double)g1);
+  const float act0 = (g0 / (1.f + e0)) * up0;
+  const float act1 = (g1 / (1.f + e1)) * up1;
   const float amax = group_max<kWave>(fmaxf(fabsf(act0), fabsf(act1)));
   const float s = fmaxf(amax, kAmaxFloor) / kFp8Max;
   const uint32_t q = e4m3_encode(act0 / s) | (e4m3_encode(act1 / s) << 8);
