@@ -45,7 +45,33 @@ def parse():
     p.add_argument("--splits2", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--sweep", default="", help="comma-separated M values: one JSON line each")
+    p.add_argument("--calibrate", action="store_true",
+                   help="time a plain 1 GiB device copy and a 4 GiB read-only sum instead")
     return p.parse_args()
+
+
+def calibrate(args) -> None:
+    """Achievable HBM bandwidth on this GPU: a plain device-to-device copy
+    of 1 GiB (reads + writes 2 GiB) and a read-only sum over 4 GiB."""
+    dev = torch.device("cuda:0")
+    src = torch.randint(0, 255, (1 << 30,), dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    big = torch.ones((1 << 30,), dtype=torch.float32, device=dev)
+    out = {}
+    for name, fn, nbytes in (("copy_1GiB", lambda: dst.copy_(src), 2 << 30),
+                             ("sum_4GiB", lambda: big.sum(), 4 << 30)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(args.steps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / args.steps
+        out[name] = {"ms": round(ms, 4), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    print(json.dumps({"calibration": out, "peak_GB/s": PEAK_HBM_GBS}), flush=True)
 
 
 def workload_name(shape) -> str:
@@ -119,6 +145,9 @@ def main():
                           "has no multi-GPU form in this library (expert-parallel sharding is "
                           "described in DESIGN.md)", "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.calibrate:
+        calibrate(args)
+        return
     dev = torch.device("cuda:0")
     base = synth.CONFIGS[args.workload]
     Ms = [int(m) for m in args.sweep.split(",")] if args.sweep else [args.M or base.M]

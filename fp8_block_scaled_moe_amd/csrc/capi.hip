@@ -17,6 +17,8 @@ using namespace moe;
 namespace {
 
 constexpr int kEvents = 8;
+constexpr int kRegions = 11;
+constexpr int kStages = 7;  // timing slots: route, GEMM1, SwiGLU, GEMM2, combine, shared x2
 constexpr int kTargetUnits = 4096;  // work units per GEMM launch to aim for (16 per CU)
 
 struct Plan {
@@ -24,6 +26,7 @@ struct Plan {
   int s1, ks1, s2, ks2;
   int grid1, grid2;
   int umax;
+  int pass_routes;  // MFMA path: routes per pass
 };
 
 struct Region {
@@ -37,7 +40,7 @@ struct moe_decode_handle {
   int device;
   unsigned char* ws;
   size_t ws_bytes;
-  Region reg[11];
+  Region reg[kRegions];
   int words;
   // shared expert scales converted to FP32 (owned), or the caller's FP32 ones
   float* s13_owned;
@@ -47,7 +50,8 @@ struct moe_decode_handle {
   bool timing;
   bool timed_run;
   hipEvent_t ev[kEvents];
-  int ev_used[kEvents];
+  int ev_stage[kEvents];  // timing slot of the interval that ends at event i
+  int ev_count;           // events recorded by the last timed run
 };
 
 namespace {
@@ -56,12 +60,12 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-// K split of one GEMM: at most kMaxKs blocks per split, enough units to fill
+// K split of one GEMM: at most max_ks blocks per split, enough units to fill
 // the chip, splits of equal size where possible.
-void choose_split(int units_per_split, int nkb, int forced, int* splits, int* ks) {
+void choose_split(int units_per_split, int nkb, int forced, int max_ks, int* splits, int* ks) {
   int s = forced > 0 ? forced : ceil_div(kTargetUnits, std::max(units_per_split, 1));
   s = std::max(1, std::min(s, nkb));
-  s = std::max(s, ceil_div(nkb, kMaxKs));
+  s = std::max(s, ceil_div(nkb, max_ks));
   int k = ceil_div(nkb, s);
   *ks = k;
   *splits = ceil_div(nkb, k);
@@ -72,11 +76,16 @@ Plan make_plan(const moe_decode_config& c, int M) {
   const int R = M * c.top_k;
   p.umax = std::min(c.experts, R);
   const int tiles1 = 2 * c.inter / kRowsPerWg, tiles2 = c.hidden / kRowsPerWg;
-  choose_split(p.umax * tiles1, c.hidden / kTile, c.splits1, &p.s1, &p.ks1);
-  choose_split(p.umax * tiles2, c.inter / kTile, c.splits2, &p.s2, &p.ks2);
+  p.path = c.gemm_path == MOE_GEMM_MFMA ? MOE_GEMM_MFMA : MOE_GEMM_VALU;
+  // an expert has at most one route per token
+  p.pass_routes = std::min(kMfmaRoutes, M);
+  int max_ks = kMaxKs;
+  if (p.path == MOE_GEMM_MFMA)
+    while (max_ks > 1 && gemm_mfma_lds_bytes(p.pass_routes, max_ks) > kMfmaLdsBudget) --max_ks;
+  choose_split(p.umax * tiles1, c.hidden / kTile, c.splits1, max_ks, &p.s1, &p.ks1);
+  choose_split(p.umax * tiles2, c.inter / kTile, c.splits2, max_ks, &p.s2, &p.ks2);
   p.grid1 = p.umax * tiles1 * p.s1;
   p.grid2 = p.umax * tiles2 * p.s2;
-  p.path = c.gemm_path == MOE_GEMM_MFMA ? MOE_GEMM_MFMA : MOE_GEMM_VALU;
   return p;
 }
 
@@ -97,6 +106,11 @@ int validate_config(const moe_decode_config* c) {
     return MOE_DECODE_ERR_UNSUPPORTED;
   if (c->gemm_path < MOE_GEMM_AUTO || c->gemm_path > MOE_GEMM_MFMA) return MOE_DECODE_ERR_UNSUPPORTED;
   if (c->splits1 < 0 || c->splits2 < 0) return MOE_DECODE_ERR_INVALID_ARG;
+  {
+    const int words = (c->max_tokens + 63) / 64;
+    if (route_quant_lds_bytes(c->experts, words, c->max_tokens * c->top_k) > kMaxRouteLds)
+      return MOE_DECODE_ERR_UNSUPPORTED;
+  }
   if (c->shared_inter != 0) {
     // The shared expert is not built into this library yet.
     return MOE_DECODE_ERR_UNSUPPORTED;
@@ -137,7 +151,7 @@ int moe_decode_create(const moe_decode_config* cfg, moe_decode_t* out) {
     p2 = std::max(p2, (size_t)p.s2 * M * c.top_k * c.hidden);
   }
   const size_t H = c.hidden, I = c.inter;
-  const size_t sizes[11] = {
+  const size_t sizes[kRegions] = {
       64 * sizeof(int32_t),           // 0 control
       Ucap * sizeof(int32_t),         // 1 uexp
       Ucap * sizeof(int32_t),         // 2 uoff
@@ -154,7 +168,7 @@ int moe_decode_create(const moe_decode_config* cfg, moe_decode_t* out) {
   if (!h) return MOE_DECODE_ERR_OUT_OF_MEMORY;
   h->cfg = c;
   size_t off = 0;
-  for (int i = 0; i < 11; ++i) {
+  for (int i = 0; i < kRegions; ++i) {
     h->reg[i] = Region{off, sizes[i]};
     off += (sizes[i] + 255) & ~size_t(255);
   }
@@ -256,15 +270,15 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   float* hs = reinterpret_cast<float*>(at(9));
   float* p2 = reinterpret_cast<float*>(at(10));
 
-  for (int i = 0; i < kEvents; ++i) h->ev_used[i] = 0;
   int evn = 0;
-  auto mark = [&]() -> hipError_t {
+  // records an event closing timing slot `stage` (the first call opens)
+  auto mark = [&](int stage) -> hipError_t {
     if (!h->timing) return hipSuccess;
-    h->ev_used[evn] = 1;
+    h->ev_stage[evn] = stage;
     return hipEventRecord(h->ev[evn++], s);
   };
 
-  hipError_t e = mark();
+  hipError_t e = mark(-1);
 
   RouteQuantArgs ra;
   ra.logits = logits;
@@ -284,7 +298,26 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   ra.xs = xs;
   ra.b = b;
   if (e == hipSuccess) e = launch_route_quant(ra, s);
-  if (e == hipSuccess) e = mark();
+  if (e == hipSuccess) e = mark(0);
+
+  SwigluArgs sa;
+  sa.part = p1;
+  sa.splits = p.s1;
+  sa.R = R;
+  sa.I = c.inter;
+  sa.limit = c.limit;
+  sa.hq = hq;
+  sa.hs = hs;
+
+  CombineArgs ca;
+  ca.part = p2;
+  ca.splits = p.s2;
+  ca.M = M;
+  ca.k = c.top_k;
+  ca.H = c.hidden;
+  ca.weights = weights;
+  ca.slots = static_cast<uint16_t*>(slots);
+  ca.combined = static_cast<uint16_t*>(combined);
 
   GemmArgs g1;
   g1.w = static_cast<const uint8_t*>(c.w13);
@@ -301,20 +334,13 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   g1.ks = p.ks1;
   g1.R = R;
   g1.act_div = c.top_k;
+  g1.pass_routes = p.pass_routes;
   if (e == hipSuccess)
     e = p.path == MOE_GEMM_MFMA ? launch_gemm_mfma(g1, p.grid1, s) : launch_gemm_valu(g1, p.grid1, s);
-  if (e == hipSuccess) e = mark();
+  if (e == hipSuccess) e = mark(1);
 
-  SwigluArgs sa;
-  sa.part = p1;
-  sa.splits = p.s1;
-  sa.R = R;
-  sa.I = c.inter;
-  sa.limit = c.limit;
-  sa.hq = hq;
-  sa.hs = hs;
   if (e == hipSuccess) e = launch_swiglu_requant(sa, s);
-  if (e == hipSuccess) e = mark();
+  if (e == hipSuccess) e = mark(2);
 
   GemmArgs g2 = g1;
   g2.w = static_cast<const uint8_t*>(c.w2);
@@ -331,21 +357,13 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   g2.act_div = 1;
   if (e == hipSuccess)
     e = p.path == MOE_GEMM_MFMA ? launch_gemm_mfma(g2, p.grid2, s) : launch_gemm_valu(g2, p.grid2, s);
-  if (e == hipSuccess) e = mark();
+  if (e == hipSuccess) e = mark(3);
 
-  CombineArgs ca;
-  ca.part = p2;
-  ca.splits = p.s2;
-  ca.M = M;
-  ca.k = c.top_k;
-  ca.H = c.hidden;
-  ca.weights = weights;
-  ca.slots = static_cast<uint16_t*>(slots);
-  ca.combined = static_cast<uint16_t*>(combined);
   if (e == hipSuccess) e = launch_combine(ca, s);
-  if (e == hipSuccess) e = mark();
+  if (e == hipSuccess) e = mark(4);
 
   h->timed_run = h->timing;
+  h->ev_count = evn;
   return e == hipSuccess ? MOE_DECODE_OK : MOE_DECODE_ERR_HIP;
 }
 
@@ -365,18 +383,15 @@ int moe_decode_set_timing(moe_decode_t h, int32_t enable) {
 }
 
 int moe_decode_last_timing(moe_decode_t h, float* ms, int32_t n) {
-  if (!h || !ms || n < 7) return MOE_DECODE_ERR_INVALID_ARG;
-  for (int i = 0; i < 7; ++i) ms[i] = 0.f;
-  if (!h->timed_run) return MOE_DECODE_ERR_INVALID_ARG;
-  int last = -1;
-  for (int i = 0; i < kEvents; ++i)
-    if (h->ev_used[i]) last = i;
-  if (last < 1) return MOE_DECODE_ERR_INVALID_ARG;
+  if (!h || !ms || n < kStages) return MOE_DECODE_ERR_INVALID_ARG;
+  for (int i = 0; i < kStages; ++i) ms[i] = 0.f;
+  if (!h->timed_run || h->ev_count < 2) return MOE_DECODE_ERR_INVALID_ARG;
+  const int last = h->ev_count - 1;
   if (hipEventSynchronize(h->ev[last]) != hipSuccess) return MOE_DECODE_ERR_HIP;
-  for (int i = 0; i < last && i < 7; ++i) {
+  for (int i = 1; i <= last; ++i) {
     float t = 0.f;
-    if (hipEventElapsedTime(&t, h->ev[i], h->ev[i + 1]) != hipSuccess) return MOE_DECODE_ERR_HIP;
-    ms[i] = t;
+    if (hipEventElapsedTime(&t, h->ev[i - 1], h->ev[i]) != hipSuccess) return MOE_DECODE_ERR_HIP;
+    ms[h->ev_stage[i]] += t;
   }
   return MOE_DECODE_OK;
 }

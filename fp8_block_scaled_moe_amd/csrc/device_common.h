@@ -17,19 +17,25 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef int int8v_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// OCP e4m3 byte nearest to v, ties to the even mantissa, magnitudes at or
-// beyond the 448/480 midpoint saturating to 448 (0x7E). Finite inputs only.
-__device__ __forceinline__ uint32_t e4m3_encode(float v) {
-  const uint32_t bits = __float_as_uint(v);
-  const uint32_t sign = (bits >> 24) & 0x80u;
-  const float a = fabsf(v);
-  if (!(a < 464.f)) return sign | 0x7Eu;
-  int binade = (int)((bits >> 23) & 0xFFu) - 127;  // exponent of a (f32 subnormals read -127)
-  int E = binade < -6 ? -6 : binade;                // below 2^-6 the grid is 2^-9
-  int q = (int)rintf(ldexpf(a, 3 - E));             // exact scaling, ties-to-even round
-  if (q >= 16) { E += 1; q = 8; }                   // rounded into the next binade
-  const uint32_t code = q >= 8 ? (uint32_t)(((E + 7) << 3) | (q - 8)) : (uint32_t)q;
-  return sign | code;
+// OCP e4m3 bytes of four values, nearest with ties to the even mantissa,
+// saturating to +-448, packed low byte first. Clamping to +-448 first and
+// then rounding to nearest-even gives exactly the saturating rounding for
+// finite inputs; gfx950 converts FP32 pairs to OCP e4m3 natively (round to
+// nearest even in the default mode).
+__device__ __forceinline__ uint32_t e4m3x4_encode(float a, float b, float c, float d) {
+  a = __builtin_amdgcn_fmed3f(a, -kFp8Max, kFp8Max);
+  b = __builtin_amdgcn_fmed3f(b, -kFp8Max, kFp8Max);
+  c = __builtin_amdgcn_fmed3f(c, -kFp8Max, kFp8Max);
+  d = __builtin_amdgcn_fmed3f(d, -kFp8Max, kFp8Max);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+__device__ __forceinline__ uint32_t e4m3x2_encode(float a, float b) {
+  a = __builtin_amdgcn_fmed3f(a, -kFp8Max, kFp8Max);
+  b = __builtin_amdgcn_fmed3f(b, -kFp8Max, kFp8Max);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }
 
 // Two e4m3 bytes of `word` (bytes 0,1 when hi == false, bytes 2,3 when true)

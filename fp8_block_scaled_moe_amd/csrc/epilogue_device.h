@@ -1,0 +1,76 @@
+// Device bodies of the two small steps around the GEMMs. Both the separate
+// kernels (epilogues.hip) and the GEMM kernels' last-arriver epilogues
+// (expert_gemm.hip) call these, so the arithmetic is one and the same.
+#pragma once
+
+#include "kernels.h"
+#include "device_common.h"
+
+namespace moe {
+
+// One wave: the fixed-order sum of GEMM1's split partials for route r and
+// 128-block c of the hidden, the clamped SwiGLU and the FP8 hidden block
+// (vLLM "mega_moe" page, hidden_block): up = clamp(u, -L, L),
+// gate = min(g, L), act = (gate / (1 + exp(-gate))) * up in FP32 operations
+// with the exp correctly rounded, scale = max(amax, 1e-10) / 448,
+// q = e4m3(act / scale). Rows 0..I-1 of GEMM1 are up, I..2I-1 gate.
+__device__ __forceinline__ void swiglu_route_block(const SwigluArgs& a, int r, int c, int lane) {
+  const int nblk = a.I / kTile;
+  const int j = c * kTile + 2 * lane;
+  const size_t row = (size_t)2 * a.I;
+  float up0 = 0.f, up1 = 0.f, g0 = 0.f, g1 = 0.f;
+#pragma unroll 4
+  for (int s = 0; s < a.splits; ++s) {
+    const float* p = a.part + ((size_t)s * a.R + r) * row;
+    const float2 u = *reinterpret_cast<const float2*>(p + j);
+    const float2 g = *reinterpret_cast<const float2*>(p + a.I + j);
+    up0 += u.x;
+    up1 += u.y;
+    g0 += g.x;
+    g1 += g.y;
+  }
+  const float L = a.limit;
+  up0 = fminf(fmaxf(up0, -L), L);
+  up1 = fminf(fmaxf(up1, -L), L);
+  g0 = fminf(g0, L);
+  g1 = fminf(g1, L);
+  // exp rounded once to FP32 from FP64, then the add, divide and product in
+  // FP32 in this order: the FP8 codes below are decided from these values.
+  const float e0 = (float)exp(-(double)g0), e1 = (float)exp(-(double)g1);
+  const float act0 = (g0 / (1.f + e0)) * up0;
+  const float act1 = (g1 / (1.f + e1)) * up1;
+  const float amax = group_max<kWave>(fmaxf(fabsf(act0), fabsf(act1)));
+  const float s = fmaxf(amax, kAmaxFloor) / kFp8Max;
+  const uint32_t q = e4m3x2_encode(act0 / s, act1 / s);
+  *reinterpret_cast<uint16_t*>(a.hq + (size_t)r * a.I + j) = (uint16_t)q;
+  if (lane == 0) a.hs[(size_t)r * nblk + c] = s;
+}
+
+// The whole workgroup (256 threads): token t, hidden columns
+// [col0, col0 + 64). Each slot value is the fixed-order sum of GEMM2's split
+// partials rounded once to BF16; combined = BF16(sum_j w[t, j] * slot_j) with
+// the FP32 sum in pick order -- the routing weights applied once, at the end
+// (nvfp4-megamoe-kernel README, slot representation). `lds` holds k * 64
+// floats. Contains a barrier: every thread of the workgroup must call it.
+__device__ __forceinline__ void combine_token_tile(const CombineArgs& a, int t, int col0, float* lds) {
+  const int tid = threadIdx.x;
+  const int c = tid & 63, jg = tid >> 6;
+  const int R = a.M * a.k;
+  for (int j = jg; j < a.k; j += 4) {
+    const int r = t * a.k + j;
+    float v = 0.f;
+#pragma unroll 4
+    for (int s = 0; s < a.splits; ++s) v += a.part[((size_t)s * R + r) * a.H + col0 + c];
+    const uint32_t b = bf16_bits(v);
+    a.slots[(size_t)r * a.H + col0 + c] = (uint16_t)b;
+    lds[j * 64 + c] = bf16_value(b);
+  }
+  __syncthreads();
+  if (tid < 64) {
+    float acc = 0.f;
+    for (int j = 0; j < a.k; ++j) acc = fmaf(a.weights[(size_t)t * a.k + j], lds[j * 64 + c], acc);
+    a.combined[(size_t)t * a.H + col0 + c] = (uint16_t)bf16_bits(acc);
+  }
+}
+
+}  // namespace moe

@@ -12,7 +12,8 @@
 // for all of its routes (up to 8 or 16 per pass); untouched experts are never
 // read. The grid is sized for the largest possible number of distinct
 // experts; workgroups past the actual count exit at once, so no host
-// synchronisation is needed.
+// synchronisation is needed. The first weight blocks are requested before
+// the activations are staged, so the weight stream starts at once.
 #include "kernels.h"
 #include "device_common.h"
 
@@ -21,9 +22,10 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kPrefetch = 4;  // 128-K blocks of weights in flight per wave
+constexpr int kStageBatch = 4;
 
 struct Unit {
-  int e, cnt, off, tile, split, kb0, nb;
+  int ui, e, cnt, off, tile, split, kb0, nb;
 };
 
 __device__ __forceinline__ bool decode_unit(const GemmArgs& a, Unit& u) {
@@ -31,16 +33,49 @@ __device__ __forceinline__ bool decode_unit(const GemmArgs& a, Unit& u) {
   const int per_expert = a.tiles * a.splits;
   const int unit = blockIdx.x;
   if (unit >= U * per_expert) return false;
-  const int ui = unit / per_expert;
-  const int rem = unit - ui * per_expert;
+  u.ui = unit / per_expert;
+  const int rem = unit - u.ui * per_expert;
   u.tile = rem / a.splits;
   u.split = rem - u.tile * a.splits;
-  u.e = a.b.uexp[ui];
-  u.cnt = a.b.ucnt[ui];
-  u.off = a.b.uoff[ui];
+  u.e = a.b.uexp[u.ui];
+  u.cnt = a.b.ucnt[u.ui];
+  u.off = a.b.uoff[u.ui];
   u.kb0 = u.split * a.ks;
   u.nb = min(a.ks, a.nkb - u.kb0);
   return true;
+}
+
+// Activations of routes rts[0..nr) for the unit's K range, widened exactly to
+// F16 into dst (route r at dst + r * stride halves). Loads of up to
+// kStageBatch chunks per thread are issued before any is converted.
+__device__ __forceinline__ void stage_f16(const GemmArgs& a, const Unit& u, const int* rts, int nr,
+                                          _Float16* dst, int stride) {
+  const int per_route = u.nb * 16;  // 8-byte chunks
+  const int chunks = nr * per_route;
+  for (int base = 0; base < chunks; base += kStageBatch * kThreads) {
+    uint2 v[kStageBatch];
+#pragma unroll
+    for (int q = 0; q < kStageBatch; ++q) {
+      const int i = base + q * kThreads + threadIdx.x;
+      if (i < chunks) {
+        const int r = i / per_route, rem = i - r * per_route;
+        const size_t row = (size_t)(rts[r] / a.act_div);
+        v[q] = *reinterpret_cast<const uint2*>(a.aq + row * a.K + (size_t)u.kb0 * kTile + rem * 8);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kStageBatch; ++q) {
+      const int i = base + q * kThreads + threadIdx.x;
+      if (i < chunks) {
+        const int r = i / per_route, rem = i - r * per_route;
+        half2_t* d = reinterpret_cast<half2_t*>(dst + r * stride + rem * 8);
+        d[0] = e4m3x2_to_f16x2<false>(v[q].x);
+        d[1] = e4m3x2_to_f16x2<true>(v[q].x);
+        d[2] = e4m3x2_to_f16x2<false>(v[q].y);
+        d[3] = e4m3x2_to_f16x2<true>(v[q].y);
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -63,24 +98,26 @@ __global__ __launch_bounds__(kThreads) void gemm_valu_kernel(GemmArgs a) {
   const float* wsr =
       a.ws + ((size_t)u.e * (a.N / kTile) + (u.tile * kRowsPerWg) / kTile) * a.nkb + u.kb0;
 
+  u32x4_t na[kPrefetch], nb_[kPrefetch];
+  auto prefetch = [&]() {
+#pragma unroll
+    for (int q = 0; q < kPrefetch; ++q) {
+      if (q < u.nb) {
+        na[q] = load_stream16(pa + q * kTile);
+        nb_[q] = load_stream16(pb + q * kTile);
+      }
+    }
+  };
+  prefetch();
+
   for (int c0 = 0; c0 < u.cnt; c0 += kValuRoutes) {
     const int nr = min(kValuRoutes, u.cnt - c0);
     if (c0) __syncthreads();
     if (tid < nr) rts[tid] = a.b.routes[u.off + c0 + tid];
     __syncthreads();
-    // Stage the routes' activations for this split as exact F16, and the
-    // per-block products of the two scales.
-    const int chunks = nr * u.nb * 16;  // 8-byte chunks
-    for (int i = tid; i < chunks; i += kThreads) {
-      const int r = i / (u.nb * 16), rem = i - r * (u.nb * 16);
-      const size_t row = (size_t)(rts[r] / a.act_div);
-      const uint2 v = *reinterpret_cast<const uint2*>(a.aq + row * a.K + (size_t)u.kb0 * kTile + rem * 8);
-      half2_t* dst = reinterpret_cast<half2_t*>(&xh[r * kMaxKs * kTile + rem * 8]);
-      dst[0] = e4m3x2_to_f16x2<false>(v.x);
-      dst[1] = e4m3x2_to_f16x2<true>(v.x);
-      dst[2] = e4m3x2_to_f16x2<false>(v.y);
-      dst[3] = e4m3x2_to_f16x2<true>(v.y);
-    }
+    // the routes' activations for this split as exact F16, and the per-block
+    // products of the two scales
+    stage_f16(a, u, rts, nr, xh, kMaxKs * kTile);
     for (int i = tid; i < nr * u.nb; i += kThreads) {
       const int r = i / u.nb, b = i - r * u.nb;
       const size_t row = (size_t)(rts[r] / a.act_div);
@@ -92,14 +129,6 @@ __global__ __launch_bounds__(kThreads) void gemm_valu_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < kValuRoutes; ++i) acc_a[i] = acc_b[i] = 0.f;
 
-    u32x4_t na[kPrefetch], nb_[kPrefetch];
-#pragma unroll
-    for (int q = 0; q < kPrefetch; ++q) {
-      if (q < u.nb) {
-        na[q] = load_stream16(pa + q * kTile);
-        nb_[q] = load_stream16(pb + q * kTile);
-      }
-    }
     for (int b0 = 0; b0 < u.nb; b0 += kPrefetch) {
       u32x4_t ca[kPrefetch], cb[kPrefetch];
 #pragma unroll
@@ -159,22 +188,37 @@ __global__ __launch_bounds__(kThreads) void gemm_valu_kernel(GemmArgs a) {
         }
       }
     }
+    if (c0 + kValuRoutes < u.cnt) prefetch();
   }
 }
 
 // ---------------------------------------------------------------------------
-// MFMA inner product: one v_mfma_f32_16x16x128_f8f6f4 per wave and 128-K
-// block gives the 16 rows x 16 routes block partial in FP32; it is scaled and
-// added to the running sum at once. Lane l feeds row l % 16 (weights) and
-// route l % 16 (activations) with 32 bytes of the block: bytes 16g..16g+15
-// and 64+16g..64+16g+15 for g = l / 16. A and B share that byte-to-slot map,
-// so the instruction still sums exactly the block's 128 products, while every
-// weight load instruction reads 64 contiguous bytes of 16 rows.
+// MFMA inner product. Weights and activations widen exactly from e4m3 to F16
+// and feed v_mfma_f32_16x16x32_f16: four instructions per wave and 128-K block
+// give the 16 rows x 16 routes block partial, which is scaled and added to the
+// running FP32 sum at once. (The FP8-input 16x16x128 instruction would take
+// the bytes directly, but its internal 128-term sum truncates: measured on
+// MI355X up to ~1e-4 of sum |terms|, enough to move FP8 hidden codes; the F16
+// instruction's sum is as accurate as FP32 accumulation.)
+// Lane l feeds row l % 16 (weights) and route l % 16 (activations) with 32
+// values of the block: bytes 16g..16g+15 and 64+16g..64+16g+15, g = l / 16.
+// A and B use the same value-to-slot map, so each block's 128 products are
+// summed exactly once, and every weight load instruction reads 64 contiguous
+// bytes of 16 rows.
 // ---------------------------------------------------------------------------
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ half8_t cat4(half2_t a, half2_t b, half2_t c, half2_t d) {
+  return half8_t{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
 __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmArgs a) {
-  __shared__ __align__(16) uint8_t xb[kMfmaRoutes * kMaxKs * kTile];
-  __shared__ float sc[kMaxKs * kMfmaRoutes];  // [block][route]
-  __shared__ int rts[kMfmaRoutes];
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int nrp = a.pass_routes;                    // routes per pass, <= 16
+  const int stride = a.ks * kTile + 8;             // halves per route row: +16 B against bank conflicts
+  _Float16* xh = reinterpret_cast<_Float16*>(smem);
+  float* sc = reinterpret_cast<float*>(smem + (size_t)nrp * stride * 2);  // [ks][16]
+  int* rts = reinterpret_cast<int*>(sc + a.ks * kMfmaRoutes);
 
   Unit u;
   if (!decode_unit(a, u)) return;
@@ -185,18 +229,24 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmArgs a) {
   const float* wsr =
       a.ws + ((size_t)u.e * (a.N / kTile) + (u.tile * kRowsPerWg) / kTile) * a.nkb + u.kb0;
 
-  for (int c0 = 0; c0 < u.cnt; c0 += kMfmaRoutes) {
-    const int nr = min(kMfmaRoutes, u.cnt - c0);
+  u32x4_t nlo[kPrefetch], nhi[kPrefetch];
+  auto prefetch = [&]() {
+#pragma unroll
+    for (int q = 0; q < kPrefetch; ++q) {
+      if (q < u.nb) {
+        nlo[q] = load_stream16(pw + q * kTile);
+        nhi[q] = load_stream16(pw + q * kTile + 64);
+      }
+    }
+  };
+  prefetch();
+
+  for (int c0 = 0; c0 < u.cnt; c0 += nrp) {
+    const int nr = min(nrp, u.cnt - c0);
     if (c0) __syncthreads();
     if (tid < nr) rts[tid] = a.b.routes[u.off + c0 + tid];
     __syncthreads();
-    const int chunks = nr * u.nb * 8;  // 16-byte chunks
-    for (int i = tid; i < chunks; i += kThreads) {
-      const int r = i / (u.nb * 8), rem = i - r * (u.nb * 8);
-      const size_t row = (size_t)(rts[r] / a.act_div);
-      *reinterpret_cast<u32x4_t*>(&xb[r * kMaxKs * kTile + rem * 16]) =
-          *reinterpret_cast<const u32x4_t*>(a.aq + row * a.K + (size_t)u.kb0 * kTile + rem * 16);
-    }
+    stage_f16(a, u, rts, nr, xh, stride);
     for (int i = tid; i < kMfmaRoutes * u.nb; i += kThreads) {
       const int r = i % kMfmaRoutes, b = i / kMfmaRoutes;
       float v = 0.f;
@@ -209,17 +259,10 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmArgs a) {
     __syncthreads();
 
     const bool live = col < nr;
-    const uint8_t* xr = &xb[col * kMaxKs * kTile + g * 16];
+    // lanes past the pass's routes read route 0's row; their columns are dropped
+    const _Float16* xr = xh + (live ? col : 0) * stride + g * 16;
     float4_t acc = {0.f, 0.f, 0.f, 0.f};
     const float4_t zero = {0.f, 0.f, 0.f, 0.f};
-    u32x4_t nlo[kPrefetch], nhi[kPrefetch];
-#pragma unroll
-    for (int q = 0; q < kPrefetch; ++q) {
-      if (q < u.nb) {
-        nlo[q] = load_stream16(pw + q * kTile);
-        nhi[q] = load_stream16(pw + q * kTile + 64);
-      }
-    }
     for (int b0 = 0; b0 < u.nb; b0 += kPrefetch) {
       u32x4_t clo[kPrefetch], chi[kPrefetch];
 #pragma unroll
@@ -239,15 +282,20 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmArgs a) {
       for (int q = 0; q < kPrefetch; ++q) {
         const int b = b0 + q;
         if (b < u.nb) {
-          u32x4_t xlo = *reinterpret_cast<const u32x4_t*>(xr + b * kTile);
-          u32x4_t xhi = *reinterpret_cast<const u32x4_t*>(xr + b * kTile + 64);
-          if (!live) xlo = xhi = u32x4_t{0u, 0u, 0u, 0u};
-          const int8v_t av = {(int)clo[q][0], (int)clo[q][1], (int)clo[q][2], (int)clo[q][3],
-                              (int)chi[q][0], (int)chi[q][1], (int)chi[q][2], (int)chi[q][3]};
-          const int8v_t bv = {(int)xlo[0], (int)xlo[1], (int)xlo[2], (int)xlo[3],
-                              (int)xhi[0], (int)xhi[1], (int)xhi[2], (int)xhi[3]};
-          const float4_t p =
-              __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, zero, 0, 0, 0, 0, 0, 0);
+          const half8_t* xb = reinterpret_cast<const half8_t*>(xr + b * kTile);
+          const half8_t x0 = xb[0], x1 = xb[1], x2 = xb[8], x3 = xb[9];  // +0, +8, +64, +72 halves
+          const half8_t w0 = cat4(e4m3x2_to_f16x2<false>(clo[q][0]), e4m3x2_to_f16x2<true>(clo[q][0]),
+                                  e4m3x2_to_f16x2<false>(clo[q][1]), e4m3x2_to_f16x2<true>(clo[q][1]));
+          const half8_t w1 = cat4(e4m3x2_to_f16x2<false>(clo[q][2]), e4m3x2_to_f16x2<true>(clo[q][2]),
+                                  e4m3x2_to_f16x2<false>(clo[q][3]), e4m3x2_to_f16x2<true>(clo[q][3]));
+          const half8_t w2 = cat4(e4m3x2_to_f16x2<false>(chi[q][0]), e4m3x2_to_f16x2<true>(chi[q][0]),
+                                  e4m3x2_to_f16x2<false>(chi[q][1]), e4m3x2_to_f16x2<true>(chi[q][1]));
+          const half8_t w3 = cat4(e4m3x2_to_f16x2<false>(chi[q][2]), e4m3x2_to_f16x2<true>(chi[q][2]),
+                                  e4m3x2_to_f16x2<false>(chi[q][3]), e4m3x2_to_f16x2<true>(chi[q][3]));
+          float4_t p = __builtin_amdgcn_mfma_f32_16x16x32_f16(w0, x0, zero, 0, 0, 0);
+          p = __builtin_amdgcn_mfma_f32_16x16x32_f16(w1, x1, p, 0, 0, 0);
+          p = __builtin_amdgcn_mfma_f32_16x16x32_f16(w2, x2, p, 0, 0, 0);
+          p = __builtin_amdgcn_mfma_f32_16x16x32_f16(w3, x3, p, 0, 0, 0);
           const float s = sc[b * kMfmaRoutes + col];
           acc[0] = fmaf(p[0], s, acc[0]);
           acc[1] = fmaf(p[1], s, acc[1]);
@@ -260,10 +308,15 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmArgs a) {
       float* dst = a.part + ((size_t)u.split * a.R + rts[col]) * a.N + row0 + 4 * g;
       *reinterpret_cast<float4_t*>(dst) = acc;
     }
+    if (c0 + nrp < u.cnt) prefetch();
   }
 }
 
 }  // namespace
+
+size_t gemm_mfma_lds_bytes(int pass_routes, int ks) {
+  return (size_t)pass_routes * (ks * kTile + 8) * 2 + (size_t)ks * kMfmaRoutes * 4 + kMfmaRoutes * 4;
+}
 
 hipError_t launch_gemm_valu(const GemmArgs& a, int grid, hipStream_t s) {
   hipLaunchKernelGGL(gemm_valu_kernel, dim3(grid), dim3(kThreads), 0, s, a);
@@ -271,7 +324,8 @@ hipError_t launch_gemm_valu(const GemmArgs& a, int grid, hipStream_t s) {
 }
 
 hipError_t launch_gemm_mfma(const GemmArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(gemm_mfma_kernel, dim3(grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(gemm_mfma_kernel, dim3(grid), dim3(kThreads),
+                     gemm_mfma_lds_bytes(a.pass_routes, a.ks), s, a);
   return hipGetLastError();
 }
 

@@ -8,6 +8,7 @@
 namespace moe {
 
 constexpr int kTile = 128;  // block size of every FP8 scale (K and N)
+constexpr int kMaxTopK = 32;
 
 // Distinct-expert buckets built by the routing kernel (device memory).
 struct Buckets {
@@ -34,6 +35,22 @@ struct RouteQuantArgs {
   Buckets b;
 };
 
+struct SwigluArgs {
+  const float* part;    // [splits, R, 2I]
+  int splits, R, I;
+  float limit;
+  uint8_t* hq;          // [R, I]
+  float* hs;            // [R, I/128]
+};
+
+struct CombineArgs {
+  const float* part;    // [splits, R, H]
+  int splits, M, k, H;
+  const float* weights; // [M, k]
+  uint16_t* slots;      // [M*k, H] bf16
+  uint16_t* combined;   // [M, H] bf16
+};
+
 // One block-scaled GEMM pass over the touched experts: for every route r of
 // distinct expert u and every weight row n,
 //   part[split, r, n] = sum_{b in split} ws[e, n/128, b] * as[row(r), b] *
@@ -51,22 +68,7 @@ struct GemmArgs {
   int splits, ks;       // K splits and 128-blocks per split
   int R;                // routes (row stride of part)
   int act_div;
-};
-
-struct SwigluArgs {
-  const float* part;    // [splits, R, 2I]
-  int splits, R, I;
-  float limit;
-  uint8_t* hq;          // [R, I]
-  float* hs;            // [R, I/128]
-};
-
-struct CombineArgs {
-  const float* part;    // [splits, R, H]
-  int splits, M, k, H;
-  const float* weights; // [M, k]
-  uint16_t* slots;      // [M*k, H] bf16
-  uint16_t* combined;   // [M, H] bf16
+  int pass_routes;      // MFMA path: routes staged per pass (<= 16)
 };
 
 // Maximum 128-blocks of K per split (bounds the LDS staging of activations).
@@ -74,11 +76,14 @@ constexpr int kMaxKs = 16;
 constexpr int kRowsPerWg = 64;
 constexpr int kValuRoutes = 8;   // routes per pass of the VALU inner product
 constexpr int kMfmaRoutes = 16;  // routes per pass of the MFMA inner product
+constexpr size_t kMfmaLdsBudget = 40 * 1024;  // keeps three workgroups per CU
+constexpr size_t kMaxRouteLds = 64 * 1024;
 
-size_t route_quant_lds_bytes(int E, int words);
+size_t route_quant_lds_bytes(int E, int words, int routes);
 hipError_t launch_route_quant(const RouteQuantArgs& a, hipStream_t s);
 hipError_t launch_gemm_valu(const GemmArgs& a, int grid, hipStream_t s);
 hipError_t launch_gemm_mfma(const GemmArgs& a, int grid, hipStream_t s);
+size_t gemm_mfma_lds_bytes(int pass_routes, int ks);
 hipError_t launch_swiglu_requant(const SwigluArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_codec_check(const float* in, uint8_t* q, float* dq, int n, hipStream_t s);

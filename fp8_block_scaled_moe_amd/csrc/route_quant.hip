@@ -1,5 +1,4 @@
-// Routing, activation quantisation and expert bucketing: one workgroup per
-// token, the last workgroup to finish groups the routes by expert.
+// Routing, activation quantisation and expert bucketing.
 //
 // Routing follows the vLLM "mega_moe" page (top_k_pick, _ordered): FP32
 // sigmoid scores, FP32 keys score + bias compared through a monotone integer
@@ -9,14 +8,20 @@
 // scale = max(amax, 1e-10) / 448 (IEEE divide), optionally rounded up to a
 // power of two after flooring it at 1e-10, then v * (1 / scale) encoded to
 // e4m3.
+//
+// Launch: one 1024-thread workgroup per 4 tokens; waves 0..3 (one per SIMD)
+// each route one token, then all 16 waves quantise. With one workgroup the
+// routes are grouped by expert right away in LDS; with several, the last
+// workgroup to arrive (atomic counter, reset by that workgroup) does it.
 #include "kernels.h"
 #include "device_common.h"
 
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kMaxPerLane = 16;  // experts per lane: E <= 1024
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / kWave;  // 16
+constexpr int kTokensPerWg = 4;           // one routing wave per SIMD
 
 // Monotone image of an FP32 value in uint32: a > b as floats (with -0 < +0)
 // iff key(a) > key(b). Negatives flip every bit, the rest flip the sign bit.
@@ -30,18 +35,46 @@ __device__ __forceinline__ float sigmoid_f32(float z) {
   return (float)(1.0 / (1.0 + exp(-(double)z)));
 }
 
-// Wave 0 of the token's workgroup: picks and weights of token t.
-__device__ void route_token(const RouteQuantArgs& a, int t, int lane) {
+template <int kCtrl>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)v, kCtrl, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), kCtrl, 0xF, 0xF, false);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Wave-wide maximum: DPP permutations inside each row of 16 lanes (swap
+// neighbours, swap pairs, half-row mirror, row mirror), then the four row
+// results through readlane. Every lane returns the same value.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = max_u64(v, dpp_u64<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = max_u64(v, dpp_u64<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = max_u64(v, dpp_u64<0x141>(v));  // row_half_mirror
+  v = max_u64(v, dpp_u64<0x140>(v));  // row_mirror
+  return max_u64(max_u64(readlane_u64(v, 0), readlane_u64(v, 16)),
+                 max_u64(readlane_u64(v, 32), readlane_u64(v, 48)));
+}
+
+// One wave: the picks and weights of token t. Lane l holds experts
+// l + 64 j for j < kPer (kPer >= E / 64).
+template <int kPer>
+__device__ void route_token(const RouteQuantArgs& a, int t, int lane, int* ids_l) {
   const int E = a.E;
-  const int per = (E + kWave - 1) / kWave;
-  float score[kMaxPerLane];
-  uint64_t key[kMaxPerLane];
+  float score[kPer];
+  uint64_t key[kPer];
 #pragma unroll
-  for (int j = 0; j < kMaxPerLane; ++j) {
+  for (int j = 0; j < kPer; ++j) {
     score[j] = 0.f;
     key[j] = 0;
     const int e = lane + kWave * j;
-    if (j < per && e < E) {
+    if (e < E) {
       const size_t at = (size_t)t * E + e;
       const float z = a.logits_bf16 ? bf16_value(((const uint16_t*)a.logits)[at])
                                     : ((const float*)a.logits)[at];
@@ -56,23 +89,22 @@ __device__ void route_token(const RouteQuantArgs& a, int t, int lane) {
   int my_id = 0;
   float my_score = 0.f;
   for (int r = 0; r < a.k; ++r) {
-    uint64_t best = 0;
+    uint64_t best = key[0];
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j)
-      if (j < per) best = key[j] > best ? key[j] : best;
+    for (int j = 1; j < kPer; ++j) best = max_u64(best, key[j]);
     best = wave_max_u64(best);
     const int winner = (int)(0xFFFFFFFFu - (uint32_t)best);
     const int owner = winner & (kWave - 1);
     const int slot = winner / kWave;
     float s_slot = 0.f;
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
+    for (int j = 0; j < kPer; ++j) {
       if (j == slot) {
         s_slot = score[j];
         if (lane == owner) key[j] = 0;
       }
     }
-    const float s = __shfl(s_slot, owner, kWave);
+    const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_slot), owner));
     total = total + s;
     if (lane == r) {
       my_id = winner;
@@ -81,87 +113,115 @@ __device__ void route_token(const RouteQuantArgs& a, int t, int lane) {
   }
   if (lane < a.k) {
     const float w = (my_score / total) * a.routed_scale;
-    a.ids[(size_t)t * a.k + lane] = my_id;
-    a.weights[(size_t)t * a.k + lane] = w;
+    const size_t at = (size_t)t * a.k + lane;
+    a.ids[at] = my_id;
+    a.weights[at] = w;
+    ids_l[at] = my_id;
   }
 }
 
-// Threads [first, first + count) of the workgroup quantise token t: eight
-// lanes per 128-block, sixteen values per lane.
-__device__ void quant_token(const RouteQuantArgs& a, int t, int first, int count) {
-  const int me = threadIdx.x - first;
-  const int groups = count / 8;
-  const int g = me / 8, sub = me % 8;
+__device__ void route_token_any(const RouteQuantArgs& a, int t, int lane, int* ids_l) {
+  const int per = (a.E + kWave - 1) / kWave;
+  if (per <= 1) route_token<1>(a, t, lane, ids_l);
+  else if (per <= 2) route_token<2>(a, t, lane, ids_l);
+  else if (per <= 4) route_token<4>(a, t, lane, ids_l);
+  else if (per <= 8) route_token<8>(a, t, lane, ids_l);
+  else route_token<16>(a, t, lane, ids_l);
+}
+
+// All threads: the 128-blocks of tokens [t0, t0 + ntok), eight lanes per
+// block and sixteen values per lane; loads of up to four blocks per lane are
+// issued before any is used.
+__device__ void quant_tokens(const RouteQuantArgs& a, int t0, int ntok) {
+  constexpr int kGroups = kThreads / 8;
+  constexpr int kBatch = 4;
+  const int group = threadIdx.x / 8, sub = threadIdx.x % 8;
   const int nblk = a.H / kTile;
-  for (int blk = g; blk < nblk; blk += groups) {
-    const size_t base = (size_t)t * a.H + (size_t)blk * kTile + sub * 16;
-    const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(a.x + base);
-    const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(a.x + base + 8);
-    float v[16];
+  const int items = ntok * nblk;
+  for (int base = 0; base < items; base += kBatch * kGroups) {
+    u32x4_t lo[kBatch], hi[kBatch];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = bf16_value(lo[i] & 0xFFFFu);
-      v[2 * i + 1] = bf16_value(lo[i] >> 16);
-      v[8 + 2 * i] = bf16_value(hi[i] & 0xFFFFu);
-      v[8 + 2 * i + 1] = bf16_value(hi[i] >> 16);
+    for (int q = 0; q < kBatch; ++q) {
+      const int item = base + q * kGroups + group;
+      if (item < items) {
+        const size_t at = (size_t)(t0 + item / nblk) * a.H + (size_t)(item % nblk) * kTile + sub * 16;
+        lo[q] = *reinterpret_cast<const u32x4_t*>(a.x + at);
+        hi[q] = *reinterpret_cast<const u32x4_t*>(a.x + at + 8);
+      }
     }
-    float amax = kAmaxFloor;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    amax = group_max<8>(amax);
-    float s = amax / kFp8Max;
-    if (a.ue8m0) {
-      const uint32_t b = __float_as_uint(fmaxf(s, kAmaxFloor));
-      s = __uint_as_float(((b >> 23) + ((b & 0x7FFFFFu) != 0u)) << 23);
-    }
-    const float inv = 1.0f / s;
-    u32x4_t q;
+    for (int q = 0; q < kBatch; ++q) {
+      const int item = base + q * kGroups + group;
+      if (item < items) {  // the same for all eight lanes of a group
+        float v[16];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      q[w] = e4m3_encode(v[4 * w] * inv) | (e4m3_encode(v[4 * w + 1] * inv) << 8) |
-             (e4m3_encode(v[4 * w + 2] * inv) << 16) | (e4m3_encode(v[4 * w + 3] * inv) << 24);
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = bf16_value(lo[q][i] & 0xFFFFu);
+          v[2 * i + 1] = bf16_value(lo[q][i] >> 16);
+          v[8 + 2 * i] = bf16_value(hi[q][i] & 0xFFFFu);
+          v[8 + 2 * i + 1] = bf16_value(hi[q][i] >> 16);
+        }
+        float amax = kAmaxFloor;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+        amax = group_max<8>(amax);
+        float s = amax / kFp8Max;
+        if (a.ue8m0) {
+          const uint32_t b = __float_as_uint(fmaxf(s, kAmaxFloor));
+          s = __uint_as_float(((b >> 23) + ((b & 0x7FFFFFu) != 0u)) << 23);
+        }
+        const float inv = 1.0f / s;
+        u32x4_t out;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          out[w] = e4m3x4_encode(v[4 * w] * inv, v[4 * w + 1] * inv, v[4 * w + 2] * inv,
+                                 v[4 * w + 3] * inv);
+        }
+        const int t = t0 + item / nblk, blk = item % nblk;
+        const size_t at = (size_t)t * a.H + (size_t)blk * kTile + sub * 16;
+        *reinterpret_cast<u32x4_t*>(a.xq + at) = out;
+        if (sub == 0) a.xs[(size_t)t * nblk + blk] = s;
+      }
     }
-    *reinterpret_cast<u32x4_t*>(a.xq + base) = q;
-    if (sub == 0) a.xs[(size_t)t * nblk + blk] = s;
   }
 }
 
-// The last workgroup: routes grouped by expert, experts in ascending order,
-// each expert's routes in ascending token order.
-__device__ void bucket_routes(const RouteQuantArgs& a, unsigned char* lds) {
-  const int tid = threadIdx.x;
-  const int E = a.E, W = a.words, R = a.M * a.k;
-  uint64_t* mask = reinterpret_cast<uint64_t*>(lds);               // [E][W]
-  int* first = reinterpret_cast<int*>(lds + (size_t)E * W * 8);    // [E]
-  int* wave_tot = first + E;                                       // [2][4]
+struct Lds {
+  uint64_t* mask;  // [E][W] token bitmask of every expert
+  int* ids;        // [M*k] picks
+  int* first;      // [E] first route slot of each expert
+  int* scratch;    // [2 * 16] per-wave scan totals
+};
 
-  for (int i = tid; i < E * W; i += kThreads) mask[i] = 0;
+__device__ __forceinline__ Lds carve(unsigned char* lds, int E, int W, int R) {
+  Lds l;
+  l.mask = reinterpret_cast<uint64_t*>(lds);
+  l.ids = reinterpret_cast<int*>(lds + (size_t)E * W * 8);
+  l.first = l.ids + R;
+  l.scratch = l.first + E;
+  return l;
+}
+
+// Routes grouped by expert, experts ascending, each expert's routes in
+// ascending token order (so ascending route index).
+__device__ void bucket_routes(const RouteQuantArgs& a, const Lds& l) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int E = a.E, W = a.words, R = a.M * a.k;
+  for (int i = tid; i < E * W; i += kThreads) l.mask[i] = 0;
   __syncthreads();
   for (int r = tid; r < R; r += kThreads) {
-    const int e = __hip_atomic_load(a.ids + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int t = r / a.k;
-    atomicOr(reinterpret_cast<unsigned long long*>(&mask[(size_t)e * W + t / 64]),
+    atomicOr(reinterpret_cast<unsigned long long*>(&l.mask[(size_t)l.ids[r] * W + t / 64]),
              1ull << (t % 64));
   }
   __syncthreads();
-
-  // Each thread owns a contiguous run of experts; a block-wide exclusive scan
-  // gives every present expert its rank and its first route slot.
-  const int per = (E + kThreads - 1) / kThreads;  // <= 4
-  int cnt[4];
-  int present = 0, routes = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    cnt[q] = 0;
-    const int e = tid * per + q;
-    if (q < per && e < E) {
-      for (int w = 0; w < W; ++w) cnt[q] += __popcll(mask[(size_t)e * W + w]);
-      present += cnt[q] > 0;
-      routes += cnt[q];
-    }
-  }
-  const int lane = tid & (kWave - 1), wave = tid / kWave;
-  int inc_p = present, inc_r = routes;
+  // thread e owns expert e (E <= 1024); block-wide exclusive scan of
+  // (present, count) gives each present expert its rank and first slot
+  int cnt = 0;
+  if (tid < E)
+    for (int w = 0; w < W; ++w) cnt += __popcll(l.mask[(size_t)tid * W + w]);
+  const int present = cnt > 0;
+  int inc_p = present, inc_r = cnt;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
     const int up_p = __shfl_up(inc_p, o, kWave);
@@ -172,76 +232,73 @@ __device__ void bucket_routes(const RouteQuantArgs& a, unsigned char* lds) {
     }
   }
   if (lane == kWave - 1) {
-    wave_tot[wave] = inc_p;
-    wave_tot[4 + wave] = inc_r;
+    l.scratch[wave] = inc_p;
+    l.scratch[kWaves + wave] = inc_r;
   }
   __syncthreads();
   int base_p = 0, base_r = 0, all_p = 0;
-  for (int w = 0; w < kThreads / kWave; ++w) {
+  for (int w = 0; w < kWaves; ++w) {
+    const int tp = l.scratch[w], tr = l.scratch[kWaves + w];
     if (w < wave) {
-      base_p += wave_tot[w];
-      base_r += wave_tot[4 + w];
+      base_p += tp;
+      base_r += tr;
     }
-    all_p += wave_tot[w];
+    all_p += tp;
   }
-  int u = base_p + inc_p - present;
-  int o = base_r + inc_r - routes;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = tid * per + q;
-    if (q < per && e < E) {
-      first[e] = o;
-      if (cnt[q] > 0) {
-        a.b.uexp[u] = e;
-        a.b.uoff[u] = o;
-        a.b.ucnt[u] = cnt[q];
-        ++u;
-        o += cnt[q];
-      }
-    }
+  if (present) {
+    const int u = base_p + inc_p - 1;
+    const int o = base_r + inc_r - cnt;
+    a.b.uexp[u] = tid;
+    a.b.uoff[u] = o;
+    a.b.ucnt[u] = cnt;
+    l.first[tid] = o;
   }
   if (tid == 0) a.b.ctrl[1] = all_p;
   __syncthreads();
   for (int r = tid; r < R; r += kThreads) {
-    const int e = __hip_atomic_load(a.ids + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int e = l.ids[r];
     const int t = r / a.k;
-    const uint64_t* m = mask + (size_t)e * W;
+    const uint64_t* m = l.mask + (size_t)e * W;
     int before = 0;
     for (int w = 0; w < t / 64; ++w) before += __popcll(m[w]);
     before += __popcll(m[t / 64] & ((1ull << (t % 64)) - 1ull));
-    a.b.routes[first[e] + before] = r;
+    a.b.routes[l.first[e] + before] = r;
   }
 }
 
 __global__ __launch_bounds__(kThreads) void route_quant_kernel(RouteQuantArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   __shared__ int is_last;
-  const int t = blockIdx.x;
-  const int wave = threadIdx.x / kWave;
-  if (wave == 0) {
-    route_token(a, t, threadIdx.x);
-  } else {
-    quant_token(a, t, kWave, kThreads - kWave);
+  const Lds l = carve(lds, a.E, a.words, a.M * a.k);
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int t0 = blockIdx.x * kTokensPerWg;
+  const int ntok = min(kTokensPerWg, a.M - t0);
+  if (wave < ntok) route_token_any(a, t0 + wave, lane, l.ids);
+  quant_tokens(a, t0, ntok);
+  if (gridDim.x == 1) {
+    __syncthreads();
+    bucket_routes(a, l);
+    return;
   }
-  // Publish this token's picks, then count arrivals; the last arrival sees
-  // every token's picks.
+  // Publish this workgroup's picks, then count arrivals; the last arrival
+  // reads every workgroup's picks.
   __threadfence();
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = atomicAdd(a.b.ctrl, 1);
-    is_last = prev == a.M - 1;
-  }
+  if (threadIdx.x == 0) is_last = atomicAdd(a.b.ctrl, 1) == (int)gridDim.x - 1;
   __syncthreads();
   if (!is_last) return;
   __threadfence();
   if (threadIdx.x == 0) __hip_atomic_store(a.b.ctrl, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  bucket_routes(a, lds);
+  for (int r = threadIdx.x; r < a.M * a.k; r += kThreads)
+    l.ids[r] = __hip_atomic_load(a.ids + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  bucket_routes(a, l);
 }
 
 __global__ void codec_check_kernel(const float* in, uint8_t* q, float* dq, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
-  q[i] = (uint8_t)e4m3_encode(in[i]);
+  q[i] = (uint8_t)e4m3x2_encode(in[i], 0.f);
   const uint32_t c = (uint32_t)i & 0xFFu;
   const int variant = (i >> 8) & 3;  // which byte of a word carries the code
   const uint32_t word = c << (8 * variant);
@@ -251,13 +308,14 @@ __global__ void codec_check_kernel(const float* in, uint8_t* q, float* dq, int n
 
 }  // namespace
 
-size_t route_quant_lds_bytes(int E, int words) {
-  return (size_t)E * words * 8 + (size_t)E * 4 + 8 * 4;
+size_t route_quant_lds_bytes(int E, int words, int routes) {
+  return (size_t)E * words * 8 + (size_t)routes * 4 + (size_t)E * 4 + 2 * kWaves * 4;
 }
 
 hipError_t launch_route_quant(const RouteQuantArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(route_quant_kernel, dim3(a.M), dim3(kThreads),
-                     route_quant_lds_bytes(a.E, a.words), s, a);
+  const int grid = (a.M + kTokensPerWg - 1) / kTokensPerWg;
+  hipLaunchKernelGGL(route_quant_kernel, dim3(grid), dim3(kThreads),
+                     route_quant_lds_bytes(a.E, a.words, a.M * a.k), s, a);
   return hipGetLastError();
 }
 

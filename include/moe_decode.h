@@ -177,9 +177,10 @@ int moe_decode_debug_stage(moe_decode_t h, int32_t stage, void* dst, size_t byte
 
 /* Per-kernel timing of subsequent runs with HIP events recorded between the
  * launches (enable != 0; not for use under graph capture). After a run has
- * completed, moe_decode_last_timing writes the milliseconds of each launch
- * in order: route+quant, GEMM1, SwiGLU+requant, GEMM2, combine, shared
- * gate_up, shared down (0 when not run). n is the capacity of ms (>= 7). */
+ * completed, moe_decode_last_timing writes the milliseconds of each launch in
+ * order: route+quant, GEMM1, SwiGLU+requant, GEMM2, combine, shared gate_up,
+ * shared down (0 for a launch that did not run). n is the capacity of ms
+ * (>= 7). */
 int moe_decode_set_timing(moe_decode_t h, int32_t enable);
 int moe_decode_last_timing(moe_decode_t h, float* ms, int32_t n);
 
