@@ -47,6 +47,9 @@ def parse():
     p.add_argument("--sweep", default="", help="comma-separated M values: one JSON line each")
     p.add_argument("--calibrate", action="store_true",
                    help="time a plain 1 GiB device copy and a 4 GiB read-only sum instead")
+    p.add_argument("--with-copy", action="store_true",
+                   help="after the timed steps, run three 256 MiB device copies (a kernel of "
+                        "known traffic to scale hardware byte counters by)")
     return p.parse_args()
 
 
@@ -217,6 +220,12 @@ def main():
             line["cpu_baseline"] = cpu_baseline(inp, r["counted"])
         print(json.dumps(line), flush=True)
     moe.close()
+    if args.with_copy:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
 
 if __name__ == "__main__":

@@ -207,11 +207,11 @@ class MoeDecode:
 
     # -- introspection ------------------------------------------------------
     def plan(self, M: int) -> dict:
-        buf = (ctypes.c_int32 * 7)()
-        rc = lib().moe_decode_plan(self._h, M, buf, 7)
+        buf = (ctypes.c_int32 * 9)()
+        rc = lib().moe_decode_plan(self._h, M, buf, 9)
         if rc != OK:
             raise MoeDecodeError(rc, "moe_decode_plan")
-        keys = ("path", "splits1", "splits2", "ks1", "ks2", "grid1", "grid2")
+        keys = ("path", "splits1", "splits2", "ks1", "ks2", "grid1", "grid2", "tpw1", "tpw2")
         return dict(zip(keys, list(buf)))
 
     def stage(self, name: str, dst: torch.Tensor, stream=None) -> torch.Tensor:

@@ -27,6 +27,7 @@ struct Plan {
   int grid1, grid2;
   int umax;
   int pass_routes;  // MFMA path: routes per pass
+  int tpw1, tpw2;   // 64-row tiles per workgroup
 };
 
 struct Region {
@@ -76,16 +77,36 @@ Plan make_plan(const moe_decode_config& c, int M) {
   const int R = M * c.top_k;
   p.umax = std::min(c.experts, R);
   const int tiles1 = 2 * c.inter / kRowsPerWg, tiles2 = c.hidden / kRowsPerWg;
-  p.path = c.gemm_path == MOE_GEMM_MFMA ? MOE_GEMM_MFMA : MOE_GEMM_VALU;
+  // MFMA costs the same per weight byte for any number of routes of an
+  // expert (up to 16 per pass), VALU dot products cost per route. Measured on
+  // MI355X with every expert taking n routes (E=64, H=7168, I=2048), GEMM1
+  // streams at 6.69/6.67 TB/s (VALU/MFMA) for n=1, 5.68/5.86 for n=4,
+  // 4.10/5.46 for n=8 and 2.01/5.06 for n=16; so MFMA unless every expert has
+  // exactly one route (M = 1).
+  if (c.gemm_path == MOE_GEMM_AUTO)
+    p.path = M == 1 ? MOE_GEMM_VALU : MOE_GEMM_MFMA;
+  else
+    p.path = c.gemm_path;
   // an expert has at most one route per token
   p.pass_routes = std::min(kMfmaRoutes, M);
   int max_ks = kMaxKs;
   if (p.path == MOE_GEMM_MFMA)
     while (max_ks > 1 && gemm_mfma_lds_bytes(p.pass_routes, max_ks) > kMfmaLdsBudget) --max_ks;
-  choose_split(p.umax * tiles1, c.hidden / kTile, c.splits1, max_ks, &p.s1, &p.ks1);
-  choose_split(p.umax * tiles2, c.inter / kTile, c.splits2, max_ks, &p.s2, &p.ks2);
-  p.grid1 = p.umax * tiles1 * p.s1;
-  p.grid2 = p.umax * tiles2 * p.s2;
+  // Staging a unit's activations costs about as much as streaming a few
+  // blocks of weights per route; with many tokens (so many routes per
+  // expert) a workgroup streams several tiles per staging.
+  const int want = M <= 2 ? 1 : (M <= 8 ? 2 : kMaxTpw);
+  auto tiles_per_wg = [&](int tiles) {
+    int t = want;
+    while (tiles % t) t /= 2;
+    return t;
+  };
+  p.tpw1 = tiles_per_wg(tiles1);
+  p.tpw2 = tiles_per_wg(tiles2);
+  choose_split(p.umax * (tiles1 / p.tpw1), c.hidden / kTile, c.splits1, max_ks, &p.s1, &p.ks1);
+  choose_split(p.umax * (tiles2 / p.tpw2), c.inter / kTile, c.splits2, max_ks, &p.s2, &p.ks2);
+  p.grid1 = p.umax * (tiles1 / p.tpw1) * p.s1;
+  p.grid2 = p.umax * (tiles2 / p.tpw2) * p.s2;
   return p;
 }
 
@@ -223,7 +244,7 @@ void moe_decode_destroy(moe_decode_t h) {
 }
 
 int moe_decode_plan(moe_decode_t h, int32_t M, int32_t* out, int32_t n) {
-  if (!h || !out || n < 7 || M < 1) return MOE_DECODE_ERR_INVALID_ARG;
+  if (!h || !out || n < 9 || M < 1) return MOE_DECODE_ERR_INVALID_ARG;
   if (M > h->cfg.max_tokens) return MOE_DECODE_ERR_TOO_MANY_TOKENS;
   const Plan p = make_plan(h->cfg, M);
   out[0] = p.path;
@@ -233,6 +254,8 @@ int moe_decode_plan(moe_decode_t h, int32_t M, int32_t* out, int32_t n) {
   out[4] = p.ks2;
   out[5] = p.grid1;
   out[6] = p.grid2;
+  out[7] = p.tpw1;
+  out[8] = p.tpw2;
   return MOE_DECODE_OK;
 }
 
@@ -335,8 +358,9 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   g1.R = R;
   g1.act_div = c.top_k;
   g1.pass_routes = p.pass_routes;
+  g1.tpw = p.tpw1;
   if (e == hipSuccess)
-    e = p.path == MOE_GEMM_MFMA ? launch_gemm_mfma(g1, p.grid1, s) : launch_gemm_valu(g1, p.grid1, s);
+    e = p.path == MOE_GEMM_MFMA ? launch_gemm_mfma(g1, 1, p.grid1, s) : launch_gemm_valu(g1, 1, p.grid1, s);
   if (e == hipSuccess) e = mark(1);
 
   if (e == hipSuccess) e = launch_swiglu_requant(sa, s);
@@ -355,8 +379,9 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   g2.splits = p.s2;
   g2.ks = p.ks2;
   g2.act_div = 1;
+  g2.tpw = p.tpw2;
   if (e == hipSuccess)
-    e = p.path == MOE_GEMM_MFMA ? launch_gemm_mfma(g2, p.grid2, s) : launch_gemm_valu(g2, p.grid2, s);
+    e = p.path == MOE_GEMM_MFMA ? launch_gemm_mfma(g2, 2, p.grid2, s) : launch_gemm_valu(g2, 2, p.grid2, s);
   if (e == hipSuccess) e = mark(3);
 
   if (e == hipSuccess) e = launch_combine(ca, s);

@@ -7,13 +7,15 @@
 // over one 128-K block is multiplied by (weight scale x activation scale) of
 // that block before it joins the running FP32 sum.
 //
-// Work unit = (distinct expert, 64 weight rows, one K split). Each of the four
-// waves of a workgroup owns 16 rows. A touched expert's weights are read once
-// for all of its routes (up to 8 or 16 per pass); untouched experts are never
-// read. The grid is sized for the largest possible number of distinct
-// experts; workgroups past the actual count exit at once, so no host
-// synchronisation is needed. The first weight blocks are requested before
-// the activations are staged, so the weight stream starts at once.
+// Work unit = (distinct expert, group of `tpw` 64-row tiles, one K split).
+// Each of the four waves of a workgroup owns 16 rows of a tile. A touched
+// expert's weights are read once for all of its routes (up to 8 or 16 per
+// pass); untouched experts are never read. The unit's activations are staged
+// once and its tiles are streamed back to back as one sequence of 128-K
+// blocks, so staging is paid once per `tpw` tiles. The grid is sized for the
+// largest possible number of distinct experts; workgroups past the actual
+// count exit at once, so no host synchronisation is needed. The first weight
+// blocks are requested before the activations are staged.
 #include "kernels.h"
 #include "device_common.h"
 
@@ -25,18 +27,20 @@ constexpr int kPrefetch = 4;  // 128-K blocks of weights in flight per wave
 constexpr int kStageBatch = 4;
 
 struct Unit {
-  int ui, e, cnt, off, tile, split, kb0, nb;
+  int ui, e, cnt, off, tile0, split, kb0, nb;
 };
 
 __device__ __forceinline__ bool decode_unit(const GemmArgs& a, Unit& u) {
   const int U = a.b.ctrl[1];
-  const int per_expert = a.tiles * a.splits;
+  const int groups = a.tiles / a.tpw;
+  const int per_expert = groups * a.splits;
   const int unit = blockIdx.x;
   if (unit >= U * per_expert) return false;
   u.ui = unit / per_expert;
   const int rem = unit - u.ui * per_expert;
-  u.tile = rem / a.splits;
-  u.split = rem - u.tile * a.splits;
+  const int group = rem / a.splits;
+  u.tile0 = group * a.tpw;
+  u.split = rem - group * a.splits;
   u.e = a.b.uexp[u.ui];
   u.cnt = a.b.ucnt[u.ui];
   u.off = a.b.uoff[u.ui];
@@ -45,36 +49,31 @@ __device__ __forceinline__ bool decode_unit(const GemmArgs& a, Unit& u) {
   return true;
 }
 
-// Activations of routes rts[0..nr) for the unit's K range, widened exactly to
-// F16 into dst (route r at dst + r * stride halves). Loads of up to
-// kStageBatch chunks per thread are issued before any is converted.
-__device__ __forceinline__ void stage_f16(const GemmArgs& a, const Unit& u, const int* rts, int nr,
-                                          _Float16* dst, int stride) {
-  const int per_route = u.nb * 16;  // 8-byte chunks
-  const int chunks = nr * per_route;
-  for (int base = 0; base < chunks; base += kStageBatch * kThreads) {
-    uint2 v[kStageBatch];
-#pragma unroll
-    for (int q = 0; q < kStageBatch; ++q) {
-      const int i = base + q * kThreads + threadIdx.x;
-      if (i < chunks) {
-        const int r = i / per_route, rem = i - r * per_route;
-        const size_t row = (size_t)(rts[r] / a.act_div);
-        v[q] = *reinterpret_cast<const uint2*>(a.aq + row * a.K + (size_t)u.kb0 * kTile + rem * 8);
-      }
+// Position of one 128-K block in the unit's stream (tile j, block b).
+struct Cursor {
+  int j, b;
+  __device__ __forceinline__ void next(int nb) {
+    if (++b == nb) {
+      b = 0;
+      ++j;
     }
-#pragma unroll
-    for (int q = 0; q < kStageBatch; ++q) {
-      const int i = base + q * kThreads + threadIdx.x;
-      if (i < chunks) {
-        const int r = i / per_route, rem = i - r * per_route;
-        half2_t* d = reinterpret_cast<half2_t*>(dst + r * stride + rem * 8);
-        d[0] = e4m3x2_to_f16x2<false>(v[q].x);
-        d[1] = e4m3x2_to_f16x2<true>(v[q].x);
-        d[2] = e4m3x2_to_f16x2<false>(v[q].y);
-        d[3] = e4m3x2_to_f16x2<true>(v[q].y);
-      }
-    }
+  }
+};
+
+// Weight scales of the unit's tiles (wsl[j * kMaxKs + b]) and activation
+// scales of the pass's routes (xsl[r * kMaxKs + b]); the block scale of
+// (tile j, route r, block b) is their product.
+__device__ __forceinline__ void stage_scales(const GemmArgs& a, const Unit& u, const int* rts, int nr,
+                                             float* wsl, float* xsl) {
+  const float* ws = a.ws + (size_t)u.e * (a.N / kTile) * a.nkb + u.kb0;
+  for (int i = threadIdx.x; i < a.tpw * u.nb; i += kThreads) {
+    const int j = i / u.nb, b = i - j * u.nb;
+    wsl[j * kMaxKs + b] = ws[(size_t)(((u.tile0 + j) * kRowsPerWg) / kTile) * a.nkb + b];
+  }
+  for (int i = threadIdx.x; i < nr * u.nb; i += kThreads) {
+    const int r = i / u.nb, b = i - r * u.nb;
+    const size_t row = (size_t)(rts[r] / a.act_div);
+    xsl[r * kMaxKs + b] = a.as[row * a.nkb + u.kb0 + b];
   }
 }
 
@@ -83,30 +82,40 @@ __device__ __forceinline__ void stage_f16(const GemmArgs& a, const Unit& u, cons
 // block of two rows; e4m3 pairs widen exactly to F16 pairs and v_dot2 adds
 // two exact products into FP32.
 // ---------------------------------------------------------------------------
+
+// kRole only names the instantiation (1: W13 / GEMM1, 2: W2 / GEMM2), so that
+// profiles report the two GEMMs apart.
+template <int kRole>
 __global__ __launch_bounds__(kThreads) void gemm_valu_kernel(GemmArgs a) {
   __shared__ __align__(16) _Float16 xh[kValuRoutes * kMaxKs * kTile];
-  __shared__ float sc[kValuRoutes * kMaxKs];
+  __shared__ float xsl[kValuRoutes * kMaxKs];
+  __shared__ float wsl[kMaxTpw * kMaxKs];
   __shared__ int rts[kValuRoutes];
 
   Unit u;
   if (!decode_unit(a, u)) return;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int rg = lane >> 3, ch = lane & 7;
-  const int row_a = u.tile * kRowsPerWg + wave * 16 + rg;
-  const uint8_t* pa = a.w + ((size_t)u.e * a.N + row_a) * a.K + (size_t)u.kb0 * kTile + ch * 16;
-  const uint8_t* pb = pa + (size_t)8 * a.K;
-  const float* wsr =
-      a.ws + ((size_t)u.e * (a.N / kTile) + (u.tile * kRowsPerWg) / kTile) * a.nkb + u.kb0;
+  const int rows_in_tile = wave * 16 + rg;  // and + 8
+  const uint8_t* p0 = a.w + ((size_t)u.e * a.N + u.tile0 * kRowsPerWg + rows_in_tile) * a.K +
+                      (size_t)u.kb0 * kTile + ch * 16;
+  const size_t tile_step = (size_t)kRowsPerWg * a.K;
+  const size_t half_step = (size_t)8 * a.K;
+  const int nsteps = a.tpw * u.nb;
 
   u32x4_t na[kPrefetch], nb_[kPrefetch];
+  Cursor ld{0, 0};
+  auto load_next = [&](int q) {
+    const uint8_t* p = p0 + ld.j * tile_step + (size_t)ld.b * kTile;
+    na[q] = load_stream16(p);
+    nb_[q] = load_stream16(p + half_step);
+    ld.next(u.nb);
+  };
   auto prefetch = [&]() {
+    ld = Cursor{0, 0};
 #pragma unroll
-    for (int q = 0; q < kPrefetch; ++q) {
-      if (q < u.nb) {
-        na[q] = load_stream16(pa + q * kTile);
-        nb_[q] = load_stream16(pb + q * kTile);
-      }
-    }
+    for (int q = 0; q < kPrefetch; ++q)
+      if (q < nsteps) load_next(q);
   };
   prefetch();
 
@@ -115,47 +124,59 @@ __global__ __launch_bounds__(kThreads) void gemm_valu_kernel(GemmArgs a) {
     if (c0) __syncthreads();
     if (tid < nr) rts[tid] = a.b.routes[u.off + c0 + tid];
     __syncthreads();
-    // the routes' activations for this split as exact F16, and the per-block
-    // products of the two scales
-    stage_f16(a, u, rts, nr, xh, kMaxKs * kTile);
-    for (int i = tid; i < nr * u.nb; i += kThreads) {
-      const int r = i / u.nb, b = i - r * u.nb;
-      const size_t row = (size_t)(rts[r] / a.act_div);
-      sc[r * kMaxKs + b] = wsr[b] * a.as[row * a.nkb + u.kb0 + b];
+    // the routes' activations for this split as exact F16, and the scales
+    {
+      const int per_route = u.nb * 16;  // 8-byte chunks
+      const int chunks = nr * per_route;
+      for (int base = 0; base < chunks; base += kStageBatch * kThreads) {
+        uint2 v[kStageBatch];
+#pragma unroll
+        for (int q = 0; q < kStageBatch; ++q) {
+          const int i = base + q * kThreads + tid;
+          if (i < chunks) {
+            const int r = i / per_route, rem = i - r * per_route;
+            const size_t row = (size_t)(rts[r] / a.act_div);
+            v[q] = *reinterpret_cast<const uint2*>(a.aq + row * a.K + (size_t)u.kb0 * kTile + rem * 8);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < kStageBatch; ++q) {
+          const int i = base + q * kThreads + tid;
+          if (i < chunks) {
+            const int r = i / per_route, rem = i - r * per_route;
+            half2_t* d = reinterpret_cast<half2_t*>(&xh[r * kMaxKs * kTile + rem * 8]);
+            d[0] = e4m3x2_to_f16x2<false>(v[q].x);
+            d[1] = e4m3x2_to_f16x2<true>(v[q].x);
+            d[2] = e4m3x2_to_f16x2<false>(v[q].y);
+            d[3] = e4m3x2_to_f16x2<true>(v[q].y);
+          }
+        }
+      }
     }
+    stage_scales(a, u, rts, nr, wsl, xsl);
     __syncthreads();
 
     float acc_a[kValuRoutes], acc_b[kValuRoutes];
 #pragma unroll
     for (int i = 0; i < kValuRoutes; ++i) acc_a[i] = acc_b[i] = 0.f;
-
-    for (int b0 = 0; b0 < u.nb; b0 += kPrefetch) {
-      u32x4_t ca[kPrefetch], cb[kPrefetch];
+    Cursor at{0, 0};
+    // Rotating prefetch: the registers of step st are refilled with step
+    // st + kPrefetch as soon as they are consumed.
+    for (int st0 = 0; st0 < nsteps; st0 += kPrefetch) {
 #pragma unroll
       for (int q = 0; q < kPrefetch; ++q) {
-        ca[q] = na[q];
-        cb[q] = nb_[q];
-      }
-#pragma unroll
-      for (int q = 0; q < kPrefetch; ++q) {
-        const int b = b0 + kPrefetch + q;
-        if (b < u.nb) {
-          na[q] = load_stream16(pa + (size_t)b * kTile);
-          nb_[q] = load_stream16(pb + (size_t)b * kTile);
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < kPrefetch; ++q) {
-        const int b = b0 + q;
-        if (b < u.nb) {
+        if (st0 + q < nsteps) {
           half2_t wa[8], wb[8];
 #pragma unroll
           for (int d = 0; d < 4; ++d) {
-            wa[2 * d] = e4m3x2_to_f16x2<false>(ca[q][d]);
-            wa[2 * d + 1] = e4m3x2_to_f16x2<true>(ca[q][d]);
-            wb[2 * d] = e4m3x2_to_f16x2<false>(cb[q][d]);
-            wb[2 * d + 1] = e4m3x2_to_f16x2<true>(cb[q][d]);
+            wa[2 * d] = e4m3x2_to_f16x2<false>(na[q][d]);
+            wa[2 * d + 1] = e4m3x2_to_f16x2<true>(na[q][d]);
+            wb[2 * d] = e4m3x2_to_f16x2<false>(nb_[q][d]);
+            wb[2 * d + 1] = e4m3x2_to_f16x2<true>(nb_[q][d]);
           }
+          if (st0 + q + kPrefetch < nsteps) load_next(q);
+          const int b = at.b;
+          const float ws = wsl[at.j * kMaxKs + b];
 #pragma unroll
           for (int i = 0; i < kValuRoutes; ++i) {
             if (i < nr) {
@@ -168,23 +189,28 @@ __global__ __launch_bounds__(kThreads) void gemm_valu_kernel(GemmArgs a) {
                 da = __builtin_amdgcn_fdot2(wa[p], xv, da, false);
                 db = __builtin_amdgcn_fdot2(wb[p], xv, db, false);
               }
-              const float s = sc[i * kMaxKs + b];
+              const float s = ws * xsl[i * kMaxKs + b];
               acc_a[i] = fmaf(da, s, acc_a[i]);
               acc_b[i] = fmaf(db, s, acc_b[i]);
             }
           }
-        }
-      }
-    }
+          if (b == u.nb - 1) {  // tile at.j complete: reduce over the 8 lanes of a row, store
+            const int row = (u.tile0 + at.j) * kRowsPerWg + rows_in_tile;
 #pragma unroll
-    for (int i = 0; i < kValuRoutes; ++i) {
-      if (i < nr) {
-        const float sa = group_sum<8>(acc_a[i]);
-        const float sb = group_sum<8>(acc_b[i]);
-        if (ch == 0) {
-          float* dst = a.part + ((size_t)u.split * a.R + rts[i]) * a.N;
-          dst[row_a] = sa;
-          dst[row_a + 8] = sb;
+            for (int i = 0; i < kValuRoutes; ++i) {
+              if (i < nr) {
+                const float sa = group_sum<8>(acc_a[i]);
+                const float sb = group_sum<8>(acc_b[i]);
+                if (ch == 0) {
+                  float* dst = a.part + ((size_t)u.split * a.R + rts[i]) * a.N;
+                  dst[row] = sa;
+                  dst[row + 8] = sb;
+                }
+              }
+              acc_a[i] = acc_b[i] = 0.f;
+            }
+          }
+          at.next(u.nb);
         }
       }
     }
@@ -200,44 +226,69 @@ __global__ __launch_bounds__(kThreads) void gemm_valu_kernel(GemmArgs a) {
 // the bytes directly, but its internal 128-term sum truncates: measured on
 // MI355X up to ~1e-4 of sum |terms|, enough to move FP8 hidden codes; the F16
 // instruction's sum is as accurate as FP32 accumulation.)
-// Lane l feeds row l % 16 (weights) and route l % 16 (activations) with 32
-// values of the block: bytes 16g..16g+15 and 64+16g..64+16g+15, g = l / 16.
-// A and B use the same value-to-slot map, so each block's 128 products are
-// summed exactly once, and every weight load instruction reads 64 contiguous
-// bytes of 16 rows.
+//
+// Weights are loaded exactly as in the VALU kernel -- eight lanes read a
+// row's full 128-byte block, 16 B each -- because reading half-lines of
+// twice as many rows per instruction measured ~20% slower on MI355X. Each
+// wave then passes its 16 x 128-byte block through a private LDS tile (row
+// stride 144 B, so the reads below hit every bank once) into the MFMA
+// layout: lane l feeds row l % 16 with bytes 16g..16g+15 and 64+16g..64+16g+15
+// of the block, g = l / 16, and the activations of route l % 16 with the same
+// bytes, so each block's 128 products are summed exactly once.
 // ---------------------------------------------------------------------------
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ half8_t cat4(half2_t a, half2_t b, half2_t c, half2_t d) {
+constexpr int kTileStride = kTile + 16;       // bytes per row of a wave's weight tile
+constexpr int kTileBytes = 16 * kTileStride;  // one wave's 16 rows
+
+__device__ __forceinline__ half8_t widen8(uint32_t w0, uint32_t w1) {
+  const half2_t a = e4m3x2_to_f16x2<false>(w0), b = e4m3x2_to_f16x2<true>(w0);
+  const half2_t c = e4m3x2_to_f16x2<false>(w1), d = e4m3x2_to_f16x2<true>(w1);
   return half8_t{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
+// Orders this wave's LDS accesses around the tile exchange (a wave's LDS
+// operations complete in order; this keeps the compiler from moving them).
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
+template <int kRole>
 __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int nrp = a.pass_routes;                    // routes per pass, <= 16
-  const int stride = a.ks * kTile + 8;             // halves per route row: +16 B against bank conflicts
-  _Float16* xh = reinterpret_cast<_Float16*>(smem);
-  float* sc = reinterpret_cast<float*>(smem + (size_t)nrp * stride * 2);  // [ks][16]
-  int* rts = reinterpret_cast<int*>(sc + a.ks * kMfmaRoutes);
+  const int nrp = a.pass_routes;         // routes per pass, <= 16
+  const int stride = a.ks * kTile + 16;  // bytes per staged route row: +16 B against bank conflicts
+  uint8_t* tiles = smem;                                           // [4 waves][kTileBytes]
+  uint8_t* xb = smem + 4 * kTileBytes;                             // [nrp][stride] e4m3
+  float* xsl = reinterpret_cast<float*>(xb + (size_t)nrp * stride);  // [16][kMaxKs]
+  float* wsl = xsl + kMfmaRoutes * kMaxKs;                         // [kMaxTpw][kMaxKs]
+  int* rts = reinterpret_cast<int*>(wsl + kMaxTpw * kMaxKs);
 
   Unit u;
   if (!decode_unit(a, u)) return;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int col = lane & 15, g = lane >> 4;
-  const int row0 = u.tile * kRowsPerWg + wave * 16;
-  const uint8_t* pw = a.w + ((size_t)u.e * a.N + row0 + col) * a.K + (size_t)u.kb0 * kTile + g * 16;
-  const float* wsr =
-      a.ws + ((size_t)u.e * (a.N / kTile) + (u.tile * kRowsPerWg) / kTile) * a.nkb + u.kb0;
+  const int rg = lane >> 3, ch = lane & 7;   // load layout
+  const int col = lane & 15, g = lane >> 4;  // MFMA layout
+  const uint8_t* p0 = a.w + ((size_t)u.e * a.N + u.tile0 * kRowsPerWg + wave * 16 + rg) * a.K +
+                      (size_t)u.kb0 * kTile + ch * 16;
+  const size_t tile_step = (size_t)kRowsPerWg * a.K;
+  const size_t half_step = (size_t)8 * a.K;
+  const int nsteps = a.tpw * u.nb;
+  uint8_t* tile = tiles + wave * kTileBytes;
 
-  u32x4_t nlo[kPrefetch], nhi[kPrefetch];
+  u32x4_t na[kPrefetch], nb_[kPrefetch];
+  Cursor ld{0, 0};
+  auto load_next = [&](int q) {
+    const uint8_t* p = p0 + ld.j * tile_step + (size_t)ld.b * kTile;
+    na[q] = load_stream16(p);
+    nb_[q] = load_stream16(p + half_step);
+    ld.next(u.nb);
+  };
   auto prefetch = [&]() {
+    ld = Cursor{0, 0};
 #pragma unroll
-    for (int q = 0; q < kPrefetch; ++q) {
-      if (q < u.nb) {
-        nlo[q] = load_stream16(pw + q * kTile);
-        nhi[q] = load_stream16(pw + q * kTile + 64);
-      }
-    }
+    for (int q = 0; q < kPrefetch; ++q)
+      if (q < nsteps) load_next(q);
   };
   prefetch();
 
@@ -246,67 +297,80 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmArgs a) {
     if (c0) __syncthreads();
     if (tid < nr) rts[tid] = a.b.routes[u.off + c0 + tid];
     __syncthreads();
-    stage_f16(a, u, rts, nr, xh, stride);
-    for (int i = tid; i < kMfmaRoutes * u.nb; i += kThreads) {
-      const int r = i % kMfmaRoutes, b = i / kMfmaRoutes;
-      float v = 0.f;
-      if (r < nr) {
-        const size_t row = (size_t)(rts[r] / a.act_div);
-        v = wsr[b] * a.as[row * a.nkb + u.kb0 + b];
+    {  // the routes' activations for this split, e4m3 as stored
+      const int per_route = u.nb * 8;  // 16-byte chunks
+      const int chunks = nr * per_route;
+      for (int base = 0; base < chunks; base += kStageBatch * kThreads) {
+        u32x4_t v[kStageBatch];
+#pragma unroll
+        for (int q = 0; q < kStageBatch; ++q) {
+          const int i = base + q * kThreads + tid;
+          if (i < chunks) {
+            const int r = i / per_route, rem = i - r * per_route;
+            const size_t row = (size_t)(rts[r] / a.act_div);
+            v[q] = *reinterpret_cast<const u32x4_t*>(a.aq + row * a.K + (size_t)u.kb0 * kTile + rem * 16);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < kStageBatch; ++q) {
+          const int i = base + q * kThreads + tid;
+          if (i < chunks) {
+            const int r = i / per_route, rem = i - r * per_route;
+            *reinterpret_cast<u32x4_t*>(xb + r * stride + rem * 16) = v[q];
+          }
+        }
       }
-      sc[b * kMfmaRoutes + r] = v;
     }
+    stage_scales(a, u, rts, nr, wsl, xsl);
     __syncthreads();
 
     const bool live = col < nr;
     // lanes past the pass's routes read route 0's row; their columns are dropped
-    const _Float16* xr = xh + (live ? col : 0) * stride + g * 16;
+    const uint8_t* xr = xb + (live ? col : 0) * stride + g * 16;
+    const float* xs_col = xsl + (live ? col : 0) * kMaxKs;
     float4_t acc = {0.f, 0.f, 0.f, 0.f};
     const float4_t zero = {0.f, 0.f, 0.f, 0.f};
-    for (int b0 = 0; b0 < u.nb; b0 += kPrefetch) {
-      u32x4_t clo[kPrefetch], chi[kPrefetch];
+    Cursor at{0, 0};
+    for (int st0 = 0; st0 < nsteps; st0 += kPrefetch) {
 #pragma unroll
       for (int q = 0; q < kPrefetch; ++q) {
-        clo[q] = nlo[q];
-        chi[q] = nhi[q];
-      }
-#pragma unroll
-      for (int q = 0; q < kPrefetch; ++q) {
-        const int b = b0 + kPrefetch + q;
-        if (b < u.nb) {
-          nlo[q] = load_stream16(pw + (size_t)b * kTile);
-          nhi[q] = load_stream16(pw + (size_t)b * kTile + 64);
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < kPrefetch; ++q) {
-        const int b = b0 + q;
-        if (b < u.nb) {
-          const half8_t* xb = reinterpret_cast<const half8_t*>(xr + b * kTile);
-          const half8_t x0 = xb[0], x1 = xb[1], x2 = xb[8], x3 = xb[9];  // +0, +8, +64, +72 halves
-          const half8_t w0 = cat4(e4m3x2_to_f16x2<false>(clo[q][0]), e4m3x2_to_f16x2<true>(clo[q][0]),
-                                  e4m3x2_to_f16x2<false>(clo[q][1]), e4m3x2_to_f16x2<true>(clo[q][1]));
-          const half8_t w1 = cat4(e4m3x2_to_f16x2<false>(clo[q][2]), e4m3x2_to_f16x2<true>(clo[q][2]),
-                                  e4m3x2_to_f16x2<false>(clo[q][3]), e4m3x2_to_f16x2<true>(clo[q][3]));
-          const half8_t w2 = cat4(e4m3x2_to_f16x2<false>(chi[q][0]), e4m3x2_to_f16x2<true>(chi[q][0]),
-                                  e4m3x2_to_f16x2<false>(chi[q][1]), e4m3x2_to_f16x2<true>(chi[q][1]));
-          const half8_t w3 = cat4(e4m3x2_to_f16x2<false>(chi[q][2]), e4m3x2_to_f16x2<true>(chi[q][2]),
-                                  e4m3x2_to_f16x2<false>(chi[q][3]), e4m3x2_to_f16x2<true>(chi[q][3]));
-          float4_t p = __builtin_amdgcn_mfma_f32_16x16x32_f16(w0, x0, zero, 0, 0, 0);
-          p = __builtin_amdgcn_mfma_f32_16x16x32_f16(w1, x1, p, 0, 0, 0);
-          p = __builtin_amdgcn_mfma_f32_16x16x32_f16(w2, x2, p, 0, 0, 0);
-          p = __builtin_amdgcn_mfma_f32_16x16x32_f16(w3, x3, p, 0, 0, 0);
-          const float s = sc[b * kMfmaRoutes + col];
+        if (st0 + q < nsteps) {
+          // weights: load layout -> tile -> MFMA layout; the registers of
+          // step st are refilled with step st + kPrefetch right away
+          *reinterpret_cast<u32x4_t*>(tile + rg * kTileStride + ch * 16) = na[q];
+          *reinterpret_cast<u32x4_t*>(tile + (rg + 8) * kTileStride + ch * 16) = nb_[q];
+          if (st0 + q + kPrefetch < nsteps) load_next(q);
+          const int b = at.b;
+          wave_lds_fence();
+          const u32x4_t wlo = *reinterpret_cast<const u32x4_t*>(tile + col * kTileStride + g * 16);
+          const u32x4_t whi = *reinterpret_cast<const u32x4_t*>(tile + col * kTileStride + 64 + g * 16);
+          const u32x4_t xlo = *reinterpret_cast<const u32x4_t*>(xr + b * kTile);
+          const u32x4_t xhi = *reinterpret_cast<const u32x4_t*>(xr + b * kTile + 64);
+          wave_lds_fence();
+          float4_t p = __builtin_amdgcn_mfma_f32_16x16x32_f16(widen8(wlo[0], wlo[1]),
+                                                              widen8(xlo[0], xlo[1]), zero, 0, 0, 0);
+          p = __builtin_amdgcn_mfma_f32_16x16x32_f16(widen8(wlo[2], wlo[3]), widen8(xlo[2], xlo[3]), p,
+                                                     0, 0, 0);
+          p = __builtin_amdgcn_mfma_f32_16x16x32_f16(widen8(whi[0], whi[1]), widen8(xhi[0], xhi[1]), p,
+                                                     0, 0, 0);
+          p = __builtin_amdgcn_mfma_f32_16x16x32_f16(widen8(whi[2], whi[3]), widen8(xhi[2], xhi[3]), p,
+                                                     0, 0, 0);
+          const float s = wsl[at.j * kMaxKs + b] * xs_col[b];
           acc[0] = fmaf(p[0], s, acc[0]);
           acc[1] = fmaf(p[1], s, acc[1]);
           acc[2] = fmaf(p[2], s, acc[2]);
           acc[3] = fmaf(p[3], s, acc[3]);
+          if (b == u.nb - 1) {  // tile at.j complete
+            if (live) {
+              const int row = (u.tile0 + at.j) * kRowsPerWg + wave * 16 + 4 * g;
+              float* dst = a.part + ((size_t)u.split * a.R + rts[col]) * a.N + row;
+              *reinterpret_cast<float4_t*>(dst) = acc;
+            }
+            acc = zero;
+          }
+          at.next(u.nb);
         }
       }
-    }
-    if (live) {
-      float* dst = a.part + ((size_t)u.split * a.R + rts[col]) * a.N + row0 + 4 * g;
-      *reinterpret_cast<float4_t*>(dst) = acc;
     }
     if (c0 + nrp < u.cnt) prefetch();
   }
@@ -315,17 +379,24 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmArgs a) {
 }  // namespace
 
 size_t gemm_mfma_lds_bytes(int pass_routes, int ks) {
-  return (size_t)pass_routes * (ks * kTile + 8) * 2 + (size_t)ks * kMfmaRoutes * 4 + kMfmaRoutes * 4;
+  return 4 * (size_t)kTileBytes + (size_t)pass_routes * (ks * kTile + 16) +
+         (size_t)(kMfmaRoutes + kMaxTpw) * kMaxKs * 4 + kMfmaRoutes * 4;
 }
 
-hipError_t launch_gemm_valu(const GemmArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(gemm_valu_kernel, dim3(grid), dim3(kThreads), 0, s, a);
+hipError_t launch_gemm_valu(const GemmArgs& a, int role, int grid, hipStream_t s) {
+  if (role == 1)
+    hipLaunchKernelGGL(gemm_valu_kernel<1>, dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(gemm_valu_kernel<2>, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_mfma(const GemmArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(gemm_mfma_kernel, dim3(grid), dim3(kThreads),
-                     gemm_mfma_lds_bytes(a.pass_routes, a.ks), s, a);
+hipError_t launch_gemm_mfma(const GemmArgs& a, int role, int grid, hipStream_t s) {
+  const size_t lds = gemm_mfma_lds_bytes(a.pass_routes, a.ks);
+  if (role == 1)
+    hipLaunchKernelGGL(gemm_mfma_kernel<1>, dim3(grid), dim3(kThreads), lds, s, a);
+  else
+    hipLaunchKernelGGL(gemm_mfma_kernel<2>, dim3(grid), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 

@@ -69,6 +69,7 @@ struct GemmArgs {
   int R;                // routes (row stride of part)
   int act_div;
   int pass_routes;      // MFMA path: routes staged per pass (<= 16)
+  int tpw;              // 64-row tiles streamed per workgroup (divides tiles, <= kMaxTpw)
 };
 
 // Maximum 128-blocks of K per split (bounds the LDS staging of activations).
@@ -76,13 +77,15 @@ constexpr int kMaxKs = 16;
 constexpr int kRowsPerWg = 64;
 constexpr int kValuRoutes = 8;   // routes per pass of the VALU inner product
 constexpr int kMfmaRoutes = 16;  // routes per pass of the MFMA inner product
+constexpr int kMaxTpw = 4;
 constexpr size_t kMfmaLdsBudget = 40 * 1024;  // keeps three workgroups per CU
 constexpr size_t kMaxRouteLds = 64 * 1024;
 
 size_t route_quant_lds_bytes(int E, int words, int routes);
 hipError_t launch_route_quant(const RouteQuantArgs& a, hipStream_t s);
-hipError_t launch_gemm_valu(const GemmArgs& a, int grid, hipStream_t s);
-hipError_t launch_gemm_mfma(const GemmArgs& a, int grid, hipStream_t s);
+// role: 1 = GEMM1 (W13), 2 = GEMM2 (W2); it only selects the kernel symbol.
+hipError_t launch_gemm_valu(const GemmArgs& a, int role, int grid, hipStream_t s);
+hipError_t launch_gemm_mfma(const GemmArgs& a, int role, int grid, hipStream_t s);
 size_t gemm_mfma_lds_bytes(int pass_routes, int ks);
 hipError_t launch_swiglu_requant(const SwigluArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);

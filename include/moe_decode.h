@@ -65,8 +65,8 @@ extern "C" {
 #define MOE_SCALES_UE8M0_PACKED 1 /* int32 [n, ceil(k/512)]: byte g%4 of word g/4 = biased exponent of K group g */
 
 #define MOE_GEMM_AUTO 0  /* choose the inner product per call */
-#define MOE_GEMM_VALU 1  /* packed FP8->F16 conversion + F16 dot2 into FP32 */
-#define MOE_GEMM_MFMA 2  /* v_mfma_f32_16x16x128_f8f6f4, one 128-K block per instruction */
+#define MOE_GEMM_VALU 1  /* exact FP8->F16 widening + F16 dot2 into FP32 */
+#define MOE_GEMM_MFMA 2  /* exact FP8->F16 widening + v_mfma_f32_16x16x32_f16 (16 routes at once) */
 
 /* Limits of this implementation. */
 #define MOE_DECODE_MAX_EXPERTS 1024
@@ -159,7 +159,8 @@ const char* moe_decode_error_string(int code);
 /* The launch plan run() uses for M tokens: out[0] = GEMM path used
  * (MOE_GEMM_VALU or MOE_GEMM_MFMA), out[1] = splits1, out[2] = splits2,
  * out[3] = blocks per split in GEMM1, out[4] = in GEMM2, out[5] = grid of
- * GEMM1, out[6] = grid of GEMM2. n is the capacity of out (>= 7). */
+ * GEMM1, out[6] = grid of GEMM2, out[7] / out[8] = 64-row tiles streamed per
+ * workgroup in GEMM1 / GEMM2. n is the capacity of out (>= 9). */
 int moe_decode_plan(moe_decode_t h, int32_t M, int32_t* out, int32_t n);
 
 /* Stage read-back: copies workspace region `stage` of the last run into the

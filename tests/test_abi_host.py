@@ -86,7 +86,7 @@ def test_null_arguments(L):
     assert L.moe_decode_create(ctypes.byref(_cfg()), None) == _capi.ERR_INVALID_ARG
     assert L.moe_decode_run(None, 1, *([None] * 9)) == _capi.ERR_INVALID_ARG
     L.moe_decode_destroy(None)
-    assert L.moe_decode_plan(None, 1, None, 7) == _capi.ERR_INVALID_ARG
+    assert L.moe_decode_plan(None, 1, None, 9) == _capi.ERR_INVALID_ARG
     assert L.moe_decode_debug_stage(None, 0, None, 0, None) == _capi.ERR_INVALID_ARG
     assert L.moe_decode_set_timing(None, 1) == _capi.ERR_INVALID_ARG
     assert L.moe_decode_debug_codec(None, None, None, 4, None) == _capi.ERR_INVALID_ARG
