@@ -1,6 +1,5 @@
-// Device bodies of the two small steps around the GEMMs. Both the separate
-// kernels (epilogues.hip) and the GEMM kernels' last-arriver epilogues
-// (expert_gemm.hip) call these, so the arithmetic is one and the same.
+// Device bodies of the two small steps around the GEMMs, launched by the
+// kernels of epilogues.hip.
 #pragma once
 
 #include "kernels.h"

@@ -35,8 +35,9 @@ def sigmoid_f32(z: np.ndarray) -> np.ndarray:
     """binary32 rounding of 1 / (1 + exp(-z)) evaluated in float64.
 
     The "mega_moe" page (top_k_pick docstring) computes the sigmoid with an
-    approximate exp and divide "a few ulp" off; the reading taken here is the
-    correctly rounded FP32 sigmoid, which the GPU side also computes."""
+    approximate exp and divide, a few units in the last place off; the reading
+    taken here is the correctly rounded FP32 sigmoid, which the GPU side also
+    computes."""
     with np.errstate(over="ignore"):
         return f32(1.0 / (1.0 + np.exp(-np.asarray(z, dtype=np.float64))))
 
