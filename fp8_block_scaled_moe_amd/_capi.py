@@ -33,7 +33,10 @@ GEMM_PATHS = {"auto": 0, "valu": 1, "mfma": 2}
 STAGES = {
     "ctrl": 0, "uexp": 1, "uoff": 2, "ucnt": 3, "routes": 4, "x_q": 5, "x_s": 6,
     "part1": 7, "h_q": 8, "h_s": 9, "part2": 10,
+    "shared_x_q": 11, "shared_x_s": 12, "shared_part1": 13, "shared_h_q": 14,
+    "shared_h_s": 15, "shared_part2": 16,
 }
+TIMING_SLOTS = ("route_quant", "gemm1", "swiglu_requant", "gemm2", "combine")
 
 
 class MoeDecodeConfig(ctypes.Structure):
@@ -146,12 +149,17 @@ class MoeDecode:
     Weight tensors are borrowed: the handle keeps references so they outlive
     it. w13 [E, 2I, H] (up rows, then gate rows) and w2 [E, H, I] are e4m3
     bytes (uint8 or float8_e4m3fn); scales are FP32 [E, N/128, K/128].
+
+    Optional shared expert: sw13 [2Is, H] (gate rows, then up rows) and
+    sw2 [H, Is] e4m3, with FP32 block scales [2Is/128, H/128] / [H/128, Is/128]
+    or packed UE8M0 int32 scales [2Is, ceil(H/512)] / [H, ceil(Is/512)].
     """
 
     def __init__(self, w13, w13_scale, w2, w2_scale, *, top_k: int, limit: float,
                  routed_scale: float, max_tokens: int, logits_dtype=torch.float32,
                  ue8m0_act: bool = False, gemm_path: str = "auto", splits1: int = 0,
-                 splits2: int = 0):
+                 splits2: int = 0, sw13=None, sw13_scale=None, sw2=None, sw2_scale=None,
+                 shared_limit: Optional[float] = None, shared_ue8m0_act: bool = True):
         self.device = w13.device
         for t, n, d in ((w13, "w13", _FP8), (w2, "w2", _FP8), (w13_scale, "w13_scale", (torch.float32,)),
                         (w2_scale, "w2_scale", (torch.float32,))):
@@ -170,6 +178,33 @@ class MoeDecode:
         cfg.w13, cfg.w13_scale, cfg.w2, cfg.w2_scale = (t.data_ptr() for t in self._keep)
         cfg.gemm_path = GEMM_PATHS[gemm_path]
         cfg.splits1, cfg.splits2 = splits1, splits2
+        self.shared_inter = 0
+        if sw13 is not None:
+            _need(sw13, "sw13", _FP8, self.device)
+            _need(sw2, "sw2", _FP8, self.device)
+            sdt = (torch.float32, torch.int32)
+            _need(sw13_scale, "sw13_scale", sdt, self.device)
+            _need(sw2_scale, "sw2_scale", sdt, self.device)
+            if sw13_scale.dtype != sw2_scale.dtype:
+                raise ValueError("sw13_scale and sw2_scale must have the same format")
+            Is = sw13.shape[0] // 2
+            if tuple(sw13.shape) != (2 * Is, H) or tuple(sw2.shape) != (H, Is):
+                raise ValueError(f"shared weights must be [2Is, {H}] and [{H}, Is]")
+            if sw13_scale.dtype == torch.float32:
+                want13, want2 = (2 * Is // 128, H // 128), (H // 128, Is // 128)
+            else:
+                want13, want2 = (2 * Is, -(-H // 512)), (H, -(-Is // 512))
+            if tuple(sw13_scale.shape) != want13 or tuple(sw2_scale.shape) != want2:
+                raise ValueError(f"shared scales must be {want13} and {want2}")
+            self.shared_inter = Is
+            self._keep += (sw13, sw13_scale, sw2, sw2_scale)
+            cfg.shared_inter = self.shared_inter
+            cfg.shared_scale_format = (SCALES_F32 if sw13_scale.dtype == torch.float32
+                                       else SCALES_UE8M0_PACKED)
+            cfg.shared_ue8m0_act = int(bool(shared_ue8m0_act))
+            cfg.shared_limit = limit if shared_limit is None else shared_limit
+            cfg.sw13, cfg.sw13_scale, cfg.sw2, cfg.sw2_scale = (
+                t.data_ptr() for t in (sw13, sw13_scale, sw2, sw2_scale))
         self.cfg = cfg
         h = ctypes.c_void_p()
         with torch.cuda.device(self.device):
@@ -197,21 +232,27 @@ class MoeDecode:
 
     def __call__(self, x, logits, bias, stream=None):
         """(slots [M*k, H] bf16, ids [M, k] int32, weights [M, k] f32,
-        combined [M, H] bf16)."""
+        combined [M, H] bf16), plus shared_out [M, H] bf16 when the handle
+        has a shared expert."""
         _need(x, "x", (torch.bfloat16,), self.device)
         _need(logits, "logits", (self.logits_dtype,), self.device)
         _need(bias, "bias", (torch.float32,), self.device)
         out = self.outputs(x.shape[0])
-        self.run_into(x, logits, bias, *out, stream=stream)
-        return out
+        shared = None
+        if self.shared_inter:
+            shared = torch.empty((x.shape[0], self.hidden), dtype=torch.bfloat16, device=self.device)
+        self.run_into(x, logits, bias, *out, shared_out=shared, stream=stream)
+        return out + (shared,) if shared is not None else out
 
     # -- introspection ------------------------------------------------------
     def plan(self, M: int) -> dict:
-        buf = (ctypes.c_int32 * 9)()
-        rc = lib().moe_decode_plan(self._h, M, buf, 9)
+        buf = (ctypes.c_int32 * 15)()
+        rc = lib().moe_decode_plan(self._h, M, buf, 15)
         if rc != OK:
             raise MoeDecodeError(rc, "moe_decode_plan")
-        keys = ("path", "splits1", "splits2", "ks1", "ks2", "grid1", "grid2", "tpw1", "tpw2")
+        keys = ("path", "splits1", "splits2", "ks1", "ks2", "grid1", "grid2", "tpw1", "tpw2",
+                "shared_splits1", "shared_splits2", "shared_ks1", "shared_ks2",
+                "shared_units1", "shared_units2")
         return dict(zip(keys, list(buf)))
 
     def stage(self, name: str, dst: torch.Tensor, stream=None) -> torch.Tensor:
@@ -227,8 +268,11 @@ class MoeDecode:
             raise MoeDecodeError(rc, "moe_decode_set_timing")
 
     def last_timing(self):
-        ms = (ctypes.c_float * 7)()
-        rc = lib().moe_decode_last_timing(self._h, ms, 7)
+        """Milliseconds of each launch of the last timed run, in the order of
+        TIMING_SLOTS."""
+        n = len(TIMING_SLOTS)
+        ms = (ctypes.c_float * n)()
+        rc = lib().moe_decode_last_timing(self._h, ms, n)
         if rc != OK:
             raise MoeDecodeError(rc, "moe_decode_last_timing")
         return list(ms)

@@ -17,17 +17,27 @@ using namespace moe;
 namespace {
 
 constexpr int kEvents = 8;
-constexpr int kRegions = 11;
-constexpr int kStages = 7;  // timing slots: route, GEMM1, SwiGLU, GEMM2, combine, shared x2
+constexpr int kRegions = 17;
+constexpr int kStages = 5;  // timing slots: route, GEMM1, SwiGLU, GEMM2, combine
 constexpr int kTargetUnits = 4096;  // work units per GEMM launch to aim for (16 per CU)
+constexpr int kDenseTargetUnits = 256;  // units of the shared expert per GEMM launch
+constexpr int kBadFlagWord = 32;        // word of the control region used by create
+
+// Workspace regions (the debug stages use the same numbering).
+enum {
+  kCtrl, kUexp, kUoff, kUcnt, kRoutes, kXq, kXs, kP1, kHq, kHs, kP2,
+  kSXq, kSXs, kSP1, kSHq, kSHs, kSP2,
+};
 
 struct Plan {
   int path;
   int s1, ks1, s2, ks2;
-  int grid1, grid2;
+  int grid1, grid2;  // whole launches, shared units included
   int umax;
   int pass_routes;  // MFMA path: routes per pass
   int tpw1, tpw2;   // 64-row tiles per workgroup
+  // shared expert (all zero without one)
+  int ss1, sks1, ss2, sks2, stpw1, stpw2, sunits1, sunits2;
 };
 
 struct Region {
@@ -43,6 +53,7 @@ struct moe_decode_handle {
   size_t ws_bytes;
   Region reg[kRegions];
   int words;
+  bool shared_own_quant;  // the shared expert quantises x with its own scale rule
   // shared expert scales converted to FP32 (owned), or the caller's FP32 ones
   float* s13_owned;
   float* s2_owned;
@@ -72,6 +83,29 @@ void choose_split(int units_per_split, int nkb, int forced, int max_ks, int* spl
   *splits = ceil_div(nkb, k);
 }
 
+int tiles_per_wg(int tiles, int want) {
+  int t = want;
+  while (tiles % t) t /= 2;
+  return t;
+}
+
+// The dense problem (shared expert, M routes, N x K weights): about one unit
+// per CU, but split-K partials (splits * M * N * 4 bytes written and read)
+// kept within an eighth of the N * K weight bytes unless the LDS bound on
+// blocks per split needs more splits.
+void plan_dense(int M, int N, int K, int max_ks, int want_tpw, int* splits, int* ks, int* tpw,
+                int* units) {
+  const int tiles = N / kRowsPerWg, nkb = K / kTile;
+  *tpw = tiles_per_wg(tiles, want_tpw);
+  const int groups = tiles / *tpw;
+  const int cap = std::max(1, K / (32 * M));
+  int s = std::min(ceil_div(kDenseTargetUnits, groups), std::min(cap, nkb));
+  s = std::max(s, ceil_div(nkb, max_ks));
+  *ks = ceil_div(nkb, s);
+  *splits = ceil_div(nkb, *ks);
+  *units = groups * *splits;
+}
+
 Plan make_plan(const moe_decode_config& c, int M) {
   Plan p{};
   const int R = M * c.top_k;
@@ -96,17 +130,18 @@ Plan make_plan(const moe_decode_config& c, int M) {
   // blocks of weights per route; with many tokens (so many routes per
   // expert) a workgroup streams several tiles per staging.
   const int want = M <= 2 ? 1 : (M <= 8 ? 2 : kMaxTpw);
-  auto tiles_per_wg = [&](int tiles) {
-    int t = want;
-    while (tiles % t) t /= 2;
-    return t;
-  };
-  p.tpw1 = tiles_per_wg(tiles1);
-  p.tpw2 = tiles_per_wg(tiles2);
+  p.tpw1 = tiles_per_wg(tiles1, want);
+  p.tpw2 = tiles_per_wg(tiles2, want);
   choose_split(p.umax * (tiles1 / p.tpw1), c.hidden / kTile, c.splits1, max_ks, &p.s1, &p.ks1);
   choose_split(p.umax * (tiles2 / p.tpw2), c.inter / kTile, c.splits2, max_ks, &p.s2, &p.ks2);
   p.grid1 = p.umax * (tiles1 / p.tpw1) * p.s1;
   p.grid2 = p.umax * (tiles2 / p.tpw2) * p.s2;
+  if (c.shared_inter > 0) {
+    plan_dense(M, 2 * c.shared_inter, c.hidden, max_ks, want, &p.ss1, &p.sks1, &p.stpw1, &p.sunits1);
+    plan_dense(M, c.hidden, c.shared_inter, max_ks, want, &p.ss2, &p.sks2, &p.stpw2, &p.sunits2);
+    p.grid1 += p.sunits1;
+    p.grid2 += p.sunits2;
+  }
   return p;
 }
 
@@ -132,10 +167,48 @@ int validate_config(const moe_decode_config* c) {
     if (route_quant_lds_bytes(c->experts, words, c->max_tokens * c->top_k) > kMaxRouteLds)
       return MOE_DECODE_ERR_UNSUPPORTED;
   }
-  if (c->shared_inter != 0) {
-    // The shared expert is not built into this library yet.
-    return MOE_DECODE_ERR_UNSUPPORTED;
+  if (c->shared_inter < 0) return MOE_DECODE_ERR_INVALID_ARG;
+  if (c->shared_inter > 0) {
+    if (!c->sw13 || !c->sw13_scale || !c->sw2 || !c->sw2_scale) return MOE_DECODE_ERR_INVALID_ARG;
+    if (!aligned16(c->sw13) || !aligned16(c->sw2) || !aligned16(c->sw13_scale) ||
+        !aligned16(c->sw2_scale))
+      return MOE_DECODE_ERR_INVALID_ARG;
+    if (!(c->shared_limit > 0.f)) return MOE_DECODE_ERR_INVALID_ARG;
+    if (c->shared_inter % kTile) return MOE_DECODE_ERR_UNSUPPORTED;
+    if (c->shared_scale_format != MOE_SCALES_F32 && c->shared_scale_format != MOE_SCALES_UE8M0_PACKED)
+      return MOE_DECODE_ERR_UNSUPPORTED;
   }
+  return MOE_DECODE_OK;
+}
+
+// Shared-expert scales as FP32: the caller's own, or converted once from the
+// packed UE8M0 form into buffers the handle owns. Synchronises the device.
+int prepare_shared_scales(moe_decode_handle* h) {
+  const moe_decode_config& c = h->cfg;
+  if (c.shared_scale_format == MOE_SCALES_F32) {
+    h->s13 = static_cast<const float*>(c.sw13_scale);
+    h->s2 = static_cast<const float*>(c.sw2_scale);
+    return MOE_DECODE_OK;
+  }
+  const int H = c.hidden, Is = c.shared_inter;
+  const size_t n13 = (size_t)(2 * Is / kTile) * (H / kTile), n2 = (size_t)(H / kTile) * (Is / kTile);
+  if (hipMalloc(&h->s13_owned, n13 * sizeof(float)) != hipSuccess ||
+      hipMalloc(&h->s2_owned, n2 * sizeof(float)) != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_DECODE_ERR_OUT_OF_MEMORY;
+  }
+  int32_t* bad = reinterpret_cast<int32_t*>(h->ws + h->reg[kCtrl].off) + kBadFlagWord;
+  int32_t flag = 0;
+  if (launch_unpack_ue8m0(static_cast<const int32_t*>(c.sw13_scale), 2 * Is, H, h->s13_owned, bad, nullptr) !=
+          hipSuccess ||
+      launch_unpack_ue8m0(static_cast<const int32_t*>(c.sw2_scale), H, Is, h->s2_owned, bad, nullptr) !=
+          hipSuccess ||
+      hipMemcpy(&flag, bad, sizeof(flag), hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemset(bad, 0, sizeof(int32_t)) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+    return MOE_DECODE_ERR_HIP;
+  if (flag) return MOE_DECODE_ERR_INVALID_ARG;  // scales vary inside a 128-row block
+  h->s13 = h->s13_owned;
+  h->s2 = h->s2_owned;
   return MOE_DECODE_OK;
 }
 
@@ -165,25 +238,35 @@ int moe_decode_create(const moe_decode_config* cfg, moe_decode_t* out) {
   // Workspace sized for every M up to max_tokens.
   const size_t Rcap = (size_t)c.max_tokens * c.top_k;
   const size_t Ucap = std::min<size_t>(c.experts, Rcap);
-  size_t p1 = 0, p2 = 0;
+  size_t p1 = 0, p2 = 0, sp1 = 0, sp2 = 0;
   for (int M = 1; M <= c.max_tokens; ++M) {
     const Plan p = make_plan(c, M);
     p1 = std::max(p1, (size_t)p.s1 * M * c.top_k * 2 * c.inter);
     p2 = std::max(p2, (size_t)p.s2 * M * c.top_k * c.hidden);
+    sp1 = std::max(sp1, (size_t)p.ss1 * M * 2 * c.shared_inter);
+    sp2 = std::max(sp2, (size_t)p.ss2 * M * c.hidden);
   }
-  const size_t H = c.hidden, I = c.inter;
+  const size_t H = c.hidden, I = c.inter, Is = c.shared_inter, T = c.max_tokens;
+  // the shared expert reuses the routed x quantisation when the rules agree
+  const bool own_quant = Is > 0 && (c.shared_ue8m0_act != 0) != (c.ue8m0_act != 0);
   const size_t sizes[kRegions] = {
-      64 * sizeof(int32_t),           // 0 control
-      Ucap * sizeof(int32_t),         // 1 uexp
-      Ucap * sizeof(int32_t),         // 2 uoff
-      Ucap * sizeof(int32_t),         // 3 ucnt
-      Rcap * sizeof(int32_t),         // 4 routes
-      (size_t)c.max_tokens * H,       // 5 x_q
-      (size_t)c.max_tokens * (H / kTile) * sizeof(float),  // 6 x_s
-      p1 * sizeof(float),             // 7 GEMM1 partials
-      Rcap * I,                       // 8 h_q
-      Rcap * (I / kTile) * sizeof(float),  // 9 h_s
-      p2 * sizeof(float),             // 10 GEMM2 partials
+      64 * sizeof(int32_t),           // control
+      Ucap * sizeof(int32_t),         // uexp
+      Ucap * sizeof(int32_t),         // uoff
+      Ucap * sizeof(int32_t),         // ucnt
+      Rcap * sizeof(int32_t),         // routes
+      T * H,                          // x_q
+      T * (H / kTile) * sizeof(float),  // x_s
+      p1 * sizeof(float),             // GEMM1 partials
+      Rcap * I,                       // h_q
+      Rcap * (I / kTile) * sizeof(float),  // h_s
+      p2 * sizeof(float),             // GEMM2 partials
+      own_quant ? T * H : 0,          // shared x_q
+      own_quant ? T * (H / kTile) * sizeof(float) : 0,  // shared x_s
+      sp1 * sizeof(float),            // shared gate_up partials
+      T * Is,                         // shared h_q
+      T * (Is / kTile) * sizeof(float),  // shared h_s
+      sp2 * sizeof(float),            // shared down partials
   };
   moe_decode_handle* h = new (std::nothrow) moe_decode_handle();
   if (!h) return MOE_DECODE_ERR_OUT_OF_MEMORY;
@@ -195,6 +278,7 @@ int moe_decode_create(const moe_decode_config* cfg, moe_decode_t* out) {
   }
   h->ws_bytes = off;
   h->words = (c.max_tokens + 63) / 64;
+  h->shared_own_quant = own_quant;
   if (hipGetDevice(&h->device) != hipSuccess) {
     delete h;
     return MOE_DECODE_ERR_HIP;
@@ -215,6 +299,13 @@ int moe_decode_create(const moe_decode_config* cfg, moe_decode_t* out) {
       (void)hipFree(h->ws);
       delete h;
       return MOE_DECODE_ERR_HIP;
+    }
+  }
+  if (Is > 0) {
+    const int r = prepare_shared_scales(h);
+    if (r != MOE_DECODE_OK) {
+      moe_decode_destroy(h);
+      return r;
     }
   }
   if (std::getenv("MOE_DECODE_DEBUG")) {
@@ -256,6 +347,14 @@ int moe_decode_plan(moe_decode_t h, int32_t M, int32_t* out, int32_t n) {
   out[6] = p.grid2;
   out[7] = p.tpw1;
   out[8] = p.tpw2;
+  if (n >= 15) {
+    out[9] = p.ss1;
+    out[10] = p.ss2;
+    out[11] = p.sks1;
+    out[12] = p.sks2;
+    out[13] = p.sunits1;
+    out[14] = p.sunits2;
+  }
   return MOE_DECODE_OK;
 }
 
@@ -271,7 +370,9 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   if (!aligned16(x) || !aligned16(slots) || !aligned16(combined) || !aligned16(logits) ||
       ((uintptr_t)ids & 3u) || ((uintptr_t)weights & 3u) || ((uintptr_t)bias & 3u))
     return MOE_DECODE_ERR_INVALID_ARG;
-  if (shared_out) return MOE_DECODE_ERR_INVALID_ARG;  // no shared expert in this handle
+  if (shared_out && (h->cfg.shared_inter == 0 || !aligned16(shared_out)))
+    return MOE_DECODE_ERR_INVALID_ARG;
+  const bool shared = shared_out != nullptr;
 
   const moe_decode_config& c = h->cfg;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -280,18 +381,21 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   unsigned char* ws = h->ws;
   auto at = [&](int i) { return ws + h->reg[i].off; };
 
+  auto atf = [&](int i) { return reinterpret_cast<float*>(at(i)); };
   Buckets b;
-  b.ctrl = reinterpret_cast<int32_t*>(at(0));
-  b.uexp = reinterpret_cast<int32_t*>(at(1));
-  b.uoff = reinterpret_cast<int32_t*>(at(2));
-  b.ucnt = reinterpret_cast<int32_t*>(at(3));
-  b.routes = reinterpret_cast<int32_t*>(at(4));
-  uint8_t* xq = at(5);
-  float* xs = reinterpret_cast<float*>(at(6));
-  float* p1 = reinterpret_cast<float*>(at(7));
-  uint8_t* hq = at(8);
-  float* hs = reinterpret_cast<float*>(at(9));
-  float* p2 = reinterpret_cast<float*>(at(10));
+  b.ctrl = reinterpret_cast<int32_t*>(at(kCtrl));
+  b.uexp = reinterpret_cast<int32_t*>(at(kUexp));
+  b.uoff = reinterpret_cast<int32_t*>(at(kUoff));
+  b.ucnt = reinterpret_cast<int32_t*>(at(kUcnt));
+  b.routes = reinterpret_cast<int32_t*>(at(kRoutes));
+  uint8_t* xq = at(kXq);
+  float* xs = atf(kXs);
+  float* p1 = atf(kP1);
+  uint8_t* hq = at(kHq);
+  float* hs = atf(kHs);
+  float* p2 = atf(kP2);
+  uint8_t* sxq = h->shared_own_quant ? at(kSXq) : xq;
+  float* sxs = h->shared_own_quant ? atf(kSXs) : xs;
 
   int evn = 0;
   // records an event closing timing slot `stage` (the first call opens)
@@ -319,6 +423,9 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   ra.weights = weights;
   ra.xq = xq;
   ra.xs = xs;
+  ra.xq2 = shared && h->shared_own_quant ? sxq : nullptr;
+  ra.xs2 = sxs;
+  ra.ue8m0_2 = c.shared_ue8m0_act;
   ra.b = b;
   if (e == hipSuccess) e = launch_route_quant(ra, s);
   if (e == hipSuccess) e = mark(0);
@@ -331,6 +438,14 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   sa.limit = c.limit;
   sa.hq = hq;
   sa.hs = hs;
+  sa.spart = shared ? atf(kSP1) : nullptr;
+  sa.ssplits = p.ss1;
+  sa.M = M;
+  sa.Is = c.shared_inter;
+  sa.slimit = c.shared_limit;
+  sa.sue8m0 = c.shared_ue8m0_act;
+  sa.shq = at(kSHq);
+  sa.shs = atf(kSHs);
 
   CombineArgs ca;
   ca.part = p2;
@@ -341,47 +456,61 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   ca.weights = weights;
   ca.slots = static_cast<uint16_t*>(slots);
   ca.combined = static_cast<uint16_t*>(combined);
+  ca.spart = shared ? atf(kSP2) : nullptr;
+  ca.ssplits = p.ss2;
+  ca.shared_out = static_cast<uint16_t*>(shared_out);
 
-  GemmArgs g1;
-  g1.w = static_cast<const uint8_t*>(c.w13);
-  g1.ws = c.w13_scale;
-  g1.aq = xq;
-  g1.as = xs;
-  g1.part = p1;
-  g1.b = b;
-  g1.N = 2 * c.inter;
-  g1.K = c.hidden;
-  g1.nkb = c.hidden / kTile;
-  g1.tiles = g1.N / kRowsPerWg;
-  g1.splits = p.s1;
-  g1.ks = p.ks1;
-  g1.R = R;
-  g1.act_div = c.top_k;
+  // problem descriptor of N x K weights and their activations
+  auto problem = [](const void* w, const float* ws, const uint8_t* aq, const float* as, float* part, int N,
+                    int K, int splits, int ks, int R, int act_div, int tpw) {
+    GemmProblem q{};
+    q.w = static_cast<const uint8_t*>(w);
+    q.ws = ws;
+    q.aq = aq;
+    q.as = as;
+    q.part = part;
+    q.N = N;
+    q.K = K;
+    q.nkb = K / kTile;
+    q.tiles = N / kRowsPerWg;
+    q.splits = splits;
+    q.ks = ks;
+    q.R = R;
+    q.act_div = act_div;
+    q.tpw = tpw;
+    return q;
+  };
+  auto launch_gemm = [&](const GemmArgs& g, int role, int grid) {
+    return p.path == MOE_GEMM_MFMA ? launch_gemm_mfma(g, role, grid, s) : launch_gemm_valu(g, role, grid, s);
+  };
+
+  GemmArgs g1{};
+  g1.p[1] = problem(c.w13, c.w13_scale, xq, xs, p1, 2 * c.inter, c.hidden, p.s1, p.ks1, R, c.top_k, p.tpw1);
+  g1.p[1].b = b;
   g1.pass_routes = p.pass_routes;
-  g1.tpw = p.tpw1;
-  if (e == hipSuccess)
-    e = p.path == MOE_GEMM_MFMA ? launch_gemm_mfma(g1, 1, p.grid1, s) : launch_gemm_valu(g1, 1, p.grid1, s);
+  if (shared) {
+    g1.p[0] = problem(c.sw13, h->s13, sxq, sxs, atf(kSP1), 2 * c.shared_inter, c.hidden, p.ss1, p.sks1, M, 1,
+                      p.stpw1);
+    g1.p[0].dense = M;
+    g1.units0 = p.sunits1;
+  }
+  if (e == hipSuccess) e = launch_gemm(g1, 1, p.grid1 - (shared ? 0 : p.sunits1));
   if (e == hipSuccess) e = mark(1);
 
   if (e == hipSuccess) e = launch_swiglu_requant(sa, s);
   if (e == hipSuccess) e = mark(2);
 
-  GemmArgs g2 = g1;
-  g2.w = static_cast<const uint8_t*>(c.w2);
-  g2.ws = c.w2_scale;
-  g2.aq = hq;
-  g2.as = hs;
-  g2.part = p2;
-  g2.N = c.hidden;
-  g2.K = c.inter;
-  g2.nkb = c.inter / kTile;
-  g2.tiles = g2.N / kRowsPerWg;
-  g2.splits = p.s2;
-  g2.ks = p.ks2;
-  g2.act_div = 1;
-  g2.tpw = p.tpw2;
-  if (e == hipSuccess)
-    e = p.path == MOE_GEMM_MFMA ? launch_gemm_mfma(g2, 2, p.grid2, s) : launch_gemm_valu(g2, 2, p.grid2, s);
+  GemmArgs g2{};
+  g2.p[1] = problem(c.w2, c.w2_scale, hq, hs, p2, c.hidden, c.inter, p.s2, p.ks2, R, 1, p.tpw2);
+  g2.p[1].b = b;
+  g2.pass_routes = p.pass_routes;
+  if (shared) {
+    g2.p[0] = problem(c.sw2, h->s2, at(kSHq), atf(kSHs), atf(kSP2), c.hidden, c.shared_inter, p.ss2, p.sks2,
+                      M, 1, p.stpw2);
+    g2.p[0].dense = M;
+    g2.units0 = p.sunits2;
+  }
+  if (e == hipSuccess) e = launch_gemm(g2, 2, p.grid2 - (shared ? 0 : p.sunits2));
   if (e == hipSuccess) e = mark(3);
 
   if (e == hipSuccess) e = launch_combine(ca, s);
@@ -393,7 +522,9 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
 }
 
 int moe_decode_debug_stage(moe_decode_t h, int32_t stage, void* dst, size_t bytes, void* stream) {
-  if (!h || !dst || stage < 0 || stage > 10) return MOE_DECODE_ERR_INVALID_ARG;
+  if (!h || !dst || stage < 0 || stage >= kRegions) return MOE_DECODE_ERR_INVALID_ARG;
+  if (stage >= kSXq && h->cfg.shared_inter == 0) return MOE_DECODE_ERR_INVALID_ARG;
+  if (!h->shared_own_quant && (stage == kSXq || stage == kSXs)) stage = stage == kSXq ? kXq : kXs;
   const Region& r = h->reg[stage];
   const size_t n = std::min(bytes, r.bytes);
   const hipError_t e =

@@ -7,6 +7,8 @@
 
 namespace moe {
 
+__device__ __forceinline__ float bf16_round(float v) { return bf16_value(bf16_bits(v)); }
+
 // One wave: the fixed-order sum of GEMM1's split partials for route r and
 // 128-block c of the hidden, the clamped SwiGLU and the FP8 hidden block
 // (vLLM "mega_moe" page, hidden_block): up = clamp(u, -L, L),
@@ -45,6 +47,48 @@ __device__ __forceinline__ void swiglu_route_block(const SwigluArgs& a, int r, i
   if (lane == 0) a.hs[(size_t)r * nblk + c] = s;
 }
 
+// One wave, shared expert ("shared_expert" page, _DownKernel and
+// _group_scale): token t, 128-block c of the shared hidden. gate/up are the
+// fixed-order split sums rounded to BF16 (rows 0..Is-1 gate, Is..2Is-1 up);
+// gate = min(gate, L), up = clamp(up, -L, L), silu = gate / (1 + exp(-gate))
+// in FP32 steps (exp correctly rounded), act = BF16(silu * up); per 128,
+// scale = max(amax, 1e-10) / 448, rounded up to a power of two with UE8M0,
+// q = e4m3(act * (1 / scale)).
+__device__ __forceinline__ void swiglu_shared_block(const SwigluArgs& a, int t, int c, int lane) {
+  const int nblk = a.Is / kTile;
+  const int j = c * kTile + 2 * lane;
+  const size_t row = (size_t)2 * a.Is;
+  float g0 = 0.f, g1 = 0.f, up0 = 0.f, up1 = 0.f;
+#pragma unroll 4
+  for (int s = 0; s < a.ssplits; ++s) {
+    const float* p = a.spart + ((size_t)s * a.M + t) * row;
+    const float2 g = *reinterpret_cast<const float2*>(p + j);
+    const float2 u = *reinterpret_cast<const float2*>(p + a.Is + j);
+    g0 += g.x;
+    g1 += g.y;
+    up0 += u.x;
+    up1 += u.y;
+  }
+  const float L = a.slimit;
+  g0 = fminf(bf16_round(g0), L);
+  g1 = fminf(bf16_round(g1), L);
+  up0 = fminf(fmaxf(bf16_round(up0), -L), L);
+  up1 = fminf(fmaxf(bf16_round(up1), -L), L);
+  const float e0 = (float)exp(-(double)g0), e1 = (float)exp(-(double)g1);
+  const float act0 = bf16_round((g0 / (1.f + e0)) * up0);
+  const float act1 = bf16_round((g1 / (1.f + e1)) * up1);
+  const float amax = group_max<kWave>(fmaxf(fabsf(act0), fabsf(act1)));
+  float s = fmaxf(amax, kAmaxFloor) / kFp8Max;
+  if (a.sue8m0) {
+    const uint32_t b = __float_as_uint(fmaxf(s, kAmaxFloor));
+    s = __uint_as_float(((b >> 23) + ((b & 0x7FFFFFu) != 0u)) << 23);
+  }
+  const float inv = 1.f / s;
+  const uint32_t q = e4m3x2_encode(act0 * inv, act1 * inv);
+  *reinterpret_cast<uint16_t*>(a.shq + (size_t)t * a.Is + j) = (uint16_t)q;
+  if (lane == 0) a.shs[(size_t)t * nblk + c] = s;
+}
+
 // The whole workgroup (256 threads): token t, hidden columns
 // [col0, col0 + 64). Each slot value is the fixed-order sum of GEMM2's split
 // partials rounded once to BF16; combined = BF16(sum_j w[t, j] * slot_j) with
@@ -69,6 +113,11 @@ __device__ __forceinline__ void combine_token_tile(const CombineArgs& a, int t, 
     float acc = 0.f;
     for (int j = 0; j < a.k; ++j) acc = fmaf(a.weights[(size_t)t * a.k + j], lds[j * 64 + c], acc);
     a.combined[(size_t)t * a.H + col0 + c] = (uint16_t)bf16_bits(acc);
+  } else if (tid < 128 && a.spart) {
+    // the shared expert's output: fixed-order split sum rounded once to BF16
+    float v = 0.f;
+    for (int s = 0; s < a.ssplits; ++s) v += a.spart[((size_t)s * a.M + t) * a.H + col0 + c];
+    a.shared_out[(size_t)t * a.H + col0 + c] = (uint16_t)bf16_bits(v);
   }
 }
 

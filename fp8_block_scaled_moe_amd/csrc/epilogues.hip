@@ -1,6 +1,6 @@
-// The SwiGLU/requant and slot/combine steps as kernels of their own (used
-// when the GEMMs' last-arriver epilogues are switched off). The arithmetic
-// lives in epilogue_device.h.
+// The SwiGLU/requant and slot/combine steps, each one launch that also covers
+// the shared expert when there is one; the arithmetic lives in
+// epilogue_device.h. Also the one-time conversion of packed UE8M0 scales.
 #include "epilogue_device.h"
 
 namespace moe {
@@ -8,12 +8,37 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// One wave per (route, 128-block of the hidden).
+// One wave per (route, 128-block of the hidden), then one per (token,
+// 128-block of the shared hidden).
 __global__ __launch_bounds__(kThreads) void swiglu_requant_kernel(SwigluArgs a) {
   const int nblk = a.I / kTile;
   const int gw = blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
-  if (gw >= a.R * nblk) return;  // whole waves exit together
-  swiglu_route_block(a, gw / nblk, gw % nblk, threadIdx.x & (kWave - 1));
+  const int lane = threadIdx.x & (kWave - 1);
+  const int routed = a.R * nblk;
+  if (gw < routed) {
+    swiglu_route_block(a, gw / nblk, gw % nblk, lane);
+    return;
+  }
+  if (!a.spart) return;
+  const int sblk = a.Is / kTile;
+  const int w = gw - routed;
+  if (w >= a.M * sblk) return;  // whole waves exit together
+  swiglu_shared_block(a, w / sblk, w % sblk, lane);
+}
+
+// Thread per (row n, K group g): the biased exponent byte of the packed word
+// becomes the FP32 scale 2^(byte - 127) (bits byte << 23) of block
+// (n / 128, g); every row must carry its block's first row's byte.
+__global__ void unpack_ue8m0_kernel(const int32_t* packed, int n, int k, float* out, int32_t* bad) {
+  const int groups = k / kTile, words = (groups + 3) / 4;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n * groups) return;
+  const int row = i / groups, g = i - row * groups;
+  const int lead = row - row % kTile;
+  const uint32_t e = ((uint32_t)packed[(size_t)row * words + g / 4] >> (8 * (g % 4))) & 0xFFu;
+  const uint32_t e0 = ((uint32_t)packed[(size_t)lead * words + g / 4] >> (8 * (g % 4))) & 0xFFu;
+  if (e != e0) atomicOr(bad, 1);
+  if (row == lead) out[(size_t)(row / kTile) * groups + g] = __uint_as_float(e << 23);
 }
 
 // One workgroup per (token, 64 hidden columns).
@@ -26,7 +51,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
 }  // namespace
 
 hipError_t launch_swiglu_requant(const SwigluArgs& a, hipStream_t s) {
-  const int waves = a.R * (a.I / kTile);
+  const int waves = a.R * (a.I / kTile) + (a.spart ? a.M * (a.Is / kTile) : 0);
   const int wpg = kThreads / kWave;
   hipLaunchKernelGGL(swiglu_requant_kernel, dim3((waves + wpg - 1) / wpg), dim3(kThreads), 0, s, a);
   return hipGetLastError();
@@ -34,6 +59,14 @@ hipError_t launch_swiglu_requant(const SwigluArgs& a, hipStream_t s) {
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(combine_kernel, dim3(a.M * (a.H / 64)), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack_ue8m0(const int32_t* packed, int n, int k, float* out, int32_t* bad,
+                               hipStream_t s) {
+  const int items = n * (k / kTile);
+  hipLaunchKernelGGL(unpack_ue8m0_kernel, dim3((items + 255) / 256), dim3(256), 0, s, packed, n, k, out,
+                     bad);
   return hipGetLastError();
 }
 

@@ -16,6 +16,13 @@
 // largest possible number of distinct experts; workgroups past the actual
 // count exit at once, so no host synchronisation is needed. The first weight
 // blocks are requested before the activations are staged.
+//
+// A launch may also carry a dense problem -- the shared expert, whose routes
+// are the tokens themselves -- whose units run first in the same grid, so the
+// shared expert's weights stream beside the routed experts' without a launch
+// of their own.
+#include <algorithm>
+
 #include "kernels.h"
 #include "device_common.h"
 
@@ -30,23 +37,41 @@ struct Unit {
   int ui, e, cnt, off, tile0, split, kb0, nb;
 };
 
-__device__ __forceinline__ bool decode_unit(const GemmArgs& a, Unit& u) {
-  const int U = a.b.ctrl[1];
+// The problem this workgroup works on (the dense problem's units come first)
+// and its unit index within that problem.
+__device__ __forceinline__ GemmProblem select_problem(const GemmArgs& a, int& unit) {
+  const bool dense = (int)blockIdx.x < a.units0;
+  unit = dense ? (int)blockIdx.x : (int)blockIdx.x - a.units0;
+  return dense ? a.p[0] : a.p[1];
+}
+
+__device__ __forceinline__ bool decode_unit(const GemmProblem& a, int unit, Unit& u) {
+  const int U = a.dense ? 1 : a.b.ctrl[1];
   const int groups = a.tiles / a.tpw;
   const int per_expert = groups * a.splits;
-  const int unit = blockIdx.x;
   if (unit >= U * per_expert) return false;
   u.ui = unit / per_expert;
   const int rem = unit - u.ui * per_expert;
   const int group = rem / a.splits;
   u.tile0 = group * a.tpw;
   u.split = rem - group * a.splits;
-  u.e = a.b.uexp[u.ui];
-  u.cnt = a.b.ucnt[u.ui];
-  u.off = a.b.uoff[u.ui];
+  if (a.dense) {
+    u.e = 0;
+    u.cnt = a.dense;
+    u.off = 0;
+  } else {
+    u.e = a.b.uexp[u.ui];
+    u.cnt = a.b.ucnt[u.ui];
+    u.off = a.b.uoff[u.ui];
+  }
   u.kb0 = u.split * a.ks;
   u.nb = min(a.ks, a.nkb - u.kb0);
   return true;
+}
+
+// Route index i of the unit's list.
+__device__ __forceinline__ int unit_route(const GemmProblem& a, const Unit& u, int i) {
+  return a.dense ? i : a.b.routes[u.off + i];
 }
 
 // Position of one 128-K block in the unit's stream (tile j, block b).
@@ -63,7 +88,7 @@ struct Cursor {
 // Weight scales of the unit's tiles (wsl[j * kMaxKs + b]) and activation
 // scales of the pass's routes (xsl[r * kMaxKs + b]); the block scale of
 // (tile j, route r, block b) is their product.
-__device__ __forceinline__ void stage_scales(const GemmArgs& a, const Unit& u, const int* rts, int nr,
+__device__ __forceinline__ void stage_scales(const GemmProblem& a, const Unit& u, const int* rts, int nr,
                                              float* wsl, float* xsl) {
   const float* ws = a.ws + (size_t)u.e * (a.N / kTile) * a.nkb + u.kb0;
   for (int i = threadIdx.x; i < a.tpw * u.nb; i += kThreads) {
@@ -86,14 +111,16 @@ __device__ __forceinline__ void stage_scales(const GemmArgs& a, const Unit& u, c
 // kRole only names the instantiation (1: W13 / GEMM1, 2: W2 / GEMM2), so that
 // profiles report the two GEMMs apart.
 template <int kRole>
-__global__ __launch_bounds__(kThreads) void gemm_valu_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kThreads) void gemm_valu_kernel(GemmArgs args) {
   __shared__ __align__(16) _Float16 xh[kValuRoutes * kMaxKs * kTile];
   __shared__ float xsl[kValuRoutes * kMaxKs];
   __shared__ float wsl[kMaxTpw * kMaxKs];
   __shared__ int rts[kValuRoutes];
 
+  int unit;
+  const GemmProblem a = select_problem(args, unit);
   Unit u;
-  if (!decode_unit(a, u)) return;
+  if (!decode_unit(a, unit, u)) return;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int rg = lane >> 3, ch = lane & 7;
   const int rows_in_tile = wave * 16 + rg;  // and + 8
@@ -122,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void gemm_valu_kernel(GemmArgs a) {
   for (int c0 = 0; c0 < u.cnt; c0 += kValuRoutes) {
     const int nr = min(kValuRoutes, u.cnt - c0);
     if (c0) __syncthreads();
-    if (tid < nr) rts[tid] = a.b.routes[u.off + c0 + tid];
+    if (tid < nr) rts[tid] = unit_route(a, u, c0 + tid);
     __syncthreads();
     // the routes' activations for this split as exact F16, and the scales
     {
@@ -254,9 +281,11 @@ __device__ __forceinline__ void wave_lds_fence() {
 }
 
 template <int kRole>
-__global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmArgs args) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int nrp = a.pass_routes;         // routes per pass, <= 16
+  int unit;
+  const GemmProblem a = select_problem(args, unit);
+  const int nrp = args.pass_routes;      // routes per pass, <= 16
   const int stride = a.ks * kTile + 16;  // bytes per staged route row: +16 B against bank conflicts
   uint8_t* tiles = smem;                                           // [4 waves][kTileBytes]
   uint8_t* xb = smem + 4 * kTileBytes;                             // [nrp][stride] e4m3
@@ -265,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmArgs a) {
   int* rts = reinterpret_cast<int*>(wsl + kMaxTpw * kMaxKs);
 
   Unit u;
-  if (!decode_unit(a, u)) return;
+  if (!decode_unit(a, unit, u)) return;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int rg = lane >> 3, ch = lane & 7;   // load layout
   const int col = lane & 15, g = lane >> 4;  // MFMA layout
@@ -295,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmArgs a) {
   for (int c0 = 0; c0 < u.cnt; c0 += nrp) {
     const int nr = min(nrp, u.cnt - c0);
     if (c0) __syncthreads();
-    if (tid < nr) rts[tid] = a.b.routes[u.off + c0 + tid];
+    if (tid < nr) rts[tid] = unit_route(a, u, c0 + tid);
     __syncthreads();
     {  // the routes' activations for this split, e4m3 as stored
       const int per_route = u.nb * 8;  // 16-byte chunks
@@ -392,7 +421,8 @@ hipError_t launch_gemm_valu(const GemmArgs& a, int role, int grid, hipStream_t s
 }
 
 hipError_t launch_gemm_mfma(const GemmArgs& a, int role, int grid, hipStream_t s) {
-  const size_t lds = gemm_mfma_lds_bytes(a.pass_routes, a.ks);
+  const int ks = a.units0 ? std::max(a.p[0].ks, a.p[1].ks) : a.p[1].ks;
+  const size_t lds = gemm_mfma_lds_bytes(a.pass_routes, ks);
   if (role == 1)
     hipLaunchKernelGGL(gemm_mfma_kernel<1>, dim3(grid), dim3(kThreads), lds, s, a);
   else

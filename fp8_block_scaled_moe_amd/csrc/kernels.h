@@ -32,6 +32,9 @@ struct RouteQuantArgs {
   float* weights;       // [M, k]
   uint8_t* xq;          // [M, H]
   float* xs;            // [M, H/128]
+  uint8_t* xq2;         // second quantisation of x (shared expert), or nullptr
+  float* xs2;
+  int ue8m0_2;
   Buckets b;
 };
 
@@ -41,6 +44,14 @@ struct SwigluArgs {
   float limit;
   uint8_t* hq;          // [R, I]
   float* hs;            // [R, I/128]
+  // Shared expert (spart == nullptr when absent): GEMM partials
+  // [ssplits, M, 2Is], gate rows first.
+  const float* spart;
+  int ssplits, M, Is;
+  float slimit;
+  int sue8m0;
+  uint8_t* shq;         // [M, Is]
+  float* shs;           // [M, Is/128]
 };
 
 struct CombineArgs {
@@ -49,28 +60,44 @@ struct CombineArgs {
   const float* weights; // [M, k]
   uint16_t* slots;      // [M*k, H] bf16
   uint16_t* combined;   // [M, H] bf16
+  const float* spart;   // shared expert's down partials [ssplits, M, H], or nullptr
+  int ssplits;
+  uint16_t* shared_out; // [M, H] bf16
 };
 
-// One block-scaled GEMM pass over the touched experts: for every route r of
-// distinct expert u and every weight row n,
+// One block-scaled GEMM problem: for every route r of distinct expert u and
+// every weight row n,
 //   part[split, r, n] = sum_{b in split} ws[e, n/128, b] * as[row(r), b] *
 //                       sum_{i in block b} W[e, n, i] * A[row(r), i]
-// with row(r) = r / act_div.
-struct GemmArgs {
+// with row(r) = r / act_div. A routed problem takes its experts and routes
+// from the buckets; a dense one (the shared expert) is expert 0 with routes
+// 0..dense-1, one per token.
+struct GemmProblem {
   const uint8_t* w;     // [E, N, K] e4m3
   const float* ws;      // [E, N/128, K/128]
   const uint8_t* aq;    // [rows, K] e4m3
   const float* as;      // [rows, K/128]
   float* part;          // [splits, R, N]
-  Buckets b;
+  Buckets b;            // routed problems only
+  int dense;            // > 0: dense problem of this many routes
   int N, K, nkb;        // nkb = K / 128
   int tiles;            // N / 64
   int splits, ks;       // K splits and 128-blocks per split
   int R;                // routes (row stride of part)
   int act_div;
-  int pass_routes;      // MFMA path: routes staged per pass (<= 16)
   int tpw;              // 64-row tiles streamed per workgroup (divides tiles, <= kMaxTpw)
 };
+
+// One GEMM launch: the dense problem's units (if any) come first in the grid,
+// then the routed problem's.
+struct GemmArgs {
+  GemmProblem p[2];     // [0] dense (shared expert), [1] routed
+  int units0;           // work units of p[0]; 0 when there is none
+  int pass_routes;      // MFMA path: routes staged per pass (<= 16)
+};
+
+// Work units of a problem per expert: (tiles / tpw) tile groups x splits.
+inline int gemm_units_per_expert(const GemmProblem& p) { return (p.tiles / p.tpw) * p.splits; }
 
 // Maximum 128-blocks of K per split (bounds the LDS staging of activations).
 constexpr int kMaxKs = 16;
@@ -87,6 +114,10 @@ hipError_t launch_route_quant(const RouteQuantArgs& a, hipStream_t s);
 hipError_t launch_gemm_valu(const GemmArgs& a, int role, int grid, hipStream_t s);
 hipError_t launch_gemm_mfma(const GemmArgs& a, int role, int grid, hipStream_t s);
 size_t gemm_mfma_lds_bytes(int pass_routes, int ks);
+// FP32 [n/128, k/128] scales from packed UE8M0 words int32 [n, ceil(k/512)];
+// *bad is set nonzero when the rows of a 128-row block disagree.
+hipError_t launch_unpack_ue8m0(const int32_t* packed, int n, int k, float* out, int32_t* bad,
+                               hipStream_t s);
 hipError_t launch_swiglu_requant(const SwigluArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_codec_check(const float* in, uint8_t* q, float* dq, int n, hipStream_t s);

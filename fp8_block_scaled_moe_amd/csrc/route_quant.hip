@@ -165,22 +165,28 @@ __device__ void quant_tokens(const RouteQuantArgs& a, int t0, int ntok) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
         amax = group_max<8>(amax);
-        float s = amax / kFp8Max;
-        if (a.ue8m0) {
-          const uint32_t b = __float_as_uint(fmaxf(s, kAmaxFloor));
-          s = __uint_as_float(((b >> 23) + ((b & 0x7FFFFFu) != 0u)) << 23);
-        }
-        const float inv = 1.0f / s;
-        u32x4_t out;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          out[w] = e4m3x4_encode(v[4 * w] * inv, v[4 * w + 1] * inv, v[4 * w + 2] * inv,
-                                 v[4 * w + 3] * inv);
-        }
         const int t = t0 + item / nblk, blk = item % nblk;
         const size_t at = (size_t)t * a.H + (size_t)blk * kTile + sub * 16;
-        *reinterpret_cast<u32x4_t*>(a.xq + at) = out;
-        if (sub == 0) a.xs[(size_t)t * nblk + blk] = s;
+        // scale = amax / 448, optionally rounded up to a power of two; codes
+        // = e4m3(v * (1 / scale))
+        auto emit = [&](int ue8m0, uint8_t* xq, float* xs) {
+          float s = amax / kFp8Max;
+          if (ue8m0) {
+            const uint32_t b = __float_as_uint(fmaxf(s, kAmaxFloor));
+            s = __uint_as_float(((b >> 23) + ((b & 0x7FFFFFu) != 0u)) << 23);
+          }
+          const float inv = 1.0f / s;
+          u32x4_t out;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            out[w] = e4m3x4_encode(v[4 * w] * inv, v[4 * w + 1] * inv, v[4 * w + 2] * inv,
+                                   v[4 * w + 3] * inv);
+          }
+          *reinterpret_cast<u32x4_t*>(xq + at) = out;
+          if (sub == 0) xs[(size_t)t * nblk + blk] = s;
+        };
+        emit(a.ue8m0, a.xq, a.xs);
+        if (a.xq2) emit(a.ue8m0_2, a.xq2, a.xs2);  // the shared expert's own scale rule
       }
     }
   }

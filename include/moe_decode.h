@@ -97,7 +97,9 @@ typedef struct moe_decode_config {
   const float* w2_scale;
 
   /* Optional dense shared expert ("shared_expert" page); all zero/NULL when
-   * absent. shared_inter (Is) is a multiple of 128.
+   * absent. shared_inter (Is) is a multiple of 128. Its units run inside the
+   * routed GEMM, SwiGLU and combine launches. The packed scales must repeat
+   * one exponent over each 128-row block (INVALID_ARG from create if not).
    * sw13 [2Is, H] e4m3, rows 0..Is-1 gate, Is..2Is-1 up; sw2 [H, Is] e4m3.
    * Scales per shared_scale_format: FP32 [2Is/128, H/128] / [H/128, Is/128],
    * or MOE_SCALES_UE8M0_PACKED int32 [2Is, ceil(H/512)] / [H, ceil(Is/512)]
@@ -159,8 +161,12 @@ const char* moe_decode_error_string(int code);
 /* The launch plan run() uses for M tokens: out[0] = GEMM path used
  * (MOE_GEMM_VALU or MOE_GEMM_MFMA), out[1] = splits1, out[2] = splits2,
  * out[3] = blocks per split in GEMM1, out[4] = in GEMM2, out[5] = grid of
- * GEMM1, out[6] = grid of GEMM2, out[7] / out[8] = 64-row tiles streamed per
- * workgroup in GEMM1 / GEMM2. n is the capacity of out (>= 9). */
+ * GEMM1, out[6] = grid of GEMM2 (both including the shared expert's units
+ * when the handle has one), out[7] / out[8] = 64-row tiles streamed per
+ * workgroup in GEMM1 / GEMM2. With n >= 15 also the shared expert's plan
+ * (zeros without one): out[9] / out[10] = K splits of its gate_up / down
+ * GEMV, out[11] / out[12] = blocks per split, out[13] / out[14] = work units
+ * in the GEMM1 / GEMM2 launches. n is the capacity of out (>= 9). */
 int moe_decode_plan(moe_decode_t h, int32_t M, int32_t* out, int32_t n);
 
 /* Stage read-back: copies workspace region `stage` of the last run into the
@@ -172,6 +178,12 @@ int moe_decode_plan(moe_decode_t h, int32_t M, int32_t* out, int32_t n);
  *  7 GEMM1 split partials FP32 [splits1, M*k, 2I]
  *  8 h_q [M*k, I] e4m3                      9 h_s [M*k, I/128] FP32
  * 10 GEMM2 split partials FP32 [splits2, M*k, H]
+ * Shared expert (handles with one; INVALID_ARG otherwise):
+ * 11 its x_q [M, H] e4m3                   12 its x_s [M, H/128] FP32
+ *    (the routed stages 5 and 6 when both use the same scale rule)
+ * 13 gate_up split partials FP32 [splits, M, 2Is]
+ * 14 h_q [M, Is] e4m3                      15 h_s [M, Is/128] FP32
+ * 16 down split partials FP32 [splits, M, H]
  * The size copied is min(bytes, size of the stage for the handle's maximum). */
 int moe_decode_debug_stage(moe_decode_t h, int32_t stage, void* dst, size_t bytes,
                            void* stream);
@@ -179,9 +191,9 @@ int moe_decode_debug_stage(moe_decode_t h, int32_t stage, void* dst, size_t byte
 /* Per-kernel timing of subsequent runs with HIP events recorded between the
  * launches (enable != 0; not for use under graph capture). After a run has
  * completed, moe_decode_last_timing writes the milliseconds of each launch in
- * order: route+quant, GEMM1, SwiGLU+requant, GEMM2, combine, shared gate_up,
- * shared down (0 for a launch that did not run). n is the capacity of ms
- * (>= 7). */
+ * order: route+quant, GEMM1, SwiGLU+requant, GEMM2, combine (the shared
+ * expert, when run, is part of the last four). n is the capacity of ms
+ * (>= 5). */
 int moe_decode_set_timing(moe_decode_t h, int32_t enable);
 int moe_decode_last_timing(moe_decode_t h, float* ms, int32_t n);
 

@@ -28,6 +28,7 @@ from .moe import (  # noqa: F401
     requantize_hidden,
     route,
     shared_expert,
+    silu_f32,
     swiglu,
     ue8m0_round_up,
     unpack_ue8m0,

@@ -39,11 +39,11 @@ def oracle_layer(inp, **over):
     return oracle.moe_decode(host(inp.x), host(inp.logits), host(inp.bias), expert_fn(inp), **kw)
 
 
-def oracle_shared(inp):
+def oracle_shared(inp, ue8m0_act: bool = True):
     s = inp.shape
     return oracle.shared_expert(host(inp.x), inp.sw13.cpu().numpy(), host(inp.sw13_scale),
                                 inp.sw2.cpu().numpy(), host(inp.sw2_scale),
-                                limit=s.shared_limit, ue8m0_act=True)
+                                limit=s.shared_limit, ue8m0_act=ue8m0_act)
 
 
 def row_errors(got: np.ndarray, ref: np.ndarray) -> np.ndarray:

@@ -58,6 +58,9 @@ def _cfg(**kw):
     return c
 
 
+_SHARED = dict(sw13=8192, sw13_scale=8192, sw2=8192, sw2_scale=8192, shared_limit=7.0)
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(hidden=200), _capi.ERR_UNSUPPORTED),
     (dict(inter=100), _capi.ERR_UNSUPPORTED),
@@ -73,6 +76,13 @@ def _cfg(**kw):
     (dict(w2_scale=4100), _capi.ERR_INVALID_ARG),   # misaligned
     (dict(gemm_path=5), _capi.ERR_UNSUPPORTED),
     (dict(splits1=-1), _capi.ERR_INVALID_ARG),
+    # shared expert
+    (dict(shared_inter=-128), _capi.ERR_INVALID_ARG),
+    (dict(shared_inter=128), _capi.ERR_INVALID_ARG),                  # no shared weights
+    (dict(shared_inter=100, **_SHARED), _capi.ERR_UNSUPPORTED),
+    (dict(shared_inter=128, shared_scale_format=2, **_SHARED), _capi.ERR_UNSUPPORTED),
+    (dict(dict(_SHARED, shared_limit=0.0), shared_inter=128), _capi.ERR_INVALID_ARG),
+    (dict(dict(_SHARED, sw2=4104), shared_inter=128), _capi.ERR_INVALID_ARG),  # misaligned
 ])
 def test_create_rejects_bad_config(L, kw, code):
     h = ctypes.c_void_p(1234)
