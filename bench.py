@@ -6,8 +6,10 @@ One step = one moe_decode_run (routing, activation quant, GEMM1, SwiGLU +
 requant, GEMM2, combine) on resident synthetic inputs. Before every step a
 1 GiB buffer is overwritten so that the weights come from HBM, not from L2 or
 the 256 MB MALL; the flush is outside the per-layer events. Counted bytes =
-distinct experts touched x (W13 + W2 FP8 bytes + FP32 scales). Prints one JSON
-line. The default workload is the DeepSeek-V3-shaped decode at M=4.
+distinct experts touched x (W13 + W2 FP8 bytes + FP32 scales), plus the shared
+expert's weights and scales for a workload that has one. Prints one JSON line
+(one per M with --sweep). The default workload is the DeepSeek-V3-shaped decode
+at M=4.
 """
 
 from __future__ import annotations
@@ -34,9 +36,11 @@ PEAK_HBM_GBS = 8000.0
 # for a plain 256 MiB copy). Valid only for the profiled workload and while the
 # GEMM sources are byte-identical to the profiled ones; otherwise null.
 GEMM1_TRAFFIC = {
-    "sources_sha256_16": "c00379b9943dc02e",
+    "sources_sha256_16": "0219c4fa4a5134fd",
     "workload": "dsv3", "M": 4, "seed": 0, "unique_experts": 27,
-    "fetch_bytes": 774327 * 1024, "write_bytes": 2098464,
+    # medians per dispatch (KiB) and the copy kernel's reading of 256 MiB
+    "fetch_kib": 387476.31, "write_kib": 2049.62,
+    "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0,
 }
 GEMM_SOURCES = ["fp8_block_scaled_moe_amd/csrc/expert_gemm.hip",
                 "fp8_block_scaled_moe_amd/csrc/device_common.h",
@@ -53,7 +57,11 @@ def gemm1_traffic(workload: str, M: int, seed: int, U: int):
     if (h.hexdigest()[:16] != t["sources_sha256_16"] or (workload, M, seed, U) !=
             (t["workload"], t["M"], t["seed"], t["unique_experts"])):
         return None
-    return t["fetch_bytes"] + t["write_bytes"]
+    fetch = t["fetch_kib"] * (262144.0 / t["copy_fetch_kib"])
+    write = t["write_kib"] * (262144.0 / t["copy_write_kib"])
+    return int(round((fetch + write) * 1024))
+
+
 METRIC = "routed-MoE decode µs/layer + achieved HBM GB/s (% peak) at M=1..64 tokens"
 KERNELS = ["route_quant", "gemm1", "swiglu_requant", "gemm2", "combine"]
 
@@ -112,10 +120,12 @@ def cpu_baseline(inp, counted_bytes: int) -> dict:
     """The oracle on the host cores, once, on the same inputs (the whole layer
     for all M tokens: it reads only the touched experts)."""
     from threadpoolctl import threadpool_info
-    from tests.helpers import oracle_layer
+    from tests.helpers import oracle_layer, oracle_shared
 
     t0 = time.perf_counter()
     oracle_layer(inp)
+    if inp.shape.shared_inter:
+        oracle_shared(inp)
     dt = time.perf_counter() - t0
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
     return {"value": counted_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads),
@@ -128,17 +138,21 @@ def run_one(args, shape, inp, moe, flush):
     dev = inp.x.device
     k = shape.top_k
     slots, ids, weights, combined = moe.outputs(shape.M)
+    shared_out = None
+    if shape.shared_inter:
+        shared_out = torch.empty((shape.M, shape.hidden), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
     def step():
-        moe.run_into(inp.x, inp.logits, inp.bias, slots, ids, weights, combined, stream=stream)
+        moe.run_into(inp.x, inp.logits, inp.bias, slots, ids, weights, combined,
+                     shared_out=shared_out, stream=stream)
 
     for _ in range(args.warmup):
         flush.zero_()
         step()
     torch.cuda.synchronize()
     U = int(torch.unique(ids).numel())
-    counted = U * shape.expert_bytes()
+    counted = U * shape.expert_bytes() + shape.shared_bytes()
 
     # pass 1: whole layer, events on torch's current stream (the library's stream)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -183,24 +197,34 @@ def main():
     maxM = max(Ms)
     shape = base.with_(M=maxM)
     inp_all = synth.make_inputs(shape, seed=args.seed, device=dev)
+    shared = {}
+    if shape.shared_inter:
+        shared = dict(sw13=inp_all.sw13, sw13_scale=inp_all.sw13_scale, sw2=inp_all.sw2,
+                      sw2_scale=inp_all.sw2_scale, shared_limit=shape.shared_limit,
+                      shared_ue8m0_act=True)
     moe = MoeDecode(inp_all.w13, inp_all.w13_scale, inp_all.w2, inp_all.w2_scale,
                     top_k=shape.top_k, limit=shape.limit, routed_scale=shape.routed_scale,
                     max_tokens=maxM, logits_dtype=inp_all.logits.dtype, ue8m0_act=shape.ue8m0_act,
-                    gemm_path=args.path, splits1=args.splits1, splits2=args.splits2)
+                    gemm_path=args.path, splits1=args.splits1, splits2=args.splits2, **shared)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     for M in Ms:
         sh = base.with_(M=M)
         inp = synth.MoeInputs(shape=sh, seed=args.seed, x=inp_all.x[:M].contiguous(),
                               logits=inp_all.logits[:M].contiguous(), bias=inp_all.bias,
                               w13=inp_all.w13, w13_scale=inp_all.w13_scale, w2=inp_all.w2,
-                              w2_scale=inp_all.w2_scale)
+                              w2_scale=inp_all.w2_scale, sw13=inp_all.sw13,
+                              sw13_scale=inp_all.sw13_scale, sw2=inp_all.sw2,
+                              sw2_scale=inp_all.sw2_scale)
         r = run_one(args, sh, inp, moe, flush)
-        ms = float(np.mean(r["layer_ms"]))
+        ms = float(np.median(r["layer_ms"]))
         us = ms * 1e3
         gbs = r["counted"] / (ms * 1e-3) / 1e9
-        per = r["per_kernel_ms"].mean(axis=0)
-        # dominant kernel: GEMM1 streams W13 (2/3 of the counted bytes)
+        # dominant kernel: GEMM1 streams W13 (2/3 of the counted bytes), and
+        # the shared expert's gate_up weights when there is one
         g1_bytes = r["U"] * (2 * sh.inter * sh.hidden + (2 * sh.inter // 128) * (sh.hidden // 128) * 4)
+        if sh.shared_inter:
+            g1_bytes += 2 * sh.shared_inter * sh.hidden + (2 * sh.shared_inter // 128) * (sh.hidden // 128) * 4
+        per = np.median(r["per_kernel_ms"], axis=0)
         g1_gbs = g1_bytes / (per[1] * 1e-3) / 1e9
         plan = moe.plan(M)
         line = {
@@ -231,7 +255,8 @@ def main():
                 "l2_mall_flush": "1 GiB overwrite before every step, outside the timed layer",
             },
             "roofline": {
-                "kernel": "gemm1 (W13 up/gate GEMM over the touched experts)",
+                "kernel": "gemm1 (W13 up/gate GEMM over the touched experts"
+                          + (" and the shared gate_up)" if sh.shared_inter else ")"),
                 "bound": "hbm",
                 "achieved": round(g1_gbs, 1),
                 "peak": PEAK_HBM_GBS,
