@@ -42,7 +42,8 @@ GEMM1_TRAFFIC = {
     "fetch_kib": 387476.31, "write_kib": 2049.62,
     "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0,
 }
-GEMM_SOURCES = ["fp8_block_scaled_moe_amd/csrc/expert_gemm.hip",
+GEMM_SOURCES = ["fp8_block_scaled_moe_amd/csrc/expert_gemm_wg.hip",
+                "fp8_block_scaled_moe_amd/csrc/gemm_device.h",
                 "fp8_block_scaled_moe_amd/csrc/device_common.h",
                 "fp8_block_scaled_moe_amd/csrc/kernels.h"]
 
@@ -74,7 +75,7 @@ def parse():
     p.add_argument("--workload", default="dsv3", choices=sorted(synth.CONFIGS))
     p.add_argument("--M", type=int, default=0, help="tokens (default: the workload's)")
     p.add_argument("--seed", type=int, default=0)
-    p.add_argument("--path", default="auto", choices=["auto", "valu", "mfma"])
+    p.add_argument("--path", default="auto", choices=["auto", "valu_splitk", "mfma_splitk", "mfma"])
     p.add_argument("--splits1", type=int, default=0)
     p.add_argument("--splits2", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -250,8 +251,9 @@ def main():
                 "pct_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
                 "kernel_us": {k: round(float(v) * 1e3, 2) for k, v in zip(KERNELS, per)},
                 "wall_ms_per_step_incl_flush": round(r["wall_s"] / args.steps * 1e3, 4),
-                "gemm_path": {1: "valu", 2: "mfma"}[plan["path"]],
+                "gemm_path": {1: "valu_splitk", 2: "mfma_splitk", 3: "mfma"}[plan["path"]],
                 "splits": [plan["splits1"], plan["splits2"]],
+                "kparts": [plan["kparts1"], plan["kparts2"]],
                 "l2_mall_flush": "1 GiB overwrite before every step, outside the timed layer",
             },
             "roofline": {

@@ -28,7 +28,7 @@ DTYPE_F32 = 0
 DTYPE_BF16 = 1
 SCALES_F32 = 0
 SCALES_UE8M0_PACKED = 1
-GEMM_PATHS = {"auto": 0, "valu": 1, "mfma": 2}
+GEMM_PATHS = {"auto": 0, "valu_splitk": 1, "mfma_splitk": 2, "mfma": 3}
 
 STAGES = {
     "ctrl": 0, "uexp": 1, "uoff": 2, "ucnt": 3, "routes": 4, "x_q": 5, "x_s": 6,
@@ -246,13 +246,13 @@ class MoeDecode:
 
     # -- introspection ------------------------------------------------------
     def plan(self, M: int) -> dict:
-        buf = (ctypes.c_int32 * 15)()
-        rc = lib().moe_decode_plan(self._h, M, buf, 15)
+        buf = (ctypes.c_int32 * 17)()
+        rc = lib().moe_decode_plan(self._h, M, buf, 17)
         if rc != OK:
             raise MoeDecodeError(rc, "moe_decode_plan")
-        keys = ("path", "splits1", "splits2", "ks1", "ks2", "grid1", "grid2", "tpw1", "tpw2",
+        keys = ("path", "splits1", "splits2", "ks1", "ks2", "grid1", "grid2", "rows1", "rows2",
                 "shared_splits1", "shared_splits2", "shared_ks1", "shared_ks2",
-                "shared_units1", "shared_units2")
+                "shared_units1", "shared_units2", "kparts1", "kparts2")
         return dict(zip(keys, list(buf)))
 
     def stage(self, name: str, dst: torch.Tensor, stream=None) -> torch.Tensor:

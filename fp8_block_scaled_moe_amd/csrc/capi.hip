@@ -21,6 +21,8 @@ constexpr int kRegions = 17;
 constexpr int kStages = 5;  // timing slots: route, GEMM1, SwiGLU, GEMM2, combine
 constexpr int kTargetUnits = 4096;  // work units per GEMM launch to aim for (16 per CU)
 constexpr int kDenseTargetUnits = 256;  // units of the shared expert per GEMM launch
+constexpr int kWgTargetUnits = 4096;    // K-in-workgroup path: units to aim for (16 per CU)
+constexpr int kWgMinPartBlocks = 14;    // shortest per-wave weight stream worth a K part (128-K blocks)
 constexpr int kBadFlagWord = 32;        // word of the control region used by create
 
 // Workspace regions (the debug stages use the same numbering).
@@ -38,6 +40,8 @@ struct Plan {
   int tpw1, tpw2;   // 64-row tiles per workgroup
   // shared expert (all zero without one)
   int ss1, sks1, ss2, sks2, stpw1, stpw2, sunits1, sunits2;
+  // K-in-workgroup path: K parts per row group (routed, shared)
+  int kp1, kp2, skp1, skp2;
 };
 
 struct Region {
@@ -106,25 +110,67 @@ void plan_dense(int M, int N, int K, int max_ks, int want_tpw, int* splits, int*
   *units = groups * *splits;
 }
 
+// K parts per row group of the K-in-workgroup kernel: the fewest (longest
+// weight streams per wave) that give about kWgTargetUnits units, as long as
+// each part keeps kWgMinPartBlocks blocks (measured on MI355X: GEMM2's
+// 16-block rows streamed at 65.5 us whole and 68.4 us in two parts, GEMM1's
+// 56-block rows at 124.6 us whole, 123.3 in two and 122.5 in four parts, at
+// 27 experts). A forced value is rounded down to 1, 2 or 4 and kept at two
+// blocks per part at least.
+int choose_kparts(int experts, int N, int nkb, int forced) {
+  int kp = 1;
+  if (forced > 0) {
+    kp = forced >= 4 ? 4 : (forced >= 2 ? 2 : 1);
+    while (kp > 1 && nkb < 2 * kp) kp /= 2;
+    return kp;
+  }
+  while (kp < 4 && experts * (N / (kRowsPerWg / kp)) < kWgTargetUnits && nkb / (2 * kp) >= kWgMinPartBlocks)
+    kp *= 2;
+  return kp;
+}
+
 Plan make_plan(const moe_decode_config& c, int M) {
   Plan p{};
   const int R = M * c.top_k;
   p.umax = std::min(c.experts, R);
   const int tiles1 = 2 * c.inter / kRowsPerWg, tiles2 = c.hidden / kRowsPerWg;
+  if (c.gemm_path == MOE_GEMM_AUTO || c.gemm_path == MOE_GEMM_MFMA) {
+    // K summed inside the workgroup: no split-K partials leave the chip
+    p.path = MOE_GEMM_MFMA;
+    p.pass_routes = kMfmaRoutes;
+    p.s1 = p.s2 = 1;
+    p.kp1 = choose_kparts(p.umax, 2 * c.inter, c.hidden / kTile, c.splits1);
+    p.kp2 = choose_kparts(p.umax, c.hidden, c.inter / kTile, c.splits2);
+    p.ks1 = ceil_div(c.hidden / kTile, p.kp1);
+    p.ks2 = ceil_div(c.inter / kTile, p.kp2);
+    p.tpw1 = kRowsPerWg / p.kp1;  // rows per workgroup
+    p.tpw2 = kRowsPerWg / p.kp2;
+    p.grid1 = p.umax * (2 * c.inter / p.tpw1);
+    p.grid2 = p.umax * (c.hidden / p.tpw2);
+    if (c.shared_inter > 0) {
+      p.ss1 = p.ss2 = 1;
+      p.skp1 = choose_kparts(1, 2 * c.shared_inter, c.hidden / kTile, p.kp1);
+      p.skp2 = choose_kparts(1, c.hidden, c.shared_inter / kTile, p.kp2);
+      p.sks1 = ceil_div(c.hidden / kTile, p.skp1);
+      p.sks2 = ceil_div(c.shared_inter / kTile, p.skp2);
+      p.sunits1 = 2 * c.shared_inter / (kRowsPerWg / p.skp1);
+      p.sunits2 = c.hidden / (kRowsPerWg / p.skp2);
+      p.grid1 += p.sunits1;
+      p.grid2 += p.sunits2;
+    }
+    return p;
+  }
   // MFMA costs the same per weight byte for any number of routes of an
   // expert (up to 16 per pass), VALU dot products cost per route. Measured on
   // MI355X with every expert taking n routes (E=64, H=7168, I=2048), GEMM1
   // streams at 6.69/6.67 TB/s (VALU/MFMA) for n=1, 5.68/5.86 for n=4,
   // 4.10/5.46 for n=8 and 2.01/5.06 for n=16; so MFMA unless every expert has
   // exactly one route (M = 1).
-  if (c.gemm_path == MOE_GEMM_AUTO)
-    p.path = M == 1 ? MOE_GEMM_VALU : MOE_GEMM_MFMA;
-  else
-    p.path = c.gemm_path;
+  p.path = c.gemm_path;
   // an expert has at most one route per token
   p.pass_routes = std::min(kMfmaRoutes, M);
   int max_ks = kMaxKs;
-  if (p.path == MOE_GEMM_MFMA)
+  if (p.path == MOE_GEMM_MFMA_SPLITK)
     while (max_ks > 1 && gemm_mfma_lds_bytes(p.pass_routes, max_ks) > kMfmaLdsBudget) --max_ks;
   // Staging a unit's activations costs about as much as streaming a few
   // blocks of weights per route; with many tokens (so many routes per
@@ -161,6 +207,8 @@ int validate_config(const moe_decode_config* c) {
   if (c->logits_dtype != MOE_DTYPE_F32 && c->logits_dtype != MOE_DTYPE_BF16)
     return MOE_DECODE_ERR_UNSUPPORTED;
   if (c->gemm_path < MOE_GEMM_AUTO || c->gemm_path > MOE_GEMM_MFMA) return MOE_DECODE_ERR_UNSUPPORTED;
+  if (gemm_wg_lds_bytes(std::max(c->hidden, std::max(c->inter, c->shared_inter)) / kTile) > kMaxWgLds)
+    return MOE_DECODE_ERR_UNSUPPORTED;
   if (c->splits1 < 0 || c->splits2 < 0) return MOE_DECODE_ERR_INVALID_ARG;
   {
     const int words = (c->max_tokens + 63) / 64;
@@ -355,6 +403,10 @@ int moe_decode_plan(moe_decode_t h, int32_t M, int32_t* out, int32_t n) {
     out[13] = p.sunits1;
     out[14] = p.sunits2;
   }
+  if (n >= 17) {
+    out[15] = p.path == MOE_GEMM_MFMA ? p.kp1 : 1;
+    out[16] = p.path == MOE_GEMM_MFMA ? p.kp2 : 1;
+  }
   return MOE_DECODE_OK;
 }
 
@@ -481,17 +533,23 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
     return q;
   };
   auto launch_gemm = [&](const GemmArgs& g, int role, int grid) {
-    return p.path == MOE_GEMM_MFMA ? launch_gemm_mfma(g, role, grid, s) : launch_gemm_valu(g, role, grid, s);
+    switch (p.path) {
+      case MOE_GEMM_MFMA: return launch_gemm_wg(g, role, grid, s);
+      case MOE_GEMM_MFMA_SPLITK: return launch_gemm_mfma(g, role, grid, s);
+      default: return launch_gemm_valu(g, role, grid, s);
+    }
   };
 
   GemmArgs g1{};
   g1.p[1] = problem(c.w13, c.w13_scale, xq, xs, p1, 2 * c.inter, c.hidden, p.s1, p.ks1, R, c.top_k, p.tpw1);
   g1.p[1].b = b;
+  g1.p[1].kparts = p.kp1;
   g1.pass_routes = p.pass_routes;
   if (shared) {
     g1.p[0] = problem(c.sw13, h->s13, sxq, sxs, atf(kSP1), 2 * c.shared_inter, c.hidden, p.ss1, p.sks1, M, 1,
                       p.stpw1);
     g1.p[0].dense = M;
+    g1.p[0].kparts = p.skp1;
     g1.units0 = p.sunits1;
   }
   if (e == hipSuccess) e = launch_gemm(g1, 1, p.grid1 - (shared ? 0 : p.sunits1));
@@ -503,11 +561,13 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   GemmArgs g2{};
   g2.p[1] = problem(c.w2, c.w2_scale, hq, hs, p2, c.hidden, c.inter, p.s2, p.ks2, R, 1, p.tpw2);
   g2.p[1].b = b;
+  g2.p[1].kparts = p.kp2;
   g2.pass_routes = p.pass_routes;
   if (shared) {
     g2.p[0] = problem(c.sw2, h->s2, at(kSHq), atf(kSHs), atf(kSP2), c.hidden, c.shared_inter, p.ss2, p.sks2,
                       M, 1, p.stpw2);
     g2.p[0].dense = M;
+    g2.p[0].kparts = p.skp2;
     g2.units0 = p.sunits2;
   }
   if (e == hipSuccess) e = launch_gemm(g2, 2, p.grid2 - (shared ? 0 : p.sunits2));

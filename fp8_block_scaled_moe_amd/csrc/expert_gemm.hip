@@ -23,8 +23,7 @@
 // of their own.
 #include <algorithm>
 
-#include "kernels.h"
-#include "device_common.h"
+#include "gemm_device.h"
 
 namespace moe {
 namespace {
@@ -36,14 +35,6 @@ constexpr int kStageBatch = 4;
 struct Unit {
   int ui, e, cnt, off, tile0, split, kb0, nb;
 };
-
-// The problem this workgroup works on (the dense problem's units come first)
-// and its unit index within that problem.
-__device__ __forceinline__ GemmProblem select_problem(const GemmArgs& a, int& unit) {
-  const bool dense = (int)blockIdx.x < a.units0;
-  unit = dense ? (int)blockIdx.x : (int)blockIdx.x - a.units0;
-  return dense ? a.p[0] : a.p[1];
-}
 
 __device__ __forceinline__ bool decode_unit(const GemmProblem& a, int unit, Unit& u) {
   const int U = a.dense ? 1 : a.b.ctrl[1];
@@ -263,23 +254,6 @@ __global__ __launch_bounds__(kThreads) void gemm_valu_kernel(GemmArgs args) {
 // of the block, g = l / 16, and the activations of route l % 16 with the same
 // bytes, so each block's 128 products are summed exactly once.
 // ---------------------------------------------------------------------------
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-
-constexpr int kTileStride = kTile + 16;       // bytes per row of a wave's weight tile
-constexpr int kTileBytes = 16 * kTileStride;  // one wave's 16 rows
-
-__device__ __forceinline__ half8_t widen8(uint32_t w0, uint32_t w1) {
-  const half2_t a = e4m3x2_to_f16x2<false>(w0), b = e4m3x2_to_f16x2<true>(w0);
-  const half2_t c = e4m3x2_to_f16x2<false>(w1), d = e4m3x2_to_f16x2<true>(w1);
-  return half8_t{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
-}
-
-// Orders this wave's LDS accesses around the tile exchange (a wave's LDS
-// operations complete in order; this keeps the compiler from moving them).
-__device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-}
-
 template <int kRole>
 __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmArgs args) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -376,14 +350,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmArgs args) {
           const u32x4_t xlo = *reinterpret_cast<const u32x4_t*>(xr + b * kTile);
           const u32x4_t xhi = *reinterpret_cast<const u32x4_t*>(xr + b * kTile + 64);
           wave_lds_fence();
-          float4_t p = __builtin_amdgcn_mfma_f32_16x16x32_f16(widen8(wlo[0], wlo[1]),
-                                                              widen8(xlo[0], xlo[1]), zero, 0, 0, 0);
-          p = __builtin_amdgcn_mfma_f32_16x16x32_f16(widen8(wlo[2], wlo[3]), widen8(xlo[2], xlo[3]), p,
-                                                     0, 0, 0);
-          p = __builtin_amdgcn_mfma_f32_16x16x32_f16(widen8(whi[0], whi[1]), widen8(xhi[0], xhi[1]), p,
-                                                     0, 0, 0);
-          p = __builtin_amdgcn_mfma_f32_16x16x32_f16(widen8(whi[2], whi[3]), widen8(xhi[2], xhi[3]), p,
-                                                     0, 0, 0);
+          const float4_t p = mfma_block(wlo, whi, xlo, xhi);
           const float s = wsl[at.j * kMaxKs + b] * xs_col[b];
           acc[0] = fmaf(p[0], s, acc[0]);
           acc[1] = fmaf(p[1], s, acc[1]);

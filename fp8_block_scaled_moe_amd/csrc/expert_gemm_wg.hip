@@ -1,0 +1,181 @@
+// Block-scaled FP8 GEMM over the touched experts with the whole K reduction
+// inside one workgroup.
+//
+// Same sum as the split-K kernels (expert_gemm.hip): every 128-K block's
+// partial is multiplied by (weight scale x activation scale) of that block
+// before it joins the FP32 total ("mega_moe" page, module docstring). What
+// differs is where the K sum is finished. Writing split-K partial sums to
+// memory in the middle of the weight stream costs far more than their bytes
+// on MI355X: the FP32 partials are written back to HBM between the weight
+// reads. Measured with every expert taking 16 routes, GEMM1 streamed at
+// 6.7 TB/s with the partials kept in L2 and 5.1 TB/s with them written out.
+// So here a workgroup owns 16, 32 or 64 weight rows of one expert over all of
+// K: its four waves split K into `kparts` contiguous ranges (four row groups
+// x one range, two x two, or one x four), and add their 16 x 16 results
+// through LDS in a fixed order. One FP32 value per (route, row) leaves the
+// chip.
+//
+// Per step a wave takes one 128-K block of its 16 rows. The weights are read
+// with eight lanes per row (full 128-byte segments, nontemporal) and passed
+// through a per-wave LDS tile into the MFMA layout. The activations of the
+// pass's 16 routes come straight from L2 into registers in the MFMA layout,
+// so no LDS staging bounds how much of K a workgroup covers. Both streams are
+// requested kDepth steps ahead.
+#include <algorithm>
+
+#include "gemm_device.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kDepth = 2;          // 128-K steps in flight per wave (keeps four waves per SIMD)
+constexpr int kRoutesPerPass = 16;  // MFMA columns
+constexpr int kRedFloats = 4 * kWave * 4;  // the four waves' 16 x 16 results
+
+template <int kRole>
+__global__ __launch_bounds__(kThreads) void gemm_wg_kernel(GemmArgs args) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int unit;
+  const GemmProblem a = select_problem(args, unit);
+  const int kparts = a.kparts;
+  const int rows_wg = kRowsPerWg / kparts;
+  const int per_expert = a.N / rows_wg;
+  const int U = a.dense ? 1 : a.b.ctrl[1];
+  if (unit >= U * per_expert) return;  // past the touched experts: the whole workgroup exits
+  const int ui = unit / per_expert, tile = unit - ui * per_expert;
+  int e, cnt, off;
+  if (a.dense) {
+    e = 0;
+    cnt = a.dense;
+    off = 0;
+  } else {
+    e = a.b.uexp[ui];
+    cnt = a.b.ucnt[ui];
+    off = a.b.uoff[ui];
+  }
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int rgrp = wave / kparts, kp = wave - rgrp * kparts;
+  const int row0 = tile * rows_wg + rgrp * 16;  // this wave's 16 rows
+  const int kb0 = (kp * a.nkb) / kparts;
+  const int nsteps = ((kp + 1) * a.nkb) / kparts - kb0;
+  const int rg = lane >> 3, ch = lane & 7;   // load layout
+  const int col = lane & 15, g = lane >> 4;  // MFMA layout
+
+  uint8_t* tile_lds = smem + wave * kTileBytes;                      // [4][kTileBytes]
+  float* red = reinterpret_cast<float*>(smem + 4 * kTileBytes);       // [4 waves][64 lanes][4]
+  float* wsl = red + kRedFloats;                                      // [4 row groups][nkb]
+  float* xsl = wsl + 4 * a.nkb;                                       // [nkb][16]
+  int* rts = reinterpret_cast<int*>(xsl + a.nkb * kRoutesPerPass);    // [16]
+
+  const uint8_t* pw = a.w + ((size_t)e * a.N + row0 + rg) * a.K + (size_t)kb0 * kTile + ch * 16;
+  const size_t half_step = (size_t)8 * a.K;
+  u32x4_t wa[kDepth], wb[kDepth], xa[kDepth], xb[kDepth];
+  auto load_w = [&](int q, int st) {
+    const uint8_t* p = pw + (size_t)st * kTile;
+    wa[q] = load_stream16(p);
+    wb[q] = load_stream16(p + half_step);
+  };
+
+  for (int c0 = 0; c0 < cnt; c0 += kRoutesPerPass) {
+    const int nr = min(kRoutesPerPass, cnt - c0);
+    if (c0) __syncthreads();  // the previous pass is done with rts, xsl and red
+#pragma unroll
+    for (int q = 0; q < kDepth; ++q)
+      if (q < nsteps) load_w(q, q);
+    if (tid < nr) rts[tid] = a.dense ? c0 + tid : a.b.routes[off + c0 + tid];
+    if (c0 == 0) {
+      // weight scales of the workgroup's row groups: one 128-row scale block each
+      const float* ws = a.ws + (size_t)e * (a.N / kTile) * a.nkb;
+      for (int i = tid; i < (kRowsPerWg / 16) * a.nkb; i += kThreads) {
+        const int r = i / a.nkb, b = i - r * a.nkb;
+        if (r < 4 / kparts) wsl[i] = ws[(size_t)((tile * rows_wg + r * 16) / kTile) * a.nkb + b];
+      }
+    }
+    __syncthreads();
+
+    const bool live = col < nr;
+    const int xrow = rts[live ? col : 0] / a.act_div;  // lanes past the routes repeat route 0
+    const uint8_t* px = a.aq + (size_t)xrow * a.K + (size_t)kb0 * kTile + g * 16;
+    auto load_x = [&](int q, int st) {
+      const uint8_t* p = px + (size_t)st * kTile;
+      xa[q] = *reinterpret_cast<const u32x4_t*>(p);
+      xb[q] = *reinterpret_cast<const u32x4_t*>(p + 64);
+    };
+#pragma unroll
+    for (int q = 0; q < kDepth; ++q)
+      if (q < nsteps) load_x(q, q);
+    for (int i = tid; i < nr * a.nkb; i += kThreads) {
+      const int r = i / a.nkb, b = i - r * a.nkb;
+      xsl[b * kRoutesPerPass + r] = a.as[(size_t)(rts[r] / a.act_div) * a.nkb + b];
+    }
+    __syncthreads();
+
+    const float* wsr = wsl + rgrp * a.nkb + kb0;
+    const float* xsr = xsl + kb0 * kRoutesPerPass + (live ? col : 0);
+    float4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int st0 = 0; st0 < nsteps; st0 += kDepth) {
+#pragma unroll
+      for (int q = 0; q < kDepth; ++q) {
+        const int st = st0 + q;
+        if (st < nsteps) {
+          *reinterpret_cast<u32x4_t*>(tile_lds + rg * kTileStride + ch * 16) = wa[q];
+          *reinterpret_cast<u32x4_t*>(tile_lds + (rg + 8) * kTileStride + ch * 16) = wb[q];
+          const u32x4_t xlo = xa[q], xhi = xb[q];
+          if (st + kDepth < nsteps) {
+            load_w(q, st + kDepth);
+            load_x(q, st + kDepth);
+          }
+          wave_lds_fence();
+          const u32x4_t wlo = *reinterpret_cast<const u32x4_t*>(tile_lds + col * kTileStride + g * 16);
+          const u32x4_t whi = *reinterpret_cast<const u32x4_t*>(tile_lds + col * kTileStride + 64 + g * 16);
+          wave_lds_fence();
+          const float4_t p = mfma_block(wlo, whi, xlo, xhi);
+          const float s = wsr[st] * xsr[st * kRoutesPerPass];
+          acc[0] = fmaf(p[0], s, acc[0]);
+          acc[1] = fmaf(p[1], s, acc[1]);
+          acc[2] = fmaf(p[2], s, acc[2]);
+          acc[3] = fmaf(p[3], s, acc[3]);
+        }
+      }
+    }
+
+    if (kparts > 1) {  // K parts of a row group added in a fixed order: part 0, 1, ...
+      *reinterpret_cast<float4_t*>(red + (wave * kWave + lane) * 4) = acc;
+      __syncthreads();
+      if (kp == 0) {
+        for (int j = 1; j < kparts; ++j) {
+          const float4_t o = *reinterpret_cast<const float4_t*>(red + ((wave + j) * kWave + lane) * 4);
+          acc[0] += o[0];
+          acc[1] += o[1];
+          acc[2] += o[2];
+          acc[3] += o[3];
+        }
+      }
+    }
+    if (kp == 0 && live) {
+      float* dst = a.part + (size_t)rts[col] * a.N + row0 + 4 * g;
+      *reinterpret_cast<float4_t*>(dst) = acc;
+    }
+  }
+}
+
+}  // namespace
+
+size_t gemm_wg_lds_bytes(int nkb) {
+  return 4 * (size_t)kTileBytes + kRedFloats * 4 + (size_t)4 * nkb * 4 + (size_t)nkb * kRoutesPerPass * 4 +
+         kRoutesPerPass * 4;
+}
+
+hipError_t launch_gemm_wg(const GemmArgs& a, int role, int grid, hipStream_t s) {
+  const int nkb = a.units0 ? std::max(a.p[0].nkb, a.p[1].nkb) : a.p[1].nkb;
+  const size_t lds = gemm_wg_lds_bytes(nkb);
+  if (role == 1)
+    hipLaunchKernelGGL(gemm_wg_kernel<1>, dim3(grid), dim3(kThreads), lds, s, a);
+  else
+    hipLaunchKernelGGL(gemm_wg_kernel<2>, dim3(grid), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

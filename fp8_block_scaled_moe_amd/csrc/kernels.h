@@ -85,7 +85,8 @@ struct GemmProblem {
   int splits, ks;       // K splits and 128-blocks per split
   int R;                // routes (row stride of part)
   int act_div;
-  int tpw;              // 64-row tiles streamed per workgroup (divides tiles, <= kMaxTpw)
+  int tpw;              // split-K kernels: 64-row tiles streamed per workgroup (divides tiles, <= kMaxTpw)
+  int kparts;           // K-in-workgroup kernel: K ranges per row group (1, 2 or 4); 64 / kparts rows
 };
 
 // One GEMM launch: the dense problem's units (if any) come first in the grid,
@@ -107,6 +108,7 @@ constexpr int kMfmaRoutes = 16;  // routes per pass of the MFMA inner product
 constexpr int kMaxTpw = 4;
 constexpr size_t kMfmaLdsBudget = 40 * 1024;  // keeps three workgroups per CU
 constexpr size_t kMaxRouteLds = 64 * 1024;
+constexpr size_t kMaxWgLds = 64 * 1024;
 
 size_t route_quant_lds_bytes(int E, int words, int routes);
 hipError_t launch_route_quant(const RouteQuantArgs& a, hipStream_t s);
@@ -114,6 +116,10 @@ hipError_t launch_route_quant(const RouteQuantArgs& a, hipStream_t s);
 hipError_t launch_gemm_valu(const GemmArgs& a, int role, int grid, hipStream_t s);
 hipError_t launch_gemm_mfma(const GemmArgs& a, int role, int grid, hipStream_t s);
 size_t gemm_mfma_lds_bytes(int pass_routes, int ks);
+// The kernel with the whole K sum inside a workgroup (no split-K partials):
+// writes one FP32 value per (route, row) to part[0].
+hipError_t launch_gemm_wg(const GemmArgs& a, int role, int grid, hipStream_t s);
+size_t gemm_wg_lds_bytes(int nkb);
 // FP32 [n/128, k/128] scales from packed UE8M0 words int32 [n, ceil(k/512)];
 // *bad is set nonzero when the rows of a 128-row block disagree.
 hipError_t launch_unpack_ue8m0(const int32_t* packed, int n, int k, float* out, int32_t* bad,

@@ -64,14 +64,21 @@ extern "C" {
 #define MOE_SCALES_F32 0         /* FP32 [n/128, k/128] block scales */
 #define MOE_SCALES_UE8M0_PACKED 1 /* int32 [n, ceil(k/512)]: byte g%4 of word g/4 = biased exponent of K group g */
 
-#define MOE_GEMM_AUTO 0  /* choose the inner product per call */
-#define MOE_GEMM_VALU 1  /* exact FP8->F16 widening + F16 dot2 into FP32 */
-#define MOE_GEMM_MFMA 2  /* exact FP8->F16 widening + v_mfma_f32_16x16x32_f16 (16 routes at once) */
+/* GEMM kernels. All widen FP8 exactly to F16 and add exact products in FP32.
+ * The split-K paths divide K among workgroups and sum FP32 partials in the
+ * next kernel; MOE_GEMM_MFMA sums all of K inside one workgroup. */
+#define MOE_GEMM_AUTO 0         /* MOE_GEMM_MFMA */
+#define MOE_GEMM_VALU_SPLITK 1  /* F16 dot2, split-K over workgroups */
+#define MOE_GEMM_MFMA_SPLITK 2  /* v_mfma_f32_16x16x32_f16 (16 routes at once), split-K over workgroups */
+#define MOE_GEMM_MFMA 3         /* v_mfma_f32_16x16x32_f16, K split among the waves of a workgroup */
 
 /* Limits of this implementation. */
 #define MOE_DECODE_MAX_EXPERTS 1024
 #define MOE_DECODE_MAX_TOP_K 32
 #define MOE_DECODE_MAX_TOKENS 256
+/* hidden, inter and shared_inter are also bounded by the LDS the GEMM kernel
+ * stages per workgroup: 13,376 + 80 * max(hidden, inter, shared_inter) / 128
+ * bytes must not exceed 64 KiB, i.e. at most 83,456 (ERR_UNSUPPORTED). */
 
 typedef struct moe_decode_config {
   /* Shapes. hidden (H) and inter (I) are multiples of 128; 1 <= top_k <=
@@ -114,8 +121,10 @@ typedef struct moe_decode_config {
   const void* sw2_scale;
 
   /* Tuning (0 = automatic). gemm_path: MOE_GEMM_*. splits1/splits2: K splits
-   * of GEMM1/GEMM2 (work units are 64 weight rows x one K split of one touched
-   * expert). */
+   * of GEMM1/GEMM2: over workgroups on the split-K paths (a work unit is 64
+   * weight rows x one K split of one touched expert), over the waves of a
+   * workgroup on MOE_GEMM_MFMA (1, 2 or 4; a workgroup then owns 64, 32 or 16
+   * weight rows). */
   int32_t gemm_path;
   int32_t splits1;
   int32_t splits2;
@@ -159,14 +168,17 @@ const char* moe_decode_error_string(int code);
 /* ---- Introspection (tests and benchmarks) ------------------------------ */
 
 /* The launch plan run() uses for M tokens: out[0] = GEMM path used
- * (MOE_GEMM_VALU or MOE_GEMM_MFMA), out[1] = splits1, out[2] = splits2,
- * out[3] = blocks per split in GEMM1, out[4] = in GEMM2, out[5] = grid of
- * GEMM1, out[6] = grid of GEMM2 (both including the shared expert's units
- * when the handle has one), out[7] / out[8] = 64-row tiles streamed per
- * workgroup in GEMM1 / GEMM2. With n >= 15 also the shared expert's plan
- * (zeros without one): out[9] / out[10] = K splits of its gate_up / down
- * GEMV, out[11] / out[12] = blocks per split, out[13] / out[14] = work units
- * in the GEMM1 / GEMM2 launches. n is the capacity of out (>= 9). */
+ * (MOE_GEMM_*, never AUTO), out[1] / out[2] = partial-sum slices GEMM1 /
+ * GEMM2 write (the K splits of the split-K paths; 1 on MOE_GEMM_MFMA),
+ * out[3] / out[4] = 128-K blocks per split or per K part, out[5] / out[6] =
+ * grids of GEMM1 / GEMM2 (including the shared expert's units when the
+ * handle has one), out[7] / out[8] = on the split-K paths 64-row tiles
+ * streamed per workgroup, on MOE_GEMM_MFMA weight rows per workgroup. With
+ * n >= 15 also the shared expert's plan (zeros without one): out[9] /
+ * out[10] = its partial-sum slices, out[11] / out[12] = blocks per split or
+ * part, out[13] / out[14] = its work units in the GEMM1 / GEMM2 launches.
+ * With n >= 17: out[15] / out[16] = K parts per workgroup in GEMM1 / GEMM2
+ * (1 on the split-K paths). n is the capacity of out (>= 9). */
 int moe_decode_plan(moe_decode_t h, int32_t M, int32_t* out, int32_t n);
 
 /* Stage read-back: copies workspace region `stage` of the last run into the

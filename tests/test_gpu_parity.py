@@ -21,6 +21,7 @@ from tests.helpers import (WEIGHT_RTOL, assert_rows_close, expert_fn, host, orac
 pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
+PATHS = ["valu_splitk", "mfma_splitk", "mfma"]
 
 
 def make(inp, M=None, **kw):
@@ -83,7 +84,7 @@ def gpu_h1(moe, inp, M):
 # v_dot2 pairs then per-lane and cross-lane adds, the MFMA path with the F16
 # 16x16x32 instruction's FP32 sums; a few hundred roundings of 2**-24 at most,
 # bounded here by 2**-20.
-H1_BOUND = {"valu": 2.0**-20, "mfma": 2.0**-20}
+H1_BOUND = {"valu_splitk": 2.0**-20, "mfma_splitk": 2.0**-20, "mfma": 2.0**-20}
 
 
 def h1_bound(inp, ref, path):
@@ -162,7 +163,7 @@ def test_device_codec():
     assert np.array_equal(d[~nan], ref[~nan])
 
 
-@pytest.mark.parametrize("path", ["valu", "mfma"])
+@pytest.mark.parametrize("path", PATHS)
 def test_tiny(path):
     inp = synth.make_inputs(synth.CONFIGS["tiny"], seed=0, device=DEV)
     moe = make(inp, gemm_path=path)
@@ -183,7 +184,7 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("path", ["valu", "mfma"])
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("name,over", SHAPES, ids=[s[0] for s in SHAPES])
 def test_shapes(name, over, path):
     shape = synth.CONFIGS["tiny"].with_(name=name, **over)
@@ -192,7 +193,7 @@ def test_shapes(name, over, path):
     full_check(moe, inp)
 
 
-@pytest.mark.parametrize("path", ["valu", "mfma"])
+@pytest.mark.parametrize("path", PATHS)
 def test_skewed_routing_many_routes_per_expert(path):
     """Two experts taken by every token: 40 routes on one expert, more than one
     pass of either inner product."""
@@ -204,7 +205,7 @@ def test_skewed_routing_many_routes_per_expert(path):
     assert np.all(np.sort(ids.cpu().numpy()[:, :2], axis=1) == [5, 17])
 
 
-@pytest.mark.parametrize("path", ["valu", "mfma"])
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("splits", [(1, 1), (3, 2), (0, 0)])
 def test_exact_pow2_case(path, splits):
     """Integer weights, pow2 scales, integer activations with a +-7 in every
@@ -240,7 +241,7 @@ def test_zero_inputs():
     assert not slots.float().abs().max().item() and not combined.float().abs().max().item()
 
 
-@pytest.mark.parametrize("path", ["valu", "mfma"])
+@pytest.mark.parametrize("path", PATHS)
 def test_deterministic_and_token_independent(path):
     shape = synth.CONFIGS["tiny"].with_(M=9, hidden=512, inter=256, experts=20, top_k=4)
     inp = synth.make_inputs(shape, seed=15, device=DEV)
@@ -286,7 +287,7 @@ def dsv3():
     return synth.make_inputs(synth.CONFIGS["dsv3"], seed=0, device=DEV)
 
 
-@pytest.mark.parametrize("path", ["valu", "mfma"])
+@pytest.mark.parametrize("path", PATHS)
 def test_dsv3_m4(dsv3, path):
     moe = make(dsv3, gemm_path=path)
     full_check(moe, dsv3, stages=True)
@@ -312,13 +313,13 @@ def _sampled(inp, M_run, sample, path):
     np.testing.assert_allclose(host(weights), rw, rtol=WEIGHT_RTOL, atol=0)
 
 
-@pytest.mark.parametrize("path", ["valu", "mfma"])
+@pytest.mark.parametrize("path", PATHS)
 def test_dsv3_m32_sampled(path):
     inp = synth.make_inputs(synth.CONFIGS["dsv3"].with_(M=32), seed=1, device=DEV)
     _sampled(inp, 32, [0, 13, 31], path)
 
 
-@pytest.mark.parametrize("path", ["valu", "mfma"])
+@pytest.mark.parametrize("path", PATHS)
 def test_latent_m64_sampled(path):
     inp = synth.make_inputs(synth.CONFIGS["latent"], seed=0, device=DEV)
     _sampled(inp, 64, [0, 21, 63], path)

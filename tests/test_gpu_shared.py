@@ -23,6 +23,7 @@ from tests.helpers import (WEIGHT_RTOL, assert_rows_close, host, oracle_layer, o
 pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
+PATHS = ["valu_splitk", "mfma_splitk", "mfma"]
 
 
 def make(inp, shared=True, packed=False, shared_ue8m0=True, max_tokens=None, **kw):
@@ -101,7 +102,7 @@ SMALL = synth.CONFIGS["tiny"].with_(name="shared_small", M=5, hidden=512, inter=
                                     top_k=3, shared_inter=384)
 
 
-@pytest.mark.parametrize("path", ["valu", "mfma"])
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("packed", [False, True], ids=["f32_scales", "ue8m0_packed"])
 def test_shared_small(path, packed):
     inp = synth.make_inputs(SMALL, seed=21, device=DEV)
@@ -126,7 +127,7 @@ def test_shared_small(path, packed):
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("path", ["valu", "mfma"])
+@pytest.mark.parametrize("path", PATHS)
 def test_shared_exact_pow2(path):
     """Integer weights and activations with power-of-two scales: every gate_up
     sum is exact in FP32, so the FP8 hidden and its scales agree bit for bit."""
