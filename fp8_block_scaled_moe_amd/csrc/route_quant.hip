@@ -121,7 +121,9 @@ __device__ void route_token(const RouteQuantArgs& a, int t, int lane, int* ids_l
   if (lane < a.k) {
     const float w = (my_score / total) * a.routed_scale;
     const size_t at = (size_t)t * a.k + lane;
-    a.ids[at] = my_id;
+    // written through to the device coherence point: another workgroup (on
+    // another XCD, with its own L2) may read it in the cross-workgroup handoff
+    __hip_atomic_store(a.ids + at, my_id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     a.weights[at] = w;
     ids_l[at] = my_id;
   }
@@ -336,17 +338,23 @@ __global__ __launch_bounds__(kThreads) void route_quant_kernel(RouteQuantArgs a)
     bucket_any(a, l);
     return;
   }
-  // Publish this workgroup's picks, then count arrivals; the last arrival
-  // reads every workgroup's picks.
-  __threadfence();
+  // Count arrivals once this workgroup's picks are published; the last
+  // arrival reads every workgroup's picks. The picks were stored at device
+  // scope, so waiting for those stores to complete publishes them: no fence
+  // here writes back the rest of the L2 (which a release fence would do, at
+  // the cost of every dirty line earlier kernels left there).
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) is_last = atomicAdd(a.b.ctrl, 1) == (int)gridDim.x - 1;
+  if (threadIdx.x == 0)
+    is_last = __hip_atomic_fetch_add(a.b.ctrl, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              (int)gridDim.x - 1;
   __syncthreads();
   if (!is_last) return;
-  __threadfence();
   if (threadIdx.x == 0) __hip_atomic_store(a.b.ctrl, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  for (int r = threadIdx.x; r < a.M * a.k; r += kThreads)
-    l.ids[r] = __hip_atomic_load(a.ids + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int r = threadIdx.x; r < a.M * a.k; r += kThreads) {
+    const int id = __hip_atomic_load(a.ids + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    l.ids[r] = min(max(id, 0), a.E - 1);  // keeps the bucket indexing in bounds whatever it reads
+  }
   __syncthreads();
   bucket_any(a, l);
 }
