@@ -36,10 +36,10 @@ PEAK_HBM_GBS = 8000.0
 # for a plain 256 MiB copy). Valid only for the profiled workload and while the
 # GEMM sources are byte-identical to the profiled ones; otherwise null.
 GEMM1_TRAFFIC = {
-    "sources_sha256_16": "0219c4fa4a5134fd",
+    "sources_sha256_16": "cdfecc9e308ffdc9",
     "workload": "dsv3", "M": 4, "seed": 0, "unique_experts": 27,
     # medians per dispatch (KiB) and the copy kernel's reading of 256 MiB
-    "fetch_kib": 387476.31, "write_kib": 2049.62,
+    "fetch_kib": 387777.25, "write_kib": 512.0,
     "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0,
 }
 GEMM_SOURCES = ["fp8_block_scaled_moe_amd/csrc/expert_gemm_wg.hip",

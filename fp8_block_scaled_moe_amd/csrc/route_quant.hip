@@ -9,11 +9,11 @@
 // power of two after flooring it at 1e-10, then v * (1 / scale) encoded to
 // e4m3.
 //
-// Launch: one 1024-thread workgroup for up to 8 tokens, else one per 4
-// tokens; a wave routes each token, then all 16 waves quantise. With one
-// workgroup the routes are grouped by expert right away (by one wave when
-// there are at most 64 routes, else through LDS); with several, the last
-// workgroup to arrive (atomic counter, reset by that workgroup) does it.
+// Launch: one 1024-thread workgroup per 4 tokens; waves 0..3 (one per SIMD)
+// each route one token, then all 16 waves quantise. With one workgroup the
+// routes are grouped by expert right away (by one wave when there are at most
+// 64 routes, else through LDS); with several, the last workgroup to arrive
+// (atomic counter, reset by that workgroup) does it.
 #include "kernels.h"
 #include "device_common.h"
 
@@ -22,13 +22,11 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;  // 16
-// Tokens per workgroup, one routing wave each. Routing is VALU-issue bound
-// (FP64 sigmoid, 64-bit DPP maxima), so tokens are spread one per SIMD when
-// there are many; up to eight share one workgroup, which then skips the
-// cross-workgroup handoff (measured on MI355X at M = 8: 13.0 us in one
-// workgroup against 17.2 us in two).
+// Tokens per workgroup, one routing wave each, one per SIMD: routing is
+// VALU-issue bound (FP64 sigmoid, 64-bit DPP maxima), so two routing waves
+// on a SIMD take twice as long (measured on MI355X at M = 8: 11.6 us as two
+// workgroups against 13.0 us as one).
 constexpr int kTokensPerWg = 4;
-constexpr int kTokensSingleWg = 8;
 
 // Monotone image of an FP32 value in uint32: a > b as floats (with -0 < +0)
 // iff key(a) > key(b). Negatives flip every bit, the rest flip the sign bit.
@@ -328,9 +326,8 @@ __global__ __launch_bounds__(kThreads) void route_quant_kernel(RouteQuantArgs a)
   __shared__ int is_last;
   const Lds l = carve(lds, a.E, a.words, a.M * a.k);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int per_wg = a.M <= kTokensSingleWg ? kTokensSingleWg : kTokensPerWg;
-  const int t0 = blockIdx.x * per_wg;
-  const int ntok = min(per_wg, a.M - t0);
+  const int t0 = blockIdx.x * kTokensPerWg;
+  const int ntok = min(kTokensPerWg, a.M - t0);
   if (wave < ntok) route_token_any(a, t0 + wave, lane, l.ids);
   quant_tokens(a, t0, ntok);
   if (gridDim.x == 1) {
@@ -377,8 +374,7 @@ size_t route_quant_lds_bytes(int E, int words, int routes) {
 }
 
 hipError_t launch_route_quant(const RouteQuantArgs& a, hipStream_t s) {
-  const int per_wg = a.M <= kTokensSingleWg ? kTokensSingleWg : kTokensPerWg;
-  const int grid = (a.M + per_wg - 1) / per_wg;
+  const int grid = (a.M + kTokensPerWg - 1) / kTokensPerWg;
   hipLaunchKernelGGL(route_quant_kernel, dim3(grid), dim3(kThreads),
                      route_quant_lds_bytes(a.E, a.words, a.M * a.k), s, a);
   return hipGetLastError();
