@@ -19,6 +19,7 @@ Parity status of each function is listed in its docstring; every function
 here is pinned by a `-m "not gpu"` test in tests/test_oracle_*.py.
 """
 
+from . import fp4  # noqa: F401
 from .codecs import bf16_round, e4m3_decode, e4m3_encode, f32, E4M3_VALUES  # noqa: F401
 from .moe import (  # noqa: F401
     block_scaled_gemm,
