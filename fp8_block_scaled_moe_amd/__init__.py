@@ -10,6 +10,7 @@ from ._capi import (  # noqa: F401
     MoeDecodeConfig,
     MoeDecodeError,
     debug_codec,
+    debug_codec_fp4,
     error_string,
     header_functions,
     lib,

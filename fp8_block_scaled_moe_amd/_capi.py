@@ -28,13 +28,14 @@ DTYPE_F32 = 0
 DTYPE_BF16 = 1
 SCALES_F32 = 0
 SCALES_UE8M0_PACKED = 1
-GEMM_PATHS = {"auto": 0, "valu_splitk": 1, "mfma_splitk": 2, "mfma": 3}
+WEIGHT_FORMATS = {"fp8": 0, "nvfp4": 1}
+GEMM_PATHS = {"auto": 0, "valu_splitk": 1, "mfma_splitk": 2, "mfma": 3, "fp4": 4}
 
 STAGES = {
     "ctrl": 0, "uexp": 1, "uoff": 2, "ucnt": 3, "routes": 4, "x_q": 5, "x_s": 6,
     "part1": 7, "h_q": 8, "h_s": 9, "part2": 10,
     "shared_x_q": 11, "shared_x_s": 12, "shared_part1": 13, "shared_h_q": 14,
-    "shared_h_s": 15, "shared_part2": 16,
+    "shared_h_s": 15, "shared_part2": 16, "x_f16": 17, "h_f16": 18,
 }
 TIMING_SLOTS = ("route_quant", "gemm1", "swiglu_requant", "gemm2", "combine")
 
@@ -65,6 +66,9 @@ class MoeDecodeConfig(ctypes.Structure):
         ("gemm_path", ctypes.c_int32),
         ("splits1", ctypes.c_int32),
         ("splits2", ctypes.c_int32),
+        ("weight_format", ctypes.c_int32),
+        ("local_begin", ctypes.c_int32),
+        ("local_experts", ctypes.c_int32),
     ]
 
 
@@ -113,6 +117,8 @@ def lib() -> ctypes.CDLL:
     L.moe_decode_last_timing.restype = ctypes.c_int
     L.moe_decode_debug_codec.argtypes = [vp, vp, vp, i32, vp]
     L.moe_decode_debug_codec.restype = ctypes.c_int
+    L.moe_decode_debug_codec_fp4.argtypes = [vp, vp, vp, i32, vp]
+    L.moe_decode_debug_codec_fp4.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -153,19 +159,32 @@ class MoeDecode:
     Optional shared expert: sw13 [2Is, H] (gate rows, then up rows) and
     sw2 [H, Is] e4m3, with FP32 block scales [2Is/128, H/128] / [H/128, Is/128]
     or packed UE8M0 int32 scales [2Is, ceil(H/512)] / [H, ceil(Is/512)].
+
+    weight_format "nvfp4": w13 [El, 2I, H/2] and w2 [El, H, I/2] packed E2M1
+    (uint8, low nibble first; gate rows first), w13_scale [El, 2I, H/16] and
+    w2_scale [El, H, I/16] UE4M3 bytes (uint8 or float8_e4m3fn). With
+    local_experts > 0 only experts [local_begin, local_begin + local_experts)
+    of `experts` (routing) are computed and the weights cover those alone.
     """
 
     def __init__(self, w13, w13_scale, w2, w2_scale, *, top_k: int, limit: float,
                  routed_scale: float, max_tokens: int, logits_dtype=torch.float32,
                  ue8m0_act: bool = False, gemm_path: str = "auto", splits1: int = 0,
                  splits2: int = 0, sw13=None, sw13_scale=None, sw2=None, sw2_scale=None,
-                 shared_limit: Optional[float] = None, shared_ue8m0_act: bool = True):
+                 shared_limit: Optional[float] = None, shared_ue8m0_act: bool = True,
+                 weight_format: str = "fp8", experts: Optional[int] = None, local_begin: int = 0):
         self.device = w13.device
-        for t, n, d in ((w13, "w13", _FP8), (w2, "w2", _FP8), (w13_scale, "w13_scale", (torch.float32,)),
-                        (w2_scale, "w2_scale", (torch.float32,))):
+        fp4 = weight_format == "nvfp4"
+        sdt = _FP8 if fp4 else (torch.float32,)
+        for t, n, d in ((w13, "w13", _FP8), (w2, "w2", _FP8), (w13_scale, "w13_scale", sdt),
+                        (w2_scale, "w2_scale", sdt)):
             _need(t, n, d, self.device)
-        E, N1, H = w13.shape
+        El, N1, H = w13.shape
+        if fp4:
+            H *= 2
+        E = El if experts is None else experts
         self.experts, self.hidden, self.inter, self.top_k = E, H, N1 // 2, top_k
+        self.local_begin, self.local_experts = local_begin, El
         self.max_tokens = max_tokens
         self.logits_dtype = logits_dtype
         self._keep = (w13, w13_scale, w2, w2_scale)
@@ -178,6 +197,9 @@ class MoeDecode:
         cfg.w13, cfg.w13_scale, cfg.w2, cfg.w2_scale = (t.data_ptr() for t in self._keep)
         cfg.gemm_path = GEMM_PATHS[gemm_path]
         cfg.splits1, cfg.splits2 = splits1, splits2
+        cfg.weight_format = WEIGHT_FORMATS[weight_format]
+        cfg.local_begin = local_begin
+        cfg.local_experts = 0 if El == E else El
         self.shared_inter = 0
         if sw13 is not None:
             _need(sw13, "sw13", _FP8, self.device)
@@ -245,6 +267,9 @@ class MoeDecode:
         return out + (shared,) if shared is not None else out
 
     # -- introspection ------------------------------------------------------
+    def is_local(self, ids: torch.Tensor) -> torch.Tensor:
+        return (ids >= self.local_begin) & (ids < self.local_begin + self.local_experts)
+
     def plan(self, M: int) -> dict:
         buf = (ctypes.c_int32 * 17)()
         rc = lib().moe_decode_plan(self._h, M, buf, 17)
@@ -287,6 +312,18 @@ class MoeDecode:
             self.close()
         except Exception:
             pass
+
+
+def debug_codec_fp4(values: torch.Tensor):
+    """(codes, decoded) from the library's device E2M1 encoder and its FP4
+    reader (decoded[i] is code i & 15 read from nibble position (i >> 4) & 7)."""
+    n = values.numel()
+    q = torch.empty(n, dtype=torch.uint8, device=values.device)
+    dq = torch.empty(n, dtype=torch.float32, device=values.device)
+    rc = lib().moe_decode_debug_codec_fp4(values.data_ptr(), q.data_ptr(), dq.data_ptr(), n, _stream(None))
+    if rc != OK:
+        raise MoeDecodeError(rc, "moe_decode_debug_codec_fp4")
+    return q, dq
 
 
 def debug_codec(values: torch.Tensor):

@@ -17,7 +17,7 @@ using namespace moe;
 namespace {
 
 constexpr int kEvents = 8;
-constexpr int kRegions = 17;
+constexpr int kRegions = 19;
 constexpr int kStages = 5;  // timing slots: route, GEMM1, SwiGLU, GEMM2, combine
 constexpr int kTargetUnits = 4096;  // work units per GEMM launch to aim for (16 per CU)
 constexpr int kDenseTargetUnits = 256;  // units of the shared expert per GEMM launch
@@ -29,6 +29,7 @@ constexpr int kBadFlagWord = 32;        // word of the control region used by cr
 enum {
   kCtrl, kUexp, kUoff, kUcnt, kRoutes, kXq, kXs, kP1, kHq, kHs, kP2,
   kSXq, kSXs, kSP1, kSHq, kSHs, kSP2,
+  kXd, kHd,  // FP4 form: dequantised F16 activations of GEMM1 and GEMM2
 };
 
 struct Plan {
@@ -42,6 +43,7 @@ struct Plan {
   int ss1, sks1, ss2, sks2, stpw1, stpw2, sunits1, sunits2;
   // K-in-workgroup path: K parts per row group (routed, shared)
   int kp1, kp2, skp1, skp2;
+  int rpp1, rpp2;  // FP4 kernel: routes per pass
 };
 
 struct Region {
@@ -129,10 +131,27 @@ int choose_kparts(int experts, int N, int nkb, int forced) {
   return kp;
 }
 
+int local_count(const moe_decode_config& c) { return c.local_experts ? c.local_experts : c.experts; }
+
 Plan make_plan(const moe_decode_config& c, int M) {
   Plan p{};
   const int R = M * c.top_k;
-  p.umax = std::min(c.experts, R);
+  p.umax = std::min(local_count(c), R);
+  if (c.weight_format == MOE_WEIGHTS_NVFP4) {
+    p.path = MOE_GEMM_FP4;
+    p.s1 = p.s2 = 1;
+    p.kp1 = choose_kparts(p.umax, 2 * c.inter, c.hidden / kTile, c.splits1);
+    p.kp2 = choose_kparts(p.umax, c.hidden, c.inter / kTile, c.splits2);
+    p.ks1 = ceil_div(c.hidden / kTile, p.kp1);
+    p.ks2 = ceil_div(c.inter / kTile, p.kp2);
+    p.tpw1 = kRowsPerWg / p.kp1;
+    p.tpw2 = kRowsPerWg / p.kp2;
+    p.grid1 = p.umax * (2 * c.inter / p.tpw1);
+    p.grid2 = p.umax * (c.hidden / p.tpw2);
+    p.rpp1 = gemm_fp4_routes_per_pass(c.hidden);
+    p.rpp2 = gemm_fp4_routes_per_pass(c.inter);
+    return p;
+  }
   const int tiles1 = 2 * c.inter / kRowsPerWg, tiles2 = c.hidden / kRowsPerWg;
   if (c.gemm_path == MOE_GEMM_AUTO || c.gemm_path == MOE_GEMM_MFMA) {
     // K summed inside the workgroup: no split-K partials leave the chip
@@ -207,6 +226,18 @@ int validate_config(const moe_decode_config* c) {
   if (c->logits_dtype != MOE_DTYPE_F32 && c->logits_dtype != MOE_DTYPE_BF16)
     return MOE_DECODE_ERR_UNSUPPORTED;
   if (c->gemm_path < MOE_GEMM_AUTO || c->gemm_path > MOE_GEMM_MFMA) return MOE_DECODE_ERR_UNSUPPORTED;
+  if (c->local_begin < 0 || c->local_experts < 0 || c->local_begin + local_count(*c) > c->experts)
+    return MOE_DECODE_ERR_INVALID_ARG;
+  if (c->weight_format != MOE_WEIGHTS_FP8 && c->weight_format != MOE_WEIGHTS_NVFP4)
+    return MOE_DECODE_ERR_UNSUPPORTED;
+  if (c->weight_format == MOE_WEIGHTS_NVFP4) {
+    const int step = 2 * kTile;  // the FP4 kernel's 256-value steps
+    if (c->hidden % step || c->inter % step || c->shared_inter != 0 || c->ue8m0_act ||
+        c->gemm_path != MOE_GEMM_AUTO)
+      return MOE_DECODE_ERR_UNSUPPORTED;
+    for (int K : {c->hidden, c->inter})
+      if (gemm_fp4_lds_bytes(K, gemm_fp4_routes_per_pass(K)) > kMaxWgLds) return MOE_DECODE_ERR_UNSUPPORTED;
+  }
   if (gemm_wg_lds_bytes(std::max(c->hidden, std::max(c->inter, c->shared_inter)) / kTile) > kMaxWgLds)
     return MOE_DECODE_ERR_UNSUPPORTED;
   if (c->splits1 < 0 || c->splits2 < 0) return MOE_DECODE_ERR_INVALID_ARG;
@@ -285,7 +316,8 @@ int moe_decode_create(const moe_decode_config* cfg, moe_decode_t* out) {
 
   // Workspace sized for every M up to max_tokens.
   const size_t Rcap = (size_t)c.max_tokens * c.top_k;
-  const size_t Ucap = std::min<size_t>(c.experts, Rcap);
+  const size_t Ucap = std::min<size_t>(local_count(c), Rcap);
+  const bool fp4 = c.weight_format == MOE_WEIGHTS_NVFP4;
   size_t p1 = 0, p2 = 0, sp1 = 0, sp2 = 0;
   for (int M = 1; M <= c.max_tokens; ++M) {
     const Plan p = make_plan(c, M);
@@ -303,11 +335,11 @@ int moe_decode_create(const moe_decode_config* cfg, moe_decode_t* out) {
       Ucap * sizeof(int32_t),         // uoff
       Ucap * sizeof(int32_t),         // ucnt
       Rcap * sizeof(int32_t),         // routes
-      T * H,                          // x_q
-      T * (H / kTile) * sizeof(float),  // x_s
+      T * H,                          // x_q (FP4: packed, half of it)
+      fp4 ? T * (H / 16) : T * (H / kTile) * sizeof(float),  // x_s (FP4: UE4M3 bytes per 16)
       p1 * sizeof(float),             // GEMM1 partials
       Rcap * I,                       // h_q
-      Rcap * (I / kTile) * sizeof(float),  // h_s
+      fp4 ? Rcap * (I / 16) : Rcap * (I / kTile) * sizeof(float),  // h_s
       p2 * sizeof(float),             // GEMM2 partials
       own_quant ? T * H : 0,          // shared x_q
       own_quant ? T * (H / kTile) * sizeof(float) : 0,  // shared x_s
@@ -315,6 +347,8 @@ int moe_decode_create(const moe_decode_config* cfg, moe_decode_t* out) {
       T * Is,                         // shared h_q
       T * (Is / kTile) * sizeof(float),  // shared h_s
       sp2 * sizeof(float),            // shared down partials
+      fp4 ? T * H * 2 : 0,            // dequantised x, F16
+      fp4 ? Rcap * I * 2 : 0,         // dequantised hidden, F16
   };
   moe_decode_handle* h = new (std::nothrow) moe_decode_handle();
   if (!h) return MOE_DECODE_ERR_OUT_OF_MEMORY;
@@ -430,6 +464,8 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Plan p = make_plan(c, M);
   const int R = M * c.top_k;
+  const bool fp4 = c.weight_format == MOE_WEIGHTS_NVFP4;
+  const int lb = c.local_begin, lc = local_count(c);
   unsigned char* ws = h->ws;
   auto at = [&](int i) { return ws + h->reg[i].off; };
 
@@ -478,6 +514,11 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   ra.xq2 = shared && h->shared_own_quant ? sxq : nullptr;
   ra.xs2 = sxs;
   ra.ue8m0_2 = c.shared_ue8m0_act;
+  ra.fp4 = fp4;
+  ra.xs4 = at(kXs);
+  ra.xd = reinterpret_cast<_Float16*>(at(kXd));
+  ra.lb = lb;
+  ra.lc = lc;
   ra.b = b;
   if (e == hipSuccess) e = launch_route_quant(ra, s);
   if (e == hipSuccess) e = mark(0);
@@ -498,6 +539,12 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   sa.sue8m0 = c.shared_ue8m0_act;
   sa.shq = at(kSHq);
   sa.shs = atf(kSHs);
+  sa.fp4 = fp4;
+  sa.hs4 = at(kHs);
+  sa.hd = reinterpret_cast<_Float16*>(at(kHd));
+  sa.ids = ids;
+  sa.lb = lb;
+  sa.lc = lc;
 
   CombineArgs ca;
   ca.part = p2;
@@ -511,13 +558,17 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   ca.spart = shared ? atf(kSP2) : nullptr;
   ca.ssplits = p.ss2;
   ca.shared_out = static_cast<uint16_t*>(shared_out);
+  ca.ids = ids;
+  ca.lb = lb;
+  ca.lc = lc;
 
   // problem descriptor of N x K weights and their activations
-  auto problem = [](const void* w, const float* ws, const uint8_t* aq, const float* as, float* part, int N,
+  auto problem = [](const void* w, const void* ws, const uint8_t* aq, const float* as, float* part, int N,
                     int K, int splits, int ks, int R, int act_div, int tpw) {
     GemmProblem q{};
     q.w = static_cast<const uint8_t*>(w);
-    q.ws = ws;
+    q.ws = static_cast<const float*>(ws);
+    q.ws8 = static_cast<const uint8_t*>(ws);
     q.aq = aq;
     q.as = as;
     q.part = part;
@@ -534,6 +585,7 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   };
   auto launch_gemm = [&](const GemmArgs& g, int role, int grid) {
     switch (p.path) {
+      case MOE_GEMM_FP4: return launch_gemm_fp4(g, role, grid, s);
       case MOE_GEMM_MFMA: return launch_gemm_wg(g, role, grid, s);
       case MOE_GEMM_MFMA_SPLITK: return launch_gemm_mfma(g, role, grid, s);
       default: return launch_gemm_valu(g, role, grid, s);
@@ -544,7 +596,8 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   g1.p[1] = problem(c.w13, c.w13_scale, xq, xs, p1, 2 * c.inter, c.hidden, p.s1, p.ks1, R, c.top_k, p.tpw1);
   g1.p[1].b = b;
   g1.p[1].kparts = p.kp1;
-  g1.pass_routes = p.pass_routes;
+  g1.p[1].ad = reinterpret_cast<const _Float16*>(at(kXd));
+  g1.pass_routes = fp4 ? p.rpp1 : p.pass_routes;
   if (shared) {
     g1.p[0] = problem(c.sw13, h->s13, sxq, sxs, atf(kSP1), 2 * c.shared_inter, c.hidden, p.ss1, p.sks1, M, 1,
                       p.stpw1);
@@ -562,7 +615,8 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   g2.p[1] = problem(c.w2, c.w2_scale, hq, hs, p2, c.hidden, c.inter, p.s2, p.ks2, R, 1, p.tpw2);
   g2.p[1].b = b;
   g2.p[1].kparts = p.kp2;
-  g2.pass_routes = p.pass_routes;
+  g2.p[1].ad = reinterpret_cast<const _Float16*>(at(kHd));
+  g2.pass_routes = fp4 ? p.rpp2 : p.pass_routes;
   if (shared) {
     g2.p[0] = problem(c.sw2, h->s2, at(kSHq), atf(kSHs), atf(kSP2), c.hidden, c.shared_inter, p.ss2, p.sks2,
                       M, 1, p.stpw2);
@@ -583,7 +637,8 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
 
 int moe_decode_debug_stage(moe_decode_t h, int32_t stage, void* dst, size_t bytes, void* stream) {
   if (!h || !dst || stage < 0 || stage >= kRegions) return MOE_DECODE_ERR_INVALID_ARG;
-  if (stage >= kSXq && h->cfg.shared_inter == 0) return MOE_DECODE_ERR_INVALID_ARG;
+  if (stage >= kSXq && stage <= kSP2 && h->cfg.shared_inter == 0) return MOE_DECODE_ERR_INVALID_ARG;
+  if (stage >= kXd && h->cfg.weight_format != MOE_WEIGHTS_NVFP4) return MOE_DECODE_ERR_INVALID_ARG;
   if (!h->shared_own_quant && (stage == kSXq || stage == kSXs)) stage = stage == kSXq ? kXq : kXs;
   const Region& r = h->reg[stage];
   const size_t n = std::min(bytes, r.bytes);
@@ -610,6 +665,14 @@ int moe_decode_last_timing(moe_decode_t h, float* ms, int32_t n) {
     ms[h->ev_stage[i]] += t;
   }
   return MOE_DECODE_OK;
+}
+
+int moe_decode_debug_codec_fp4(const float* in, uint8_t* q, float* dq, int32_t n, void* stream) {
+  if (!in || !q || !dq || n < 0) return MOE_DECODE_ERR_INVALID_ARG;
+  if (n == 0) return MOE_DECODE_OK;
+  return launch_codec_check_fp4(in, q, dq, n, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MOE_DECODE_OK
+             : MOE_DECODE_ERR_HIP;
 }
 
 int moe_decode_debug_codec(const float* in, uint8_t* q, float* dq, int32_t n, void* stream) {

@@ -4,6 +4,7 @@
 
 #include "kernels.h"
 #include "device_common.h"
+#include "fp4_device.h"
 
 namespace moe {
 
@@ -89,21 +90,56 @@ __device__ __forceinline__ void swiglu_shared_block(const SwigluArgs& a, int t, 
   if (lane == 0) a.shs[(size_t)t * nblk + c] = s;
 }
 
+// One wave, FP4 form (nvfp4-megamoe-kernel README: SiLU times up per slot,
+// then the activation staged to E2M1 for L2): route r, columns
+// [128c, 128c + 128) of the hidden, two per lane. gate/up are GEMM1's FP32
+// sums rounded to BF16 (gate rows first); gate = min(gate, L), up = clamp(up,
+// -L, L); act = BF16(gate / (1 + exp(-gate)) * up) in FP32 steps with the exp
+// correctly rounded; then per 16 values (eight lanes) the E2M1 codes, the
+// UE4M3 scale and the dequantised F16 values.
+__device__ __forceinline__ void swiglu_fp4_block(const SwigluArgs& a, int r, int c, int lane) {
+  const int j = c * kTile + 2 * lane;
+  const float* p = a.part + (size_t)r * 2 * a.I;
+  const float2 g = *reinterpret_cast<const float2*>(p + j);
+  const float2 u = *reinterpret_cast<const float2*>(p + a.I + j);
+  const float L = a.limit;
+  const float g0 = fminf(bf16_round(g.x), L), g1 = fminf(bf16_round(g.y), L);
+  const float u0 = fminf(fmaxf(bf16_round(u.x), -L), L), u1 = fminf(fmaxf(bf16_round(u.y), -L), L);
+  const float e0 = (float)exp(-(double)g0), e1 = (float)exp(-(double)g1);
+  const float act0 = bf16_round((g0 / (1.f + e0)) * u0);
+  const float act1 = bf16_round((g1 / (1.f + e1)) * u1);
+  const float amax = group_max<8>(fmaxf(fabsf(act0), fabsf(act1)));
+  const uint32_t sbyte = e4m3x2_encode(amax / kE2m1Max, 0.f) & 0xFFu;
+  const float s = e4m3_value(sbyte);
+  const uint32_t q0 = s > 0.f ? e2m1_encode(act0 / s) : 0u;
+  const uint32_t q1 = s > 0.f ? e2m1_encode(act1 / s) : 0u;
+  a.hq[((size_t)r * a.I + j) / 2] = (uint8_t)(q0 | (q1 << 4));
+  if ((lane & 7) == 0) a.hs4[((size_t)r * a.I + j) / kFp4Group] = (uint8_t)sbyte;
+  *reinterpret_cast<half2_t*>(a.hd + (size_t)r * a.I + j) =
+      half2_t{(_Float16)(e2m1_value(q0) * s), (_Float16)(e2m1_value(q1) * s)};
+}
+
 // The whole workgroup (256 threads): token t, hidden columns
 // [col0, col0 + 64). Each slot value is the fixed-order sum of GEMM2's split
 // partials rounded once to BF16; combined = BF16(sum_j w[t, j] * slot_j) with
 // the FP32 sum in pick order -- the routing weights applied once, at the end
-// (nvfp4-megamoe-kernel README, slot representation). `lds` holds k * 64
-// floats. Contains a barrier: every thread of the workgroup must call it.
+// (nvfp4-megamoe-kernel README, slot representation). Slots whose expert is
+// not local are zero and add nothing. With a shared expert, the otherwise
+// idle second wave writes its BF16 output for the same columns. `lds` holds
+// k * 64 floats. Contains a barrier: every thread of the workgroup must call
+// it.
 __device__ __forceinline__ void combine_token_tile(const CombineArgs& a, int t, int col0, float* lds) {
   const int tid = threadIdx.x;
   const int c = tid & 63, jg = tid >> 6;
   const int R = a.M * a.k;
   for (int j = jg; j < a.k; j += 4) {
     const int r = t * a.k + j;
-    float v = 0.f;
+    const int e = a.ids[r] - a.lb;
+    float v = 0.f;  // non-local experts: a zero slot, nothing added below
+    if (e >= 0 && e < a.lc) {
 #pragma unroll 4
-    for (int s = 0; s < a.splits; ++s) v += a.part[((size_t)s * R + r) * a.H + col0 + c];
+      for (int s = 0; s < a.splits; ++s) v += a.part[((size_t)s * R + r) * a.H + col0 + c];
+    }
     const uint32_t b = bf16_bits(v);
     a.slots[(size_t)r * a.H + col0 + c] = (uint16_t)b;
     lds[j * 64 + c] = bf16_value(b);

@@ -16,7 +16,13 @@ __global__ __launch_bounds__(kThreads) void swiglu_requant_kernel(SwigluArgs a) 
   const int lane = threadIdx.x & (kWave - 1);
   const int routed = a.R * nblk;
   if (gw < routed) {
-    swiglu_route_block(a, gw / nblk, gw % nblk, lane);
+    const int r = gw / nblk;
+    const int e = a.ids[r] - a.lb;
+    if (e < 0 || e >= a.lc) return;  // a route of another GPU's expert: nothing to compute
+    if (a.fp4)
+      swiglu_fp4_block(a, r, gw % nblk, lane);
+    else
+      swiglu_route_block(a, r, gw % nblk, lane);
     return;
   }
   if (!a.spart) return;

@@ -35,6 +35,12 @@ struct RouteQuantArgs {
   uint8_t* xq2;         // second quantisation of x (shared expert), or nullptr
   float* xs2;
   int ue8m0_2;
+  // FP4 staging instead of FP8 (fp4 != 0): packed E2M1 [M, H/2] in xq,
+  // UE4M3 bytes [M, H/16] in xs4, and the exactly dequantised x [M, H] F16.
+  int fp4;
+  uint8_t* xs4;
+  _Float16* xd;
+  int lb, lc;           // local experts [lb, lb + lc): only their routes are bucketed
   Buckets b;
 };
 
@@ -52,6 +58,14 @@ struct SwigluArgs {
   int sue8m0;
   uint8_t* shq;         // [M, Is]
   float* shs;           // [M, Is/128]
+  // FP4 form (fp4 != 0): gate rows first, BF16 rounding of the GEMM output
+  // and of the activation, E2M1 staging per 16 into hq (packed [R, I/2]),
+  // hs4 ([R, I/16] UE4M3 bytes) and hd ([R, I] F16, dequantised).
+  int fp4;
+  uint8_t* hs4;
+  _Float16* hd;
+  const int32_t* ids;   // [M, k]: routes of non-local experts are skipped
+  int lb, lc;
 };
 
 struct CombineArgs {
@@ -63,6 +77,8 @@ struct CombineArgs {
   const float* spart;   // shared expert's down partials [ssplits, M, H], or nullptr
   int ssplits;
   uint16_t* shared_out; // [M, H] bf16
+  const int32_t* ids;   // [M, k]: slots of non-local experts are zero
+  int lb, lc;
 };
 
 // One block-scaled GEMM problem: for every route r of distinct expert u and
@@ -73,8 +89,10 @@ struct CombineArgs {
 // from the buckets; a dense one (the shared expert) is expert 0 with routes
 // 0..dense-1, one per token.
 struct GemmProblem {
-  const uint8_t* w;     // [E, N, K] e4m3
+  const uint8_t* w;     // [E, N, K] e4m3 (FP4 kernel: [E, N, K/2] packed E2M1)
   const float* ws;      // [E, N/128, K/128]
+  const uint8_t* ws8;   // FP4 kernel: [E, N, K/16] UE4M3 bytes
+  const _Float16* ad;   // FP4 kernel: dequantised activations [rows, K] F16
   const uint8_t* aq;    // [rows, K] e4m3
   const float* as;      // [rows, K/128]
   float* part;          // [splits, R, N]
@@ -96,6 +114,13 @@ struct GemmArgs {
   int units0;           // work units of p[0]; 0 when there is none
   int pass_routes;      // MFMA path: routes staged per pass (<= 16)
 };
+
+// FP4 GEMM (K summed inside the workgroup, VALU, activations staged in LDS
+// as F16): routes per pass that fit the LDS budget for K.
+int gemm_fp4_routes_per_pass(int K);
+size_t gemm_fp4_lds_bytes(int K, int routes);
+hipError_t launch_gemm_fp4(const GemmArgs& a, int role, int grid, hipStream_t s);
+hipError_t launch_codec_check_fp4(const float* in, uint8_t* q, float* dq, int n, hipStream_t s);
 
 // Work units of a problem per expert: (tiles / tpw) tile groups x splits.
 inline int gemm_units_per_expert(const GemmProblem& p) { return (p.tiles / p.tpw) * p.splits; }

@@ -16,6 +16,7 @@
 // (atomic counter, reset by that workgroup) does it.
 #include "kernels.h"
 #include "device_common.h"
+#include "fp4_device.h"
 
 namespace moe {
 namespace {
@@ -168,12 +169,25 @@ __device__ void quant_tokens(const RouteQuantArgs& a, int t0, int ntok) {
           v[8 + 2 * i] = bf16_value(hi[q][i] & 0xFFFFu);
           v[8 + 2 * i + 1] = bf16_value(hi[q][i] >> 16);
         }
+        const int t = t0 + item / nblk, blk = item % nblk;
+        const size_t at = (size_t)t * a.H + (size_t)blk * kTile + sub * 16;
+        if (a.fp4) {  // this lane's 16 values are one FP4 group
+          uint32_t packed[2];
+          float dq[16];
+          const uint32_t sbyte = stage_fp4_group(v, packed, dq);
+          *reinterpret_cast<uint2*>(a.xq + at / 2) = make_uint2(packed[0], packed[1]);
+          a.xs4[at / kFp4Group] = (uint8_t)sbyte;
+          half2_t h[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) h[i] = half2_t{(_Float16)dq[2 * i], (_Float16)dq[2 * i + 1]};
+          *reinterpret_cast<u32x4_t*>(a.xd + at) = *reinterpret_cast<const u32x4_t*>(&h[0]);
+          *reinterpret_cast<u32x4_t*>(a.xd + at + 8) = *reinterpret_cast<const u32x4_t*>(&h[4]);
+          continue;
+        }
         float amax = kAmaxFloor;
 #pragma unroll
         for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
         amax = group_max<8>(amax);
-        const int t = t0 + item / nblk, blk = item % nblk;
-        const size_t at = (size_t)t * a.H + (size_t)blk * kTile + sub * 16;
         // scale = amax / 448, optionally rounded up to a power of two; codes
         // = e4m3(v * (1 / scale))
         auto emit = [&](int ue8m0, uint8_t* xq, float* xs) {
@@ -215,17 +229,19 @@ __device__ __forceinline__ Lds carve(unsigned char* lds, int E, int W, int R) {
   return l;
 }
 
-// Routes grouped by expert, experts ascending, each expert's routes in
-// ascending token order (so ascending route index).
+// Routes of the local experts grouped by expert (local index e - lb),
+// experts ascending, each expert's routes in ascending token order (so
+// ascending route index).
 __device__ void bucket_routes(const RouteQuantArgs& a, const Lds& l) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int E = a.E, W = a.words, R = a.M * a.k;
+  const int E = a.lc, W = a.words, R = a.M * a.k;
   for (int i = tid; i < E * W; i += kThreads) l.mask[i] = 0;
   __syncthreads();
   for (int r = tid; r < R; r += kThreads) {
     const int t = r / a.k;
-    atomicOr(reinterpret_cast<unsigned long long*>(&l.mask[(size_t)l.ids[r] * W + t / 64]),
-             1ull << (t % 64));
+    const int e = l.ids[r] - a.lb;
+    if (e >= 0 && e < E)
+      atomicOr(reinterpret_cast<unsigned long long*>(&l.mask[(size_t)e * W + t / 64]), 1ull << (t % 64));
   }
   __syncthreads();
   // thread e owns expert e (E <= 1024); block-wide exclusive scan of
@@ -269,7 +285,8 @@ __device__ void bucket_routes(const RouteQuantArgs& a, const Lds& l) {
   if (tid == 0) a.b.ctrl[1] = all_p;
   __syncthreads();
   for (int r = tid; r < R; r += kThreads) {
-    const int e = l.ids[r];
+    const int e = l.ids[r] - a.lb;
+    if (e < 0 || e >= E) continue;
     const int t = r / a.k;
     const uint64_t* m = l.mask + (size_t)e * W;
     int before = 0;
@@ -280,12 +297,15 @@ __device__ void bucket_routes(const RouteQuantArgs& a, const Lds& l) {
 }
 
 // The same grouping by one wave when there are at most 64 routes: lane r
-// holds (expert << 16) | r, a bitonic network over the wave sorts the keys
-// (experts ascending, routes ascending within an expert), and the first lane
-// of each expert's run writes its bucket. No LDS, no barrier.
+// holds (local expert << 16) | r (non-local routes sort last as padding), a
+// bitonic network over the wave sorts the keys (experts ascending, routes
+// ascending within an expert), and the first lane of each expert's run
+// writes its bucket. No LDS, no barrier.
 __device__ void bucket_routes_wave(const RouteQuantArgs& a, const int* ids, int lane) {
-  const int R = a.M * a.k;
-  uint32_t v = lane < R ? ((uint32_t)ids[lane] << 16) | (uint32_t)lane : 0xFFFFFFFFu;
+  const int e_own = lane < a.M * a.k ? ids[lane] - a.lb : -1;
+  const bool mine = e_own >= 0 && e_own < a.lc;
+  const int R = __popcll(__ballot(mine));  // local routes
+  uint32_t v = mine ? ((uint32_t)e_own << 16) | (uint32_t)lane : 0xFFFFFFFFu;
 #pragma unroll
   for (int k = 2; k <= kWave; k <<= 1) {
 #pragma unroll

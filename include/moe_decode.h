@@ -61,6 +61,10 @@ extern "C" {
 #define MOE_DTYPE_F32 0
 #define MOE_DTYPE_BF16 1
 
+/* Routed weight formats. */
+#define MOE_WEIGHTS_FP8 0   /* OCP e4m3, FP32 128x128 block scales */
+#define MOE_WEIGHTS_NVFP4 1 /* packed E2M1 (two per byte, low nibble first), a UE4M3 byte per 16 values along K */
+
 #define MOE_SCALES_F32 0         /* FP32 [n/128, k/128] block scales */
 #define MOE_SCALES_UE8M0_PACKED 1 /* int32 [n, ceil(k/512)]: byte g%4 of word g/4 = biased exponent of K group g */
 
@@ -71,6 +75,7 @@ extern "C" {
 #define MOE_GEMM_VALU_SPLITK 1  /* F16 dot2, split-K over workgroups */
 #define MOE_GEMM_MFMA_SPLITK 2  /* v_mfma_f32_16x16x32_f16 (16 routes at once), split-K over workgroups */
 #define MOE_GEMM_MFMA 3         /* v_mfma_f32_16x16x32_f16, K split among the waves of a workgroup */
+#define MOE_GEMM_FP4 4          /* the MOE_WEIGHTS_NVFP4 kernel (reported by moe_decode_plan; gemm_path stays AUTO) */
 
 /* Limits of this implementation. */
 #define MOE_DECODE_MAX_EXPERTS 1024
@@ -93,15 +98,25 @@ typedef struct moe_decode_config {
   float limit;          /* SwiGLU clamp L > 0 */
   float routed_scale;   /* multiplies the renormalised routing weights */
 
-  /* Routed expert weights (borrowed: they must outlive the handle).
-   * w13       [E, 2I, H] e4m3, rows 0..I-1 "up", rows I..2I-1 "gate"
-   * w13_scale [E, 2I/128, H/128] FP32, any positive values
-   * w2        [E, H, I] e4m3
-   * w2_scale  [E, H/128, I/128] FP32 */
+  /* Routed expert weights (borrowed: they must outlive the handle), for the
+   * El local experts (see local_begin below; El = experts when all are local).
+   * MOE_WEIGHTS_FP8:
+   *   w13       [El, 2I, H] e4m3, rows 0..I-1 "up", rows I..2I-1 "gate"
+   *   w13_scale [El, 2I/128, H/128] FP32, any positive values
+   *   w2        [El, H, I] e4m3
+   *   w2_scale  [El, H/128, I/128] FP32
+   * MOE_WEIGHTS_NVFP4 (nvfp4-megamoe-kernel README, "Data Formats"):
+   *   w13       [El, 2I, H/2] packed E2M1, rows 0..I-1 "gate", I..2I-1 "up"
+   *   w13_scale [El, 2I, H/16] UE4M3 bytes (e4m3 with the sign clear)
+   *   w2        [El, H, I/2] packed E2M1
+   *   w2_scale  [El, H, I/16] UE4M3 bytes
+   *   H and I multiples of 256; activations are staged to E2M1 with a UE4M3
+   *   scale of block_max / 6 per 16 values; GEMM outputs are rounded to BF16;
+   *   no shared expert; ue8m0_act must be 0. */
   const void* w13;
-  const float* w13_scale;
+  const void* w13_scale;
   const void* w2;
-  const float* w2_scale;
+  const void* w2_scale;
 
   /* Optional dense shared expert ("shared_expert" page); all zero/NULL when
    * absent. shared_inter (Is) is a multiple of 128. Its units run inside the
@@ -128,6 +143,15 @@ typedef struct moe_decode_config {
   int32_t gemm_path;
   int32_t splits1;
   int32_t splits2;
+
+  /* Weight format (MOE_WEIGHTS_*), and the local experts: routing runs over
+   * all `experts`, but only routes whose expert lies in
+   * [local_begin, local_begin + local_experts) are computed (one GPU's share
+   * under expert parallelism); the slot rows of the others are zero and they
+   * add nothing to `combined`. local_experts = 0 means all experts. */
+  int32_t weight_format;
+  int32_t local_begin;
+  int32_t local_experts;
 } moe_decode_config;
 
 typedef struct moe_decode_handle* moe_decode_t;
@@ -214,6 +238,12 @@ int moe_decode_last_timing(moe_decode_t h, float* ms, int32_t n);
  * value the GEMM inner products read for code (i & 255) through the path's
  * FP8 -> F16 conversion. in, q and dq are device buffers of n elements. */
 int moe_decode_debug_codec(const float* in, uint8_t* q, float* dq, int32_t n, void* stream);
+
+/* The same for E2M1: q[i] = the library's E2M1 code of in[i] (nearest, ties
+ * to even, saturating at +-6), and dq[i] = the value the FP4 GEMM reads for
+ * code (i & 15) through its FP4 -> F16 widening (with the code placed in
+ * each nibble and byte position of a word in turn). */
+int moe_decode_debug_codec_fp4(const float* in, uint8_t* q, float* dq, int32_t n, void* stream);
 
 #ifdef __cplusplus
 }

@@ -13,7 +13,8 @@ docstring), and the latent MoE with 896 experts and top-16 routing at latent
 width 3584 (vLLM `kimi_k3 ... ep.comm` page, module docstring).
 
 Draw order (host, numpy PCG64 seeded with `seed`): logits, bias, x, then all
-FP32 block scales. Weights are drawn expert by expert with
+FP32 block scales (the FP4 share draws its scales on the device with its
+weights; see `_make_inputs_fp4`). Weights are drawn expert by expert with
 `torch.Generator(device).manual_seed(seed * 1000 + e)` as `randn / scale`
 and cast to OCP e4m3 with torch's own cast (ties to even); a weight that
 would overflow the cast is impossible at these scales (|randn| would need to
@@ -29,6 +30,7 @@ import numpy as np
 import torch
 
 TILE = 128
+GROUP4 = 16  # FP4 values per UE4M3 scale
 
 
 @dataclasses.dataclass(frozen=True)
@@ -64,6 +66,12 @@ class MoeShape:
     # with power-of-two block scales); 0 means absent.
     shared_inter: int = 0
     shared_limit: float = 7.0
+    # "fp8": e4m3 weights, FP32 128x128 scales. "fp4": packed E2M1 weights
+    # with a UE4M3 byte per 16 values along K (gate rows first), for the
+    # local experts [local_begin, local_begin + local_count) of `experts`.
+    weight_format: str = "fp8"
+    local_begin: int = 0
+    local_count: int = 0
 
     def with_(self, **kw) -> "MoeShape":
         return dataclasses.replace(self, **kw)
@@ -73,11 +81,17 @@ class MoeShape:
         return self.M * self.top_k
 
     def expert_bytes(self) -> int:
-        """FP8 weight bytes plus FP32 scale bytes of one routed expert."""
+        """Weight bytes plus scale bytes of one routed expert."""
         H, I = self.hidden, self.inter
+        if self.weight_format == "fp4":
+            return (2 * I * H + H * I) // 2 + (2 * I * H + H * I) // GROUP4
         w = 2 * I * H + H * I
         s = (2 * I // TILE) * (H // TILE) * 4 + (H // TILE) * (I // TILE) * 4
         return w + s
+
+    @property
+    def local_experts(self) -> int:
+        return self.local_count or self.experts
 
     def shared_bytes(self) -> int:
         if not self.shared_inter:
@@ -103,6 +117,13 @@ CONFIGS = {
     "latent": MoeShape(
         name="latent", M=64, hidden=3584, inter=1024, experts=896, top_k=16,
         logits_dtype="bf16", routed_scale=1.0, limit=10.0,
+    ),
+    # One GPU's share of the FP4 variant: 48 local experts of 384, top-6,
+    # 16 tokens (nvfp4-megamoe-kernel README: 8 ranks x 48 experts, top-6,
+    # L1 6144 x 7168 and L2 7168 x 3072 per expert).
+    "fp4_share": MoeShape(
+        name="fp4_share", M=16, hidden=7168, inter=3072, experts=384, top_k=6,
+        weight_format="fp4", local_begin=0, local_count=48,
     ),
 }
 
@@ -169,8 +190,65 @@ def _expert_weights(gen: torch.Generator, rows: int, cols: int, scale: torch.Ten
     return w.to(torch.float8_e4m3fn).view(torch.uint8)
 
 
+E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _x_values_fp4(rng: np.random.Generator, shape: MoeShape) -> np.ndarray:
+    """x_kind "int" for the FP4 form: E2M1 grid values with a +-6 in every
+    16-block, so every staged scale is exactly 1 and every code exact."""
+    M, H = shape.M, shape.hidden
+    v = E2M1_GRID[rng.integers(0, 8, size=(M, H // GROUP4, GROUP4))]
+    v *= np.where(rng.integers(0, 2, size=v.shape) == 0, -1.0, 1.0)
+    pos = rng.integers(0, GROUP4, size=(M, H // GROUP4))
+    sign = np.where(rng.integers(0, 2, size=(M, H // GROUP4)) == 0, -6.0, 6.0)
+    np.put_along_axis(v, pos[..., None], sign[..., None], axis=2)
+    return v.reshape(M, H).astype(np.float32)
+
+
+def _make_inputs_fp4(shape: MoeShape, seed: int, device) -> MoeInputs:
+    """FP4 workload: packed weights are uniform random bytes (each nibble an
+    E2M1 code, low nibble first), scale bytes uniform over the UE4M3 codes
+    0x30..0x3F (0.5 .. 1.875), or over {0x30, 0x38, 0x40} (0.5, 1, 2) with
+    `pow2_scales`; local expert e draws from
+    torch.Generator(device).manual_seed(seed * 1000 + e)."""
+    rng = np.random.default_rng(seed)
+    M, H, I, E = shape.M, shape.hidden, shape.inter, shape.experts
+    assert H % TILE == 0 and I % TILE == 0
+    logits = (rng.standard_normal((M, E)) * shape.logits_std).astype(np.float32)
+    bias = (rng.standard_normal(E) * shape.bias_std).astype(np.float32)
+    xv = _x_values_fp4(rng, shape) if shape.x_kind == "int" else _x_values(rng, shape)
+    dev = torch.device(device)
+    lt = torch.from_numpy(logits)
+    if shape.logits_dtype == "bf16":
+        lt = lt.to(torch.bfloat16)
+    El = shape.local_experts
+    w13 = torch.empty((El, 2 * I, H // 2), dtype=torch.uint8, device=dev)
+    s13 = torch.empty((El, 2 * I, H // GROUP4), dtype=torch.uint8, device=dev)
+    w2 = torch.empty((El, H, I // 2), dtype=torch.uint8, device=dev)
+    s2 = torch.empty((El, H, I // GROUP4), dtype=torch.uint8, device=dev)
+    pow2 = torch.tensor([0x30, 0x38, 0x40], dtype=torch.uint8, device=dev)
+
+    def scales(gen, shape_):
+        if shape.pow2_scales:
+            return pow2[torch.randint(0, 3, shape_, generator=gen, device=dev)]
+        return torch.randint(0x30, 0x40, shape_, generator=gen, device=dev).to(torch.uint8)
+
+    for e in range(El):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(seed * 1000 + e)
+        w13[e] = torch.randint(0, 256, (2 * I, H // 2), generator=gen, device=dev).to(torch.uint8)
+        s13[e] = scales(gen, (2 * I, H // GROUP4))
+        w2[e] = torch.randint(0, 256, (H, I // 2), generator=gen, device=dev).to(torch.uint8)
+        s2[e] = scales(gen, (H, I // GROUP4))
+    return MoeInputs(shape=shape, seed=seed, x=torch.from_numpy(xv).to(torch.bfloat16).to(dev),
+                     logits=lt.to(dev), bias=torch.from_numpy(bias).to(dev),
+                     w13=w13, w13_scale=s13, w2=w2, w2_scale=s2)
+
+
 def make_inputs(shape: MoeShape, seed: int = 0, device="cpu") -> MoeInputs:
     """Draws one workload; see the module docstring for the recipe."""
+    if shape.weight_format == "fp4":
+        return _make_inputs_fp4(shape, seed, device)
     rng = np.random.default_rng(seed)
     M, H, I, E = shape.M, shape.hidden, shape.inter, shape.experts
     assert H % TILE == 0 and I % TILE == 0

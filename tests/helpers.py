@@ -39,6 +39,18 @@ def oracle_layer(inp, **over):
     return oracle.moe_decode(host(inp.x), host(inp.logits), host(inp.bias), expert_fn(inp), **kw)
 
 
+def oracle_layer_fp4(inp, local_begin=None, local_count=None):
+    s = inp.shape
+    def get(e: int):
+        return (inp.w13[e].cpu().numpy(), inp.w13_scale[e].cpu().numpy(),
+                inp.w2[e].cpu().numpy(), inp.w2_scale[e].cpu().numpy())
+    lb = s.local_begin if local_begin is None else local_begin
+    lc = s.local_experts if local_count is None else local_count
+    return oracle.fp4.moe_decode_fp4(host(inp.x), host(inp.logits), host(inp.bias), get,
+                                     top_k=s.top_k, routed_scale=s.routed_scale, limit=s.limit,
+                                     local_begin=lb, local_count=lc, inter=s.inter)
+
+
 def oracle_shared(inp, ue8m0_act: bool = True):
     s = inp.shape
     return oracle.shared_expert(host(inp.x), inp.sw13.cpu().numpy(), host(inp.sw13_scale),

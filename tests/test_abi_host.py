@@ -83,6 +83,16 @@ _SHARED = dict(sw13=8192, sw13_scale=8192, sw2=8192, sw2_scale=8192, shared_limi
     (dict(shared_inter=128, shared_scale_format=2, **_SHARED), _capi.ERR_UNSUPPORTED),
     (dict(dict(_SHARED, shared_limit=0.0), shared_inter=128), _capi.ERR_INVALID_ARG),
     (dict(dict(_SHARED, sw2=4104), shared_inter=128), _capi.ERR_INVALID_ARG),  # misaligned
+    # weight format and local experts
+    (dict(weight_format=5), _capi.ERR_UNSUPPORTED),
+    (dict(local_begin=4, local_experts=5), _capi.ERR_INVALID_ARG),   # 4 + 5 > 8 experts
+    (dict(local_begin=-1), _capi.ERR_INVALID_ARG),
+    (dict(local_experts=-2), _capi.ERR_INVALID_ARG),
+    (dict(weight_format=1, hidden=384), _capi.ERR_UNSUPPORTED),      # FP4 needs multiples of 256
+    (dict(weight_format=1, inter=128), _capi.ERR_UNSUPPORTED),
+    (dict(weight_format=1, inter=256, ue8m0_act=1), _capi.ERR_UNSUPPORTED),
+    (dict(weight_format=1, inter=256, gemm_path=3), _capi.ERR_UNSUPPORTED),
+    (dict(dict(_SHARED, shared_inter=128), weight_format=1, inter=256), _capi.ERR_UNSUPPORTED),
 ])
 def test_create_rejects_bad_config(L, kw, code):
     h = ctypes.c_void_p(1234)
