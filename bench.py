@@ -121,10 +121,13 @@ def cpu_baseline(inp, counted_bytes: int) -> dict:
     """The oracle on the host cores, once, on the same inputs (the whole layer
     for all M tokens: it reads only the touched experts)."""
     from threadpoolctl import threadpool_info
-    from tests.helpers import oracle_layer, oracle_shared
+    from tests.helpers import oracle_layer, oracle_layer_fp4, oracle_shared
 
     t0 = time.perf_counter()
-    oracle_layer(inp)
+    if inp.shape.weight_format == "fp4":
+        oracle_layer_fp4(inp)
+    else:
+        oracle_layer(inp)
     if inp.shape.shared_inter:
         oracle_shared(inp)
     dt = time.perf_counter() - t0
@@ -152,7 +155,8 @@ def run_one(args, shape, inp, moe, flush):
         flush.zero_()
         step()
     torch.cuda.synchronize()
-    U = int(torch.unique(ids).numel())
+    local = ids[(ids >= shape.local_begin) & (ids < shape.local_begin + shape.local_experts)]
+    U = int(torch.unique(local).numel())  # distinct local experts touched
     counted = U * shape.expert_bytes() + shape.shared_bytes()
 
     # pass 1: whole layer, events on torch's current stream (the library's stream)
@@ -203,10 +207,13 @@ def main():
         shared = dict(sw13=inp_all.sw13, sw13_scale=inp_all.sw13_scale, sw2=inp_all.sw2,
                       sw2_scale=inp_all.sw2_scale, shared_limit=shape.shared_limit,
                       shared_ue8m0_act=True)
+    fmt = {}
+    if shape.weight_format == "fp4":
+        fmt = dict(weight_format="nvfp4", experts=shape.experts, local_begin=shape.local_begin)
     moe = MoeDecode(inp_all.w13, inp_all.w13_scale, inp_all.w2, inp_all.w2_scale,
                     top_k=shape.top_k, limit=shape.limit, routed_scale=shape.routed_scale,
                     max_tokens=maxM, logits_dtype=inp_all.logits.dtype, ue8m0_act=shape.ue8m0_act,
-                    gemm_path=args.path, splits1=args.splits1, splits2=args.splits2, **shared)
+                    gemm_path=args.path, splits1=args.splits1, splits2=args.splits2, **shared, **fmt)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     for M in Ms:
         sh = base.with_(M=M)
@@ -222,7 +229,10 @@ def main():
         gbs = r["counted"] / (ms * 1e-3) / 1e9
         # dominant kernel: GEMM1 streams W13 (2/3 of the counted bytes), and
         # the shared expert's gate_up weights when there is one
-        g1_bytes = r["U"] * (2 * sh.inter * sh.hidden + (2 * sh.inter // 128) * (sh.hidden // 128) * 4)
+        if sh.weight_format == "fp4":  # packed E2M1 + a UE4M3 byte per 16 values
+            g1_bytes = r["U"] * (2 * sh.inter * sh.hidden // 2 + 2 * sh.inter * sh.hidden // 16)
+        else:
+            g1_bytes = r["U"] * (2 * sh.inter * sh.hidden + (2 * sh.inter // 128) * (sh.hidden // 128) * 4)
         if sh.shared_inter:
             g1_bytes += 2 * sh.shared_inter * sh.hidden + (2 * sh.shared_inter // 128) * (sh.hidden // 128) * 4
         per = np.median(r["per_kernel_ms"], axis=0)
@@ -239,7 +249,7 @@ def main():
             "higher_is_better": True,
             "scaling": "weak",
             "vs_baseline": None,
-            "dtype": "fp8",
+            "dtype": "fp4" if sh.weight_format == "fp4" else "fp8",
             "data": "synthetic",
             "config": {
                 "workload": workload_name(sh),
@@ -251,7 +261,7 @@ def main():
                 "pct_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
                 "kernel_us": {k: round(float(v) * 1e3, 2) for k, v in zip(KERNELS, per)},
                 "wall_ms_per_step_incl_flush": round(r["wall_s"] / args.steps * 1e3, 4),
-                "gemm_path": {1: "valu_splitk", 2: "mfma_splitk", 3: "mfma"}[plan["path"]],
+                "gemm_path": {1: "valu_splitk", 2: "mfma_splitk", 3: "mfma", 4: "fp4"}[plan["path"]],
                 "splits": [plan["splits1"], plan["splits2"]],
                 "kparts": [plan["kparts1"], plan["kparts2"]],
                 "l2_mall_flush": "1 GiB overwrite before every step, outside the timed layer",

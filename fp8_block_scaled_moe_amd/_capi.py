@@ -35,7 +35,7 @@ STAGES = {
     "ctrl": 0, "uexp": 1, "uoff": 2, "ucnt": 3, "routes": 4, "x_q": 5, "x_s": 6,
     "part1": 7, "h_q": 8, "h_s": 9, "part2": 10,
     "shared_x_q": 11, "shared_x_s": 12, "shared_part1": 13, "shared_h_q": 14,
-    "shared_h_s": 15, "shared_part2": 16, "x_f16": 17, "h_f16": 18,
+    "shared_h_s": 15, "shared_part2": 16, "jobs": 17, "route_jobs": 18,
 }
 TIMING_SLOTS = ("route_quant", "gemm1", "swiglu_requant", "gemm2", "combine")
 

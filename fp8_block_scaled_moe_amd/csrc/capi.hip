@@ -11,6 +11,7 @@
 
 #include "../../include/moe_decode.h"
 #include "kernels.h"
+#include "stream_device.h"
 
 using namespace moe;
 
@@ -29,7 +30,7 @@ constexpr int kBadFlagWord = 32;        // word of the control region used by cr
 enum {
   kCtrl, kUexp, kUoff, kUcnt, kRoutes, kXq, kXs, kP1, kHq, kHs, kP2,
   kSXq, kSXs, kSP1, kSHq, kSHs, kSP2,
-  kXd, kHd,  // FP4 form: dequantised F16 activations of GEMM1 and GEMM2
+  kJobs, kRjob,  // FP4 form: the job table and each route's job
 };
 
 struct Plan {
@@ -43,7 +44,6 @@ struct Plan {
   int ss1, sks1, ss2, sks2, stpw1, stpw2, sunits1, sunits2;
   // K-in-workgroup path: K parts per row group (routed, shared)
   int kp1, kp2, skp1, skp2;
-  int rpp1, rpp2;  // FP4 kernel: routes per pass
 };
 
 struct Region {
@@ -65,6 +65,10 @@ struct moe_decode_handle {
   float* s2_owned;
   const float* s13;
   const float* s2;
+  int fp4_wgs1, fp4_wgs2;  // FP4 form: resident workgroups of each GEMM launch
+  // FP4 form: the weight scales reordered for the GEMM kernel (owned)
+  uint8_t* fp4_s13;
+  uint8_t* fp4_s2;
   bool timing;
   bool timed_run;
   hipEvent_t ev[kEvents];
@@ -133,23 +137,25 @@ int choose_kparts(int experts, int N, int nkb, int forced) {
 
 int local_count(const moe_decode_config& c) { return c.local_experts ? c.local_experts : c.experts; }
 
-Plan make_plan(const moe_decode_config& c, int M) {
+// fp4_wgs1/2: the FP4 GEMM launches' resident workgroups (unused otherwise;
+// 0 while only sizing the workspace).
+Plan make_plan(const moe_decode_config& c, int M, int fp4_wgs1 = 0, int fp4_wgs2 = 0) {
   Plan p{};
   const int R = M * c.top_k;
   p.umax = std::min(local_count(c), R);
   if (c.weight_format == MOE_WEIGHTS_NVFP4) {
+    // one launch-wide stream over K steps of 256 values: at most
+    // stream_max_slots partials per tile; the resident workgroups, or one per
+    // route if there are more routes (at most one job each)
     p.path = MOE_GEMM_FP4;
-    p.s1 = p.s2 = 1;
-    p.kp1 = choose_kparts(p.umax, 2 * c.inter, c.hidden / kTile, c.splits1);
-    p.kp2 = choose_kparts(p.umax, c.hidden, c.inter / kTile, c.splits2);
-    p.ks1 = ceil_div(c.hidden / kTile, p.kp1);
-    p.ks2 = ceil_div(c.inter / kTile, p.kp2);
-    p.tpw1 = kRowsPerWg / p.kp1;
-    p.tpw2 = kRowsPerWg / p.kp2;
-    p.grid1 = p.umax * (2 * c.inter / p.tpw1);
-    p.grid2 = p.umax * (c.hidden / p.tpw2);
-    p.rpp1 = gemm_fp4_routes_per_pass(c.hidden);
-    p.rpp2 = gemm_fp4_routes_per_pass(c.inter);
+    p.ks1 = c.hidden / (2 * kTile);
+    p.ks2 = c.inter / (2 * kTile);
+    p.s1 = stream_max_slots(p.ks1);
+    p.s2 = stream_max_slots(p.ks2);
+    p.kp1 = p.kp2 = 1;
+    p.tpw1 = p.tpw2 = kRowsPerWg;
+    p.grid1 = std::max(fp4_wgs1, R);
+    p.grid2 = std::max(fp4_wgs2, R);
     return p;
   }
   const int tiles1 = 2 * c.inter / kRowsPerWg, tiles2 = c.hidden / kRowsPerWg;
@@ -164,8 +170,6 @@ Plan make_plan(const moe_decode_config& c, int M) {
     p.ks2 = ceil_div(c.inter / kTile, p.kp2);
     p.tpw1 = kRowsPerWg / p.kp1;  // rows per workgroup
     p.tpw2 = kRowsPerWg / p.kp2;
-    p.grid1 = p.umax * (2 * c.inter / p.tpw1);
-    p.grid2 = p.umax * (c.hidden / p.tpw2);
     if (c.shared_inter > 0) {
       p.ss1 = p.ss2 = 1;
       p.skp1 = choose_kparts(1, 2 * c.shared_inter, c.hidden / kTile, p.kp1);
@@ -174,9 +178,9 @@ Plan make_plan(const moe_decode_config& c, int M) {
       p.sks2 = ceil_div(c.shared_inter / kTile, p.skp2);
       p.sunits1 = 2 * c.shared_inter / (kRowsPerWg / p.skp1);
       p.sunits2 = c.hidden / (kRowsPerWg / p.skp2);
-      p.grid1 += p.sunits1;
-      p.grid2 += p.sunits2;
     }
+    p.grid1 = p.umax * (2 * c.inter / p.tpw1) + p.sunits1;
+    p.grid2 = p.umax * (c.hidden / p.tpw2) + p.sunits2;
     return p;
   }
   // MFMA costs the same per weight byte for any number of routes of an
@@ -235,8 +239,8 @@ int validate_config(const moe_decode_config* c) {
     if (c->hidden % step || c->inter % step || c->shared_inter != 0 || c->ue8m0_act ||
         c->gemm_path != MOE_GEMM_AUTO)
       return MOE_DECODE_ERR_UNSUPPORTED;
-    for (int K : {c->hidden, c->inter})
-      if (gemm_fp4_lds_bytes(K, gemm_fp4_routes_per_pass(K)) > kMaxWgLds) return MOE_DECODE_ERR_UNSUPPORTED;
+    for (int K : {c->hidden, c->inter})  // two jobs' activations over the whole K in LDS
+      if (gemm_fp4_lds_bytes(K) > kMaxWgLds) return MOE_DECODE_ERR_UNSUPPORTED;
   }
   if (gemm_wg_lds_bytes(std::max(c->hidden, std::max(c->inter, c->shared_inter)) / kTile) > kMaxWgLds)
     return MOE_DECODE_ERR_UNSUPPORTED;
@@ -347,8 +351,8 @@ int moe_decode_create(const moe_decode_config* cfg, moe_decode_t* out) {
       T * Is,                         // shared h_q
       T * (Is / kTile) * sizeof(float),  // shared h_s
       sp2 * sizeof(float),            // shared down partials
-      fp4 ? T * H * 2 : 0,            // dequantised x, F16
-      fp4 ? Rcap * I * 2 : 0,         // dequantised hidden, F16
+      fp4 ? Rcap * sizeof(int32_t) * 4 : 0,  // job table (at most one job per route)
+      fp4 ? Rcap * sizeof(int32_t) : 0,      // job of each route
   };
   moe_decode_handle* h = new (std::nothrow) moe_decode_handle();
   if (!h) return MOE_DECODE_ERR_OUT_OF_MEMORY;
@@ -383,6 +387,30 @@ int moe_decode_create(const moe_decode_config* cfg, moe_decode_t* out) {
       return MOE_DECODE_ERR_HIP;
     }
   }
+  if (fp4) {
+    h->fp4_wgs1 = gemm_fp4_resident_wgs(c.hidden);
+    h->fp4_wgs2 = gemm_fp4_resident_wgs(c.inter);
+    if (h->fp4_wgs1 <= 0 || h->fp4_wgs2 <= 0) {
+      moe_decode_destroy(h);
+      return MOE_DECODE_ERR_HIP;
+    }
+    // the weight scales, read once here into the kernel's layout
+    const size_t El = local_count(c), rows13 = El * 2 * I, rows2 = El * H;
+    if (hipMalloc(&h->fp4_s13, rows13 * (H / 16)) != hipSuccess ||
+        hipMalloc(&h->fp4_s2, rows2 * (I / 16)) != hipSuccess) {
+      (void)hipGetLastError();
+      moe_decode_destroy(h);
+      return MOE_DECODE_ERR_OUT_OF_MEMORY;
+    }
+    if (launch_reorder_fp4_scales(static_cast<const uint8_t*>(c.w13_scale), h->fp4_s13, rows13, (int)H,
+                                  nullptr) != hipSuccess ||
+        launch_reorder_fp4_scales(static_cast<const uint8_t*>(c.w2_scale), h->fp4_s2, rows2, (int)I, nullptr) !=
+            hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
+      moe_decode_destroy(h);
+      return MOE_DECODE_ERR_HIP;
+    }
+  }
   if (Is > 0) {
     const int r = prepare_shared_scales(h);
     if (r != MOE_DECODE_OK) {
@@ -391,7 +419,7 @@ int moe_decode_create(const moe_decode_config* cfg, moe_decode_t* out) {
     }
   }
   if (std::getenv("MOE_DECODE_DEBUG")) {
-    const Plan p = make_plan(c, c.max_tokens);
+    const Plan p = make_plan(c, c.max_tokens, h->fp4_wgs1, h->fp4_wgs2);
     std::fprintf(stderr,
                  "moe_decode: H=%d I=%d E=%d k=%d max_tokens=%d workspace=%zu B; at M=%d: "
                  "path=%d splits1=%d (ks %d) splits2=%d (ks %d) grid1=%d grid2=%d\n",
@@ -412,6 +440,8 @@ void moe_decode_destroy(moe_decode_t h) {
   (void)hipFree(h->ws);
   if (h->s13_owned) (void)hipFree(h->s13_owned);
   if (h->s2_owned) (void)hipFree(h->s2_owned);
+  if (h->fp4_s13) (void)hipFree(h->fp4_s13);
+  if (h->fp4_s2) (void)hipFree(h->fp4_s2);
   (void)hipSetDevice(prev);
   delete h;
 }
@@ -419,12 +449,13 @@ void moe_decode_destroy(moe_decode_t h) {
 int moe_decode_plan(moe_decode_t h, int32_t M, int32_t* out, int32_t n) {
   if (!h || !out || n < 9 || M < 1) return MOE_DECODE_ERR_INVALID_ARG;
   if (M > h->cfg.max_tokens) return MOE_DECODE_ERR_TOO_MANY_TOKENS;
-  const Plan p = make_plan(h->cfg, M);
+  const Plan p = make_plan(h->cfg, M, h->fp4_wgs1, h->fp4_wgs2);
   out[0] = p.path;
   out[1] = p.s1;
   out[2] = p.s2;
-  out[3] = p.ks1;
-  out[4] = p.ks2;
+  const int blk = p.path == MOE_GEMM_FP4 ? 2 : 1;  // the FP4 plan counts 256-value steps
+  out[3] = p.ks1 * blk;
+  out[4] = p.ks2 * blk;
   out[5] = p.grid1;
   out[6] = p.grid2;
   out[7] = p.tpw1;
@@ -462,7 +493,7 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
 
   const moe_decode_config& c = h->cfg;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const Plan p = make_plan(c, M);
+  const Plan p = make_plan(c, M, h->fp4_wgs1, h->fp4_wgs2);
   const int R = M * c.top_k;
   const bool fp4 = c.weight_format == MOE_WEIGHTS_NVFP4;
   const int lb = c.local_begin, lc = local_count(c);
@@ -476,6 +507,8 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   b.uoff = reinterpret_cast<int32_t*>(at(kUoff));
   b.ucnt = reinterpret_cast<int32_t*>(at(kUcnt));
   b.routes = reinterpret_cast<int32_t*>(at(kRoutes));
+  b.jobs = reinterpret_cast<int4*>(at(kJobs));
+  b.rjob = reinterpret_cast<int32_t*>(at(kRjob));
   uint8_t* xq = at(kXq);
   float* xs = atf(kXs);
   float* p1 = atf(kP1);
@@ -516,7 +549,7 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   ra.ue8m0_2 = c.shared_ue8m0_act;
   ra.fp4 = fp4;
   ra.xs4 = at(kXs);
-  ra.xd = reinterpret_cast<_Float16*>(at(kXd));
+  ra.job_routes = fp4 ? kFp4JobRoutes : 0;
   ra.lb = lb;
   ra.lc = lc;
   ra.b = b;
@@ -541,7 +574,7 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   sa.shs = atf(kSHs);
   sa.fp4 = fp4;
   sa.hs4 = at(kHs);
-  sa.hd = reinterpret_cast<_Float16*>(at(kHd));
+  sa.stream = StreamDesc{b.ctrl, b.rjob, 2 * c.inter / kRowsPerWg, c.hidden / (2 * kTile), h->fp4_wgs1};
   sa.ids = ids;
   sa.lb = lb;
   sa.lc = lc;
@@ -561,6 +594,8 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   ca.ids = ids;
   ca.lb = lb;
   ca.lc = lc;
+  ca.fp4 = fp4;
+  ca.stream = StreamDesc{b.ctrl, b.rjob, c.hidden / kRowsPerWg, c.inter / (2 * kTile), h->fp4_wgs2};
 
   // problem descriptor of N x K weights and their activations
   auto problem = [](const void* w, const void* ws, const uint8_t* aq, const float* as, float* part, int N,
@@ -596,8 +631,10 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   g1.p[1] = problem(c.w13, c.w13_scale, xq, xs, p1, 2 * c.inter, c.hidden, p.s1, p.ks1, R, c.top_k, p.tpw1);
   g1.p[1].b = b;
   g1.p[1].kparts = p.kp1;
-  g1.p[1].ad = reinterpret_cast<const _Float16*>(at(kXd));
-  g1.pass_routes = fp4 ? p.rpp1 : p.pass_routes;
+  g1.p[1].as8 = at(kXs);
+  if (fp4) g1.p[1].ws8 = h->fp4_s13;
+  g1.pass_routes = p.pass_routes;
+  g1.stream_wgs = h->fp4_wgs1;
   if (shared) {
     g1.p[0] = problem(c.sw13, h->s13, sxq, sxs, atf(kSP1), 2 * c.shared_inter, c.hidden, p.ss1, p.sks1, M, 1,
                       p.stpw1);
@@ -615,8 +652,10 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   g2.p[1] = problem(c.w2, c.w2_scale, hq, hs, p2, c.hidden, c.inter, p.s2, p.ks2, R, 1, p.tpw2);
   g2.p[1].b = b;
   g2.p[1].kparts = p.kp2;
-  g2.p[1].ad = reinterpret_cast<const _Float16*>(at(kHd));
-  g2.pass_routes = fp4 ? p.rpp2 : p.pass_routes;
+  g2.p[1].as8 = at(kHs);
+  if (fp4) g2.p[1].ws8 = h->fp4_s2;
+  g2.pass_routes = p.pass_routes;
+  g2.stream_wgs = h->fp4_wgs2;
   if (shared) {
     g2.p[0] = problem(c.sw2, h->s2, at(kSHq), atf(kSHs), atf(kSP2), c.hidden, c.shared_inter, p.ss2, p.sks2,
                       M, 1, p.stpw2);
@@ -638,7 +677,7 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
 int moe_decode_debug_stage(moe_decode_t h, int32_t stage, void* dst, size_t bytes, void* stream) {
   if (!h || !dst || stage < 0 || stage >= kRegions) return MOE_DECODE_ERR_INVALID_ARG;
   if (stage >= kSXq && stage <= kSP2 && h->cfg.shared_inter == 0) return MOE_DECODE_ERR_INVALID_ARG;
-  if (stage >= kXd && h->cfg.weight_format != MOE_WEIGHTS_NVFP4) return MOE_DECODE_ERR_INVALID_ARG;
+  if (stage >= kJobs && h->cfg.weight_format != MOE_WEIGHTS_NVFP4) return MOE_DECODE_ERR_INVALID_ARG;
   if (!h->shared_own_quant && (stage == kSXq || stage == kSXs)) stage = stage == kSXq ? kXq : kXs;
   const Region& r = h->reg[stage];
   const size_t n = std::min(bytes, r.bytes);

@@ -5,6 +5,7 @@
 #include "kernels.h"
 #include "device_common.h"
 #include "fp4_device.h"
+#include "stream_device.h"
 
 namespace moe {
 
@@ -90,18 +91,33 @@ __device__ __forceinline__ void swiglu_shared_block(const SwigluArgs& a, int t, 
   if (lane == 0) a.shs[(size_t)t * nblk + c] = s;
 }
 
+// The FP32 total of the stream partials of row n for route r (slot order),
+// over columns n and n + 1 (the same tile), written back to slot 0 so that
+// slot 0 holds the GEMM's output afterwards.
+__device__ __forceinline__ float2 stream_total2(const StreamDesc& d, float* part, int R, int N, int r, int n) {
+  const int slots = stream_slots(d, r, n);
+  float2 v = {0.f, 0.f};
+  for (int s = 0; s < slots; ++s) {
+    const float2 p = *reinterpret_cast<const float2*>(part + ((size_t)s * R + r) * N + n);
+    v.x += p.x;
+    v.y += p.y;
+  }
+  if (slots > 1) *reinterpret_cast<float2*>(part + (size_t)r * N + n) = v;
+  return v;
+}
+
 // One wave, FP4 form (nvfp4-megamoe-kernel README: SiLU times up per slot,
 // then the activation staged to E2M1 for L2): route r, columns
 // [128c, 128c + 128) of the hidden, two per lane. gate/up are GEMM1's FP32
-// sums rounded to BF16 (gate rows first); gate = min(gate, L), up = clamp(up,
-// -L, L); act = BF16(gate / (1 + exp(-gate)) * up) in FP32 steps with the exp
-// correctly rounded; then per 16 values (eight lanes) the E2M1 codes, the
-// UE4M3 scale and the dequantised F16 values.
+// sums (stream partials added in slot order) rounded to BF16 (gate rows
+// first); gate = min(gate, L), up = clamp(up, -L, L); act = BF16(gate /
+// (1 + exp(-gate)) * up) in FP32 steps with the exp correctly rounded; then
+// per 16 values (eight lanes) the E2M1 codes and the UE4M3 scale.
 __device__ __forceinline__ void swiglu_fp4_block(const SwigluArgs& a, int r, int c, int lane) {
   const int j = c * kTile + 2 * lane;
-  const float* p = a.part + (size_t)r * 2 * a.I;
-  const float2 g = *reinterpret_cast<const float2*>(p + j);
-  const float2 u = *reinterpret_cast<const float2*>(p + a.I + j);
+  float* part = const_cast<float*>(a.part);
+  const float2 g = stream_total2(a.stream, part, a.R, 2 * a.I, r, j);
+  const float2 u = stream_total2(a.stream, part, a.R, 2 * a.I, r, a.I + j);
   const float L = a.limit;
   const float g0 = fminf(bf16_round(g.x), L), g1 = fminf(bf16_round(g.y), L);
   const float u0 = fminf(fmaxf(bf16_round(u.x), -L), L), u1 = fminf(fmaxf(bf16_round(u.y), -L), L);
@@ -115,8 +131,6 @@ __device__ __forceinline__ void swiglu_fp4_block(const SwigluArgs& a, int r, int
   const uint32_t q1 = s > 0.f ? e2m1_encode(act1 / s) : 0u;
   a.hq[((size_t)r * a.I + j) / 2] = (uint8_t)(q0 | (q1 << 4));
   if ((lane & 7) == 0) a.hs4[((size_t)r * a.I + j) / kFp4Group] = (uint8_t)sbyte;
-  *reinterpret_cast<half2_t*>(a.hd + (size_t)r * a.I + j) =
-      half2_t{(_Float16)(e2m1_value(q0) * s), (_Float16)(e2m1_value(q1) * s)};
 }
 
 // The whole workgroup (256 threads): token t, hidden columns
@@ -137,8 +151,9 @@ __device__ __forceinline__ void combine_token_tile(const CombineArgs& a, int t, 
     const int e = a.ids[r] - a.lb;
     float v = 0.f;  // non-local experts: a zero slot, nothing added below
     if (e >= 0 && e < a.lc) {
+      const int splits = a.fp4 ? stream_slots(a.stream, r, col0 + c) : a.splits;
 #pragma unroll 4
-      for (int s = 0; s < a.splits; ++s) v += a.part[((size_t)s * R + r) * a.H + col0 + c];
+      for (int s = 0; s < splits; ++s) v += a.part[((size_t)s * R + r) * a.H + col0 + c];
     }
     const uint32_t b = bf16_bits(v);
     a.slots[(size_t)r * a.H + col0 + c] = (uint16_t)b;

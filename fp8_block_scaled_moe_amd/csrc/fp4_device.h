@@ -22,14 +22,6 @@ __device__ __forceinline__ uint32_t e2m1_encode(float a) {
   return c | ((__float_as_uint(a) >> 28) & 8u);
 }
 
-// Value of an E2M1 code: twice the magnitude is 0,1,2,3,4,6,8,12 (one byte
-// each of the constant below).
-__device__ __forceinline__ float e2m1_value(uint32_t code) {
-  const uint64_t twice = 0x0C08060403020100ull;
-  const float m = (float)((twice >> (8 * (code & 7u))) & 0xFFu) * 0.5f;
-  return (code & 8u) ? -m : m;
-}
-
 // Value of a UE4M3 (e4m3) byte, exact.
 __device__ __forceinline__ float e4m3_value(uint32_t byte) {
   return __builtin_amdgcn_cvt_f32_fp8((int)(byte & 0xFFu), 0);
@@ -38,10 +30,8 @@ __device__ __forceinline__ float e4m3_value(uint32_t byte) {
 // One 16-value group staged to FP4: scale = e4m3(block_max / 6) (FP32
 // quotient, nearest-even, saturating), codes = E2M1 of v / dec(scale), all
 // zero when the stored scale is 0. Returns the scale byte; codes packed two
-// per byte, element 2i in the low nibble, into packed[0..1]; dequantised
-// values (code value x scale, exact in F16) into dq.
-__device__ __forceinline__ uint32_t stage_fp4_group(const float v[kFp4Group], uint32_t packed[2],
-                                                    float dq[kFp4Group]) {
+// per byte, element 2i in the low nibble, into packed[0..1].
+__device__ __forceinline__ uint32_t stage_fp4_group(const float v[kFp4Group], uint32_t packed[2]) {
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < kFp4Group; ++i) amax = fmaxf(amax, fabsf(v[i]));
@@ -52,7 +42,6 @@ __device__ __forceinline__ uint32_t stage_fp4_group(const float v[kFp4Group], ui
   for (int i = 0; i < kFp4Group; ++i) {
     const uint32_t c = s > 0.f ? e2m1_encode(v[i] / s) : 0u;
     packed[i / 8] |= c << (4 * (i % 8));
-    dq[i] = e2m1_value(c) * s;
   }
   return sbyte;
 }

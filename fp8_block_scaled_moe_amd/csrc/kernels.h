@@ -12,11 +12,27 @@ constexpr int kMaxTopK = 32;
 
 // Distinct-expert buckets built by the routing kernel (device memory).
 struct Buckets {
-  int32_t* ctrl;     // [0] arrival counter (self-resetting), [1] U = distinct experts
+  int32_t* ctrl;     // [0] arrival counter (self-resetting), [1] U = distinct experts,
+                     // [2] J = jobs (FP4 form)
   int32_t* uexp;     // [U] expert ids, ascending
   int32_t* uoff;     // [U] first index of the expert's routes in `routes`
   int32_t* ucnt;     // [U] number of routes of the expert
   int32_t* routes;   // [M*k] route indices (t*k + j) grouped by expert, ascending t
+  // FP4 form: each expert's routes cut into jobs of at most job_routes
+  // consecutive entries of `routes`, experts ascending.
+  int4* jobs;        // [J] {local expert, first index in routes, count, 0}
+  int32_t* rjob;     // [M*k] job of each local route
+};
+
+// How the FP4 GEMM's stream of work items (job, 64-row tile, 256-value step;
+// the step fastest) is split over its workgroups, and where the epilogues
+// find a tile's partial sums.
+struct StreamDesc {
+  const int32_t* ctrl;  // ctrl[2] = J
+  const int32_t* rjob;  // job of each route
+  int tiles;            // N / 64
+  int steps;            // K / 256
+  int wgs;              // resident workgroups of the GEMM launch
 };
 
 struct RouteQuantArgs {
@@ -35,17 +51,17 @@ struct RouteQuantArgs {
   uint8_t* xq2;         // second quantisation of x (shared expert), or nullptr
   float* xs2;
   int ue8m0_2;
-  // FP4 staging instead of FP8 (fp4 != 0): packed E2M1 [M, H/2] in xq,
-  // UE4M3 bytes [M, H/16] in xs4, and the exactly dequantised x [M, H] F16.
+  // FP4 staging instead of FP8 (fp4 != 0): packed E2M1 [M, H/2] in xq and
+  // UE4M3 bytes [M, H/16] in xs4; jobs of at most job_routes routes.
   int fp4;
   uint8_t* xs4;
-  _Float16* xd;
+  int job_routes;
   int lb, lc;           // local experts [lb, lb + lc): only their routes are bucketed
   Buckets b;
 };
 
 struct SwigluArgs {
-  const float* part;    // [splits, R, 2I]
+  float* part;          // [splits, R, 2I] (FP4 form: slot 0 receives the totals)
   int splits, R, I;
   float limit;
   uint8_t* hq;          // [R, I]
@@ -58,12 +74,13 @@ struct SwigluArgs {
   int sue8m0;
   uint8_t* shq;         // [M, Is]
   float* shs;           // [M, Is/128]
-  // FP4 form (fp4 != 0): gate rows first, BF16 rounding of the GEMM output
-  // and of the activation, E2M1 staging per 16 into hq (packed [R, I/2]),
-  // hs4 ([R, I/16] UE4M3 bytes) and hd ([R, I] F16, dequantised).
+  // FP4 form (fp4 != 0): GEMM1's partial slots found through `stream`,
+  // their total written back to slot 0; gate rows first, BF16 rounding of
+  // the GEMM output and of the activation, E2M1 staging per 16 into hq
+  // (packed [R, I/2]) and hs4 ([R, I/16] UE4M3 bytes).
   int fp4;
   uint8_t* hs4;
-  _Float16* hd;
+  StreamDesc stream;
   const int32_t* ids;   // [M, k]: routes of non-local experts are skipped
   int lb, lc;
 };
@@ -79,6 +96,8 @@ struct CombineArgs {
   uint16_t* shared_out; // [M, H] bf16
   const int32_t* ids;   // [M, k]: slots of non-local experts are zero
   int lb, lc;
+  int fp4;              // GEMM2's partial slots found through `stream`
+  StreamDesc stream;
 };
 
 // One block-scaled GEMM problem: for every route r of distinct expert u and
@@ -91,9 +110,9 @@ struct CombineArgs {
 struct GemmProblem {
   const uint8_t* w;     // [E, N, K] e4m3 (FP4 kernel: [E, N, K/2] packed E2M1)
   const float* ws;      // [E, N/128, K/128]
-  const uint8_t* ws8;   // FP4 kernel: [E, N, K/16] UE4M3 bytes
-  const _Float16* ad;   // FP4 kernel: dequantised activations [rows, K] F16
-  const uint8_t* aq;    // [rows, K] e4m3
+  const uint8_t* ws8;   // FP4 kernel: UE4M3 bytes, reordered (launch_reorder_fp4_scales)
+  const uint8_t* as8;   // FP4 kernel: [rows, K/16] UE4M3 bytes of the activations
+  const uint8_t* aq;    // [rows, K] e4m3 (FP4 kernel: [rows, K/2] packed E2M1)
   const float* as;      // [rows, K/128]
   float* part;          // [splits, R, N]
   Buckets b;            // routed problems only
@@ -113,13 +132,20 @@ struct GemmArgs {
   GemmProblem p[2];     // [0] dense (shared expert), [1] routed
   int units0;           // work units of p[0]; 0 when there is none
   int pass_routes;      // MFMA path: routes staged per pass (<= 16)
+  int stream_wgs;       // FP4 kernel: resident workgroups (stream_map)
 };
 
-// FP4 GEMM (K summed inside the workgroup, VALU, activations staged in LDS
-// as F16): routes per pass that fit the LDS budget for K.
-int gemm_fp4_routes_per_pass(int K);
-size_t gemm_fp4_lds_bytes(int K, int routes);
+// FP4 GEMM: a stream of (job, tile, step) items split evenly over the
+// workgroups; partial sums per tile go to part[slot] (stream_device.h).
+constexpr int kFp4JobRoutes = 2;  // routes of a job (one pass over an expert's weights)
+size_t gemm_fp4_lds_bytes(int K);
+// workgroups that are resident at once on the current device (0 on error)
+int gemm_fp4_resident_wgs(int K);
 hipError_t launch_gemm_fp4(const GemmArgs& a, int role, int grid, hipStream_t s);
+// Weight scales [rows, K/16] UE4M3 (rows a multiple of 16) into the FP4
+// GEMM's layout: per 16-row group and 256-value step, 64 lanes x 4 bytes
+// (dst holds as many bytes as src).
+hipError_t launch_reorder_fp4_scales(const uint8_t* src, uint8_t* dst, size_t rows, int K, hipStream_t s);
 hipError_t launch_codec_check_fp4(const float* in, uint8_t* q, float* dq, int n, hipStream_t s);
 
 // Work units of a problem per expert: (tiles / tpw) tile groups x splits.

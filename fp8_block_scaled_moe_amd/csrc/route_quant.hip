@@ -173,15 +173,9 @@ __device__ void quant_tokens(const RouteQuantArgs& a, int t0, int ntok) {
         const size_t at = (size_t)t * a.H + (size_t)blk * kTile + sub * 16;
         if (a.fp4) {  // this lane's 16 values are one FP4 group
           uint32_t packed[2];
-          float dq[16];
-          const uint32_t sbyte = stage_fp4_group(v, packed, dq);
+          const uint32_t sbyte = stage_fp4_group(v, packed);
           *reinterpret_cast<uint2*>(a.xq + at / 2) = make_uint2(packed[0], packed[1]);
           a.xs4[at / kFp4Group] = (uint8_t)sbyte;
-          half2_t h[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) h[i] = half2_t{(_Float16)dq[2 * i], (_Float16)dq[2 * i + 1]};
-          *reinterpret_cast<u32x4_t*>(a.xd + at) = *reinterpret_cast<const u32x4_t*>(&h[0]);
-          *reinterpret_cast<u32x4_t*>(a.xd + at + 8) = *reinterpret_cast<const u32x4_t*>(&h[4]);
           continue;
         }
         float amax = kAmaxFloor;
@@ -217,7 +211,8 @@ struct Lds {
   uint64_t* mask;  // [E][W] token bitmask of every expert
   int* ids;        // [M*k] picks
   int* first;      // [E] first route slot of each expert
-  int* scratch;    // [2 * 16] per-wave scan totals
+  int* jbase;      // [E] first job of each expert (FP4 form)
+  int* scratch;    // [3 * kWaves] per-wave scan totals
 };
 
 __device__ __forceinline__ Lds carve(unsigned char* lds, int E, int W, int R) {
@@ -225,7 +220,8 @@ __device__ __forceinline__ Lds carve(unsigned char* lds, int E, int W, int R) {
   l.mask = reinterpret_cast<uint64_t*>(lds);
   l.ids = reinterpret_cast<int*>(lds + (size_t)E * W * 8);
   l.first = l.ids + R;
-  l.scratch = l.first + E;
+  l.jbase = l.first + E;
+  l.scratch = l.jbase + E;
   return l;
 }
 
@@ -244,45 +240,59 @@ __device__ void bucket_routes(const RouteQuantArgs& a, const Lds& l) {
       atomicOr(reinterpret_cast<unsigned long long*>(&l.mask[(size_t)e * W + t / 64]), 1ull << (t % 64));
   }
   __syncthreads();
-  // thread e owns expert e (E <= 1024); block-wide exclusive scan of
-  // (present, count) gives each present expert its rank and first slot
+  // thread e owns expert e (E <= kThreads); block-wide exclusive scan of
+  // (present, count, jobs) gives each present expert its rank, first slot
+  // and first job
+  const int jr = a.job_routes;
   int cnt = 0;
   if (tid < E)
     for (int w = 0; w < W; ++w) cnt += __popcll(l.mask[(size_t)tid * W + w]);
   const int present = cnt > 0;
-  int inc_p = present, inc_r = cnt;
+  const int nj = jr > 0 ? (cnt + jr - 1) / jr : 0;
+  int inc_p = present, inc_r = cnt, inc_j = nj;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
     const int up_p = __shfl_up(inc_p, o, kWave);
     const int up_r = __shfl_up(inc_r, o, kWave);
+    const int up_j = __shfl_up(inc_j, o, kWave);
     if (lane >= o) {
       inc_p += up_p;
       inc_r += up_r;
+      inc_j += up_j;
     }
   }
   if (lane == kWave - 1) {
     l.scratch[wave] = inc_p;
     l.scratch[kWaves + wave] = inc_r;
+    l.scratch[2 * kWaves + wave] = inc_j;
   }
   __syncthreads();
-  int base_p = 0, base_r = 0, all_p = 0;
+  int base_p = 0, base_r = 0, base_j = 0, all_p = 0, all_j = 0;
   for (int w = 0; w < kWaves; ++w) {
-    const int tp = l.scratch[w], tr = l.scratch[kWaves + w];
+    const int tp = l.scratch[w], tr = l.scratch[kWaves + w], tj = l.scratch[2 * kWaves + w];
     if (w < wave) {
       base_p += tp;
       base_r += tr;
+      base_j += tj;
     }
     all_p += tp;
+    all_j += tj;
   }
   if (present) {
     const int u = base_p + inc_p - 1;
     const int o = base_r + inc_r - cnt;
+    const int jb = base_j + inc_j - nj;
     a.b.uexp[u] = tid;
     a.b.uoff[u] = o;
     a.b.ucnt[u] = cnt;
     l.first[tid] = o;
+    l.jbase[tid] = jb;
+    for (int p = 0; p < nj; ++p) a.b.jobs[jb + p] = make_int4(tid, o + p * jr, min(jr, cnt - p * jr), 0);
   }
-  if (tid == 0) a.b.ctrl[1] = all_p;
+  if (tid == 0) {
+    a.b.ctrl[1] = all_p;
+    a.b.ctrl[2] = all_j;
+  }
   __syncthreads();
   for (int r = tid; r < R; r += kThreads) {
     const int e = l.ids[r] - a.lb;
@@ -293,6 +303,7 @@ __device__ void bucket_routes(const RouteQuantArgs& a, const Lds& l) {
     for (int w = 0; w < t / 64; ++w) before += __popcll(m[w]);
     before += __popcll(m[t / 64] & ((1ull << (t % 64)) - 1ull));
     a.b.routes[l.first[e] + before] = r;
+    if (jr > 0) a.b.rjob[r] = l.jbase[e] + before / jr;
   }
 }
 
@@ -321,16 +332,49 @@ __device__ void bucket_routes_wave(const RouteQuantArgs& a, const int* ids, int 
   const bool valid = lane < R;
   const bool first = valid && (lane == 0 || e != prev);
   const uint64_t starts = __ballot(first);
-  if (valid) a.b.routes[lane] = (int)(v & 0xFFFFu);
+  const int route = (int)(v & 0xFFFFu);
+  if (valid) a.b.routes[lane] = route;
+  const uint64_t later = lane == kWave - 1 ? 0ull : starts >> (lane + 1);
+  const int next = later ? lane + 1 + __builtin_ctzll(later) : R;  // end of the run (first lanes)
   if (first) {
     const int u = __popcll(starts & ((1ull << lane) - 1ull));
-    const uint64_t later = lane == kWave - 1 ? 0ull : starts >> (lane + 1);
-    const int next = later ? lane + 1 + __builtin_ctzll(later) : R;
     a.b.uexp[u] = e;
     a.b.uoff[u] = lane;
     a.b.ucnt[u] = next - lane;
   }
   if (lane == 0) a.b.ctrl[1] = __popcll(starts);
+  const int jr = a.job_routes;
+  if (jr > 0) {
+    // each run cut into jobs of jr entries: a scan of the runs' job counts
+    // gives their first jobs; the run's start, end and first job then reach
+    // every lane of the run through an inclusive max-scan (all three rise
+    // from run to run)
+    const int nj = first ? (next - lane + jr - 1) / jr : 0;
+    int inc = nj;
+    int rs = first ? lane : -1, re = first ? next : -1;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int up = __shfl_up(inc, o, kWave);
+      if (lane >= o) inc += up;
+    }
+    int rb = first ? inc - nj : -1;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int up_s = __shfl_up(rs, o, kWave), up_e = __shfl_up(re, o, kWave), up_b = __shfl_up(rb, o, kWave);
+      if (lane >= o) {
+        rs = max(rs, up_s);
+        re = max(re, up_e);
+        rb = max(rb, up_b);
+      }
+    }
+    if (valid) {
+      const int pos = lane - rs, j = rb + pos / jr;
+      a.b.rjob[route] = j;
+      if (pos % jr == 0) a.b.jobs[j] = make_int4(e, lane, min(jr, re - lane), 0);
+    }
+    const int jobs = __shfl(inc, kWave - 1, kWave);
+    if (lane == 0) a.b.ctrl[2] = jobs;
+  }
 }
 
 __device__ __forceinline__ void bucket_any(const RouteQuantArgs& a, const Lds& l) {
@@ -390,7 +434,7 @@ __global__ void codec_check_kernel(const float* in, uint8_t* q, float* dq, int n
 }  // namespace
 
 size_t route_quant_lds_bytes(int E, int words, int routes) {
-  return (size_t)E * words * 8 + (size_t)routes * 4 + (size_t)E * 4 + 2 * kWaves * 4;
+  return (size_t)E * words * 8 + (size_t)routes * 4 + (size_t)E * 8 + 3 * kWaves * 4;
 }
 
 hipError_t launch_route_quant(const RouteQuantArgs& a, hipStream_t s) {

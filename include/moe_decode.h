@@ -112,7 +112,11 @@ typedef struct moe_decode_config {
    *   w2_scale  [El, H, I/16] UE4M3 bytes
    *   H and I multiples of 256; activations are staged to E2M1 with a UE4M3
    *   scale of block_max / 6 per 16 values; GEMM outputs are rounded to BF16;
-   *   no shared expert; ue8m0_act must be 0. */
+   *   no shared expert; ue8m0_act must be 0; splits1/splits2 are ignored
+   *   (the FP4 GEMM spreads its work evenly over the resident workgroups).
+   *   create copies the two scale arrays, reordered for the GEMM kernel, into
+   *   memory the handle owns (an eighth of the weight bytes): later writes to
+   *   the caller's scale buffers are not seen; the weights are read in place. */
   const void* w13;
   const void* w13_scale;
   const void* w2;
@@ -202,12 +206,16 @@ const char* moe_decode_error_string(int code);
  * out[10] = its partial-sum slices, out[11] / out[12] = blocks per split or
  * part, out[13] / out[14] = its work units in the GEMM1 / GEMM2 launches.
  * With n >= 17: out[15] / out[16] = K parts per workgroup in GEMM1 / GEMM2
- * (1 on the split-K paths). n is the capacity of out (>= 9). */
+ * (1 on the split-K paths). On MOE_GEMM_FP4: out[1] / out[2] = the most
+ * partial slots a 64-row tile can have, out[3] / out[4] = 128-K blocks of
+ * the whole K, out[5] / out[6] = launched workgroups (the resident ones, or
+ * one per route when there are more routes). n is the capacity of out
+ * (>= 9). */
 int moe_decode_plan(moe_decode_t h, int32_t M, int32_t* out, int32_t n);
 
 /* Stage read-back: copies workspace region `stage` of the last run into the
  * device buffer dst (bytes = capacity of dst) on stream. Stages:
- *  0 control words int32[2] (arrival counter, distinct experts U)
+ *  0 control words int32[3] (arrival counter, distinct experts U, jobs J)
  *  1 distinct experts, ascending int32[U]   2 their first index into stage 4
  *  3 their route counts int32[U]            4 routes grouped by expert int32[M*k]
  *  5 x_q [M, H] e4m3                        6 x_s [M, H/128] FP32
@@ -220,6 +228,13 @@ int moe_decode_plan(moe_decode_t h, int32_t M, int32_t* out, int32_t n);
  * 13 gate_up split partials FP32 [splits, M, 2Is]
  * 14 h_q [M, Is] e4m3                      15 h_s [M, Is/128] FP32
  * 16 down split partials FP32 [splits, M, H]
+ * MOE_WEIGHTS_NVFP4 handles: stages 5 / 8 hold packed E2M1 ([M, H/2],
+ * [M*k, I/2]) and 6 / 9 UE4M3 bytes ([M, H/16], [M*k, I/16]); stages 7 / 10
+ * hold the GEMMs' partial slots ([slots, M*k, N], out[1] / out[2] of
+ * moe_decode_plan), and after a run slot 0 of stage 7 holds GEMM1's FP32
+ * sums for the local routes; control word 2 is the job count J;
+ * 17 job table int32[J][4] {local expert, first index into stage 4, route
+ *    count (at most 2), 0}         18 job of each local route int32[M*k]
  * The size copied is min(bytes, size of the stage for the handle's maximum). */
 int moe_decode_debug_stage(moe_decode_t h, int32_t stage, void* dst, size_t bytes,
                            void* stream);

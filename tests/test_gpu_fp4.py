@@ -117,16 +117,62 @@ def test_fp4_tiny():
     check_fp4_layer(moe, inp)
 
 
-@pytest.mark.parametrize("kparts", [1, 2, 4])
-def test_fp4_kparts_and_passes(kparts):
-    """Every K split inside the workgroup; many routes per expert (several
-    passes over the weights); a local range covering all experts."""
+JOB_ROUTES = 2  # routes of one job: one pass over an expert's weights
+
+
+def check_jobs(moe, shape, ids):
+    """The job table against the buckets and the routing ids: each touched
+    local expert's routes (ascending) cut into jobs of at most four, experts
+    ascending; every local route mapped to the job holding it."""
+    M, k = shape.M, shape.top_k
+    R = M * k
+    ctrl = stage(moe, "ctrl", 3, torch.int32).cpu().numpy()
+    U, J = int(ctrl[1]), int(ctrl[2])
+    e_loc = ids.reshape(-1).astype(np.int64) - shape.local_begin
+    local = (e_loc >= 0) & (e_loc < shape.local_experts)
+    experts = np.unique(e_loc[local])
+    assert U == experts.size
+    want, want_rjob = [], np.full(R, -1)
+    first = 0
+    for e in experts:
+        routes = np.nonzero(e_loc == e)[0]
+        for p in range(0, routes.size, JOB_ROUTES):
+            part = routes[p:p + JOB_ROUTES]
+            want_rjob[part] = len(want)
+            want.append((e, first + p, part.size, 0))
+        first += routes.size
+    assert J == len(want)
+    jobs = stage(moe, "jobs", 4 * J, torch.int32).cpu().numpy().reshape(J, 4)
+    assert np.array_equal(jobs, np.array(want, dtype=np.int32).reshape(J, 4))
+    rjob = stage(moe, "route_jobs", R, torch.int32).cpu().numpy()
+    assert np.array_equal(rjob[local], want_rjob[local])
+    routes = stage(moe, "routes", R, torch.int32).cpu().numpy()
+    assert np.array_equal(routes[:local.sum()], np.concatenate([np.nonzero(e_loc == e)[0] for e in experts]))
+
+
+def test_fp4_jobs_and_slots():
+    """Many routes per expert (several jobs, so several passes over its
+    weights) and a local range covering all experts; the job table bit-exact."""
     shape = TINY.with_(M=24, hidden=1024, inter=512, experts=10, top_k=4, local_begin=0, local_count=10)
     inp = synth.make_inputs(shape, seed=32, device=DEV)
     inp.bias[[2, 7]] += 10.0  # two experts take every token: 24 routes each
-    moe = make_fp4(inp, splits1=kparts, splits2=kparts)
+    moe = make_fp4(inp)
     ref, _ = check_fp4_layer(moe, inp)
     assert np.all(np.sort(ref["ids"][:, :2], axis=1) == [2, 7])
+    check_jobs(moe, shape, ref["ids"])
+
+
+def test_fp4_more_jobs_than_workgroups():
+    """More jobs than resident workgroups (about 2200 against at most 1536):
+    every workgroup then takes at most one job's items."""
+    shape = TINY.with_(M=256, hidden=512, inter=256, experts=512, top_k=16, local_begin=0, local_count=512)
+    inp = synth.make_inputs(shape, seed=36, device=DEV)
+    moe = make_fp4(inp)
+    plan = moe.plan(shape.M)
+    ref, _ = check_fp4_layer(moe, inp, stages=False)
+    check_jobs(moe, shape, ref["ids"])
+    J = int(stage(moe, "ctrl", 3, torch.int32).cpu().numpy()[2])
+    assert J > 1536 and plan["grid1"] >= J and plan["grid2"] >= J
 
 
 def test_fp4_exact_grid_case():
@@ -160,6 +206,7 @@ def test_fp4_no_local_routes():
     moe = make_fp4(inp)
     slots, ids, weights, combined = run(moe, inp)
     assert (ids.cpu().numpy() < 20).all()
+    assert stage(moe, "ctrl", 3, torch.int32).cpu().numpy()[2] == 0  # no jobs
     assert not slots.float().abs().max().item() and not combined.float().abs().max().item()
 
 
