@@ -31,36 +31,50 @@ from fp8_block_scaled_moe_amd import MoeDecode  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
 
-# HBM bytes per GEMM1 launch from the FETCH_SIZE and WRITE_SIZE counter passes
-# summarised in profiles/gemm1_dsv3_m4.md (each counter scaled by what it read
-# for a plain 256 MiB copy). Valid only for the profiled workload and while the
-# GEMM sources are byte-identical to the profiled ones; otherwise null.
-GEMM1_TRAFFIC = {
-    "sources_sha256_16": "cdfecc9e308ffdc9",
-    "workload": "dsv3", "M": 4, "seed": 0, "unique_experts": 27,
-    # medians per dispatch (KiB) and the copy kernel's reading of 256 MiB
-    "fetch_kib": 387777.25, "write_kib": 512.0,
-    "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0,
-}
-GEMM_SOURCES = ["fp8_block_scaled_moe_amd/csrc/expert_gemm_wg.hip",
-                "fp8_block_scaled_moe_amd/csrc/gemm_device.h",
-                "fp8_block_scaled_moe_amd/csrc/device_common.h",
-                "fp8_block_scaled_moe_amd/csrc/kernels.h"]
+# HBM bytes per GEMM1 launch from FETCH_SIZE and WRITE_SIZE counter passes
+# (each counter scaled by what it read for a plain 256 MiB copy), one entry
+# per profiled kernel and workload; the summaries are in profiles/. An entry
+# is valid only for its workload and while its kernel's sources are
+# byte-identical to the profiled ones; otherwise the traffic is null.
+GEMM1_TRAFFIC = [
+    {"sources": ["fp8_block_scaled_moe_amd/csrc/expert_gemm_wg.hip",
+                 "fp8_block_scaled_moe_amd/csrc/gemm_device.h",
+                 "fp8_block_scaled_moe_amd/csrc/device_common.h",
+                 "fp8_block_scaled_moe_amd/csrc/kernels.h"],
+     "sources_sha256_16": "d71b5c1871bab235",
+     "workload": "dsv3", "M": 4, "seed": 0, "unique_experts": 27,
+     # medians per dispatch (KiB) and the copy kernel's reading of 256 MiB
+     "fetch_kib": 387777.5, "write_kib": 512.0, "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0},
+    {"sources": ["fp8_block_scaled_moe_amd/csrc/expert_gemm_fp4.hip",
+                 "fp8_block_scaled_moe_amd/csrc/fp4_device.h",
+                 "fp8_block_scaled_moe_amd/csrc/stream_device.h",
+                 "fp8_block_scaled_moe_amd/csrc/device_common.h",
+                 "fp8_block_scaled_moe_amd/csrc/kernels.h"],
+     "sources_sha256_16": "ba27f312b9e3bfee",
+     "workload": "fp4_share", "M": 16, "seed": 0, "unique_experts": 4,
+     "fetch_kib": 57173.53, "write_kib": 560.0, "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0},
+]
+
+
+def sources_hash(files) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def gemm1_traffic(workload: str, M: int, seed: int, U: int):
-    import hashlib
-    h = hashlib.sha256()
-    for f in GEMM_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    t = GEMM1_TRAFFIC
-    if (h.hexdigest()[:16] != t["sources_sha256_16"] or (workload, M, seed, U) !=
-            (t["workload"], t["M"], t["seed"], t["unique_experts"])):
-        return None
-    fetch = t["fetch_kib"] * (262144.0 / t["copy_fetch_kib"])
-    write = t["write_kib"] * (262144.0 / t["copy_write_kib"])
-    return int(round((fetch + write) * 1024))
+    for t in GEMM1_TRAFFIC:
+        if (workload, M, seed, U) != (t["workload"], t["M"], t["seed"], t["unique_experts"]):
+            continue
+        if not t["copy_fetch_kib"] or sources_hash(t["sources"]) != t["sources_sha256_16"]:
+            return None
+        fetch = t["fetch_kib"] * (262144.0 / t["copy_fetch_kib"])
+        write = t["write_kib"] * (262144.0 / t["copy_write_kib"])
+        return int(round((fetch + write) * 1024))
+    return None
 
 
 METRIC = "routed-MoE decode µs/layer + achieved HBM GB/s (% peak) at M=1..64 tokens"

@@ -52,10 +52,16 @@ __host__ __device__ __forceinline__ int stream_max_slots(int steps) {
 }
 
 // Slots of row n's tile for route r, whose job the routing kernel recorded.
+// The count is kept within [0, stream_max_slots(steps)] whatever the control
+// words hold (no jobs at all gives 0), so a caller's loop over the slots
+// stays inside the partial buffer.
 __device__ __forceinline__ int stream_slots(const StreamDesc& d, int r, int n) {
   const StreamMap m = stream_map(d.ctrl[2], d.tiles, d.steps, d.wgs);
+  if (m.T <= 0) return 0;
   const int64_t base = ((int64_t)d.rjob[r] * d.tiles + n / kRowsPerWg) * d.steps;
-  return stream_owner(base + d.steps - 1, m) - stream_owner(base, m) + 1;
+  if (base < 0 || base + d.steps > m.T) return 0;
+  const int slots = stream_owner(base + d.steps - 1, m) - stream_owner(base, m) + 1;
+  return min(max(slots, 0), stream_max_slots(d.steps));
 }
 
 }  // namespace moe
