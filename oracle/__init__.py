@@ -13,13 +13,15 @@ Pages cited (all vLLM API docs unless noted):
     _group_scale, _GateUpKernel, _DownKernel, block_scales.
   * "nvfp4-megamoe-kernel" README (blame view): slot representation and the
     bugs list (per-slot SiLU, routing weights applied once).
-  * "kimi_k3 ... ep.comm" page: the combine's FP32 sum rounded once.
+  * "kimi_k3 ... ep.comm" page: the combine's FP32 sum rounded once; the
+    boundary steps of its dispatch and combine (MXFP8 quantisation of the
+    latent, reduce + RMSNorm), in oracle/boundary.py.
 
 Parity status of each function is listed in its docstring; every function
 here is pinned by a `-m "not gpu"` test in tests/test_oracle_*.py.
 """
 
-from . import fp4  # noqa: F401
+from . import boundary, fp4  # noqa: F401
 from .codecs import bf16_round, e4m3_decode, e4m3_encode, f32, E4M3_VALUES  # noqa: F401
 from .moe import (  # noqa: F401
     block_scaled_gemm,
