@@ -200,6 +200,35 @@ def run_one(args, shape, inp, moe, flush):
     return dict(U=U, counted=counted, layer_ms=layer_ms, per_kernel_ms=per, wall_s=wall, ids=ids)
 
 
+def boundary_steps_us(dev, reps: int = 200) -> dict:
+    """Per-call time of the two boundary steps (include/moe_boundary.h) at
+    the expert-parallel page's shape: 5 tokens per rank, latent width 3584,
+    partials from 16 ranks. Both are latency-bound (35 KB and 573 KB in);
+    HIP events around `reps` back-to-back calls on the current stream."""
+    from fp8_block_scaled_moe_amd import mxfp8_quantize, reduce_rmsnorm
+    g = torch.Generator(device=dev).manual_seed(5)
+    x = torch.randn((5, 3584), generator=g, device=dev).to(torch.bfloat16)
+    parts = torch.randn((5, 16, 3584), generator=g, device=dev).to(torch.bfloat16)
+    gamma = torch.ones(3584, dtype=torch.bfloat16, device=dev)
+    out = {}
+    for name, fn in (("mxfp8_quantize", lambda: mxfp8_quantize(x)),
+                     ("reduce_rmsnorm", lambda: reduce_rmsnorm(parts, gamma, 1e-5))):
+        for _ in range(20):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # a spin kernel keeps the queue ahead of the host, so the calls run
+        # back to back on the device and the events time the device work
+        torch.cuda._sleep(int(6e7))
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        b.synchronize()
+        out[name] = round(a.elapsed_time(b) * 1e3 / reps, 2)
+    out["shape"] = "T=5 tokens, D=3584, N=16 partials; calls back to back on the device, inputs L2-resident"
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -293,6 +322,8 @@ def main():
                 "avg_launch_us": round(float(per[1]) * 1e3, 2),
             },
         }
+        if M == Ms[0]:
+            line["config"]["boundary_steps_us"] = boundary_steps_us(dev)
         if not args.no_cpu_baseline and M == Ms[0]:
             line["cpu_baseline"] = cpu_baseline(inp, r["counted"])
         print(json.dumps(line), flush=True)

@@ -7,6 +7,7 @@ library's HIP kernels. PyTorch provides device memory and the stream.
 from __future__ import annotations
 
 import ctypes
+import glob
 import os
 import re
 from typing import Optional, Sequence
@@ -82,9 +83,12 @@ _lib = None
 
 
 def header_functions() -> Sequence[str]:
-    """Names of the functions include/moe_decode.h declares."""
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(moe_decode_\w+)\s*\(", text, re.M)))
+    """Names of the functions the headers in include/ declare."""
+    names = set()
+    for h in sorted(glob.glob(os.path.join(os.path.dirname(HEADER), "*.h"))):
+        text = open(h).read()
+        names |= set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(moe_\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 def lib() -> ctypes.CDLL:
@@ -119,6 +123,10 @@ def lib() -> ctypes.CDLL:
     L.moe_decode_debug_codec.restype = ctypes.c_int
     L.moe_decode_debug_codec_fp4.argtypes = [vp, vp, vp, i32, vp]
     L.moe_decode_debug_codec_fp4.restype = ctypes.c_int
+    L.moe_mxfp8_quantize.argtypes = [vp, i32, i32, vp, vp, vp]
+    L.moe_mxfp8_quantize.restype = ctypes.c_int
+    L.moe_reduce_rmsnorm.argtypes = [vp, i32, i32, i32, vp, ctypes.c_float, vp, vp, vp]
+    L.moe_reduce_rmsnorm.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -335,3 +343,35 @@ def debug_codec(values: torch.Tensor):
     if rc != OK:
         raise MoeDecodeError(rc, "moe_decode_debug_codec")
     return q, dq
+
+
+def mxfp8_quantize(x: torch.Tensor, stream=None):
+    """MXFP8 of BF16 rows x [T, D] (include/moe_boundary.h): e4m3 codes
+    [T, D] uint8 and E8M0 scale bytes [T, D/32] uint8."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [T, D] bfloat16 tensor")
+    T, D = x.shape
+    q = torch.empty((T, D), dtype=torch.uint8, device=x.device)
+    sf = torch.empty((T, max(D // 32, 0)), dtype=torch.uint8, device=x.device)
+    rc = lib().moe_mxfp8_quantize(x.data_ptr(), T, D, q.data_ptr(), sf.data_ptr(), _stream(stream))
+    if rc != OK:
+        raise MoeDecodeError(rc, "moe_mxfp8_quantize")
+    return q, sf
+
+
+def reduce_rmsnorm(partials: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-5,
+                   want_latent: bool = True, stream=None):
+    """Reduce + RMSNorm (include/moe_boundary.h): partials [T, N, D] BF16,
+    gamma [D] BF16 -> (latent [T, D] BF16 or None, out [T, D] BF16)."""
+    if partials.dtype != torch.bfloat16 or partials.dim() != 3 or not partials.is_contiguous():
+        raise ValueError("partials must be a contiguous [T, N, D] bfloat16 tensor")
+    T, N, D = partials.shape
+    if gamma.dtype != torch.bfloat16 or tuple(gamma.shape) != (D,) or not gamma.is_contiguous():
+        raise ValueError(f"gamma must be a contiguous [{D}] bfloat16 tensor")
+    out = torch.empty((T, D), dtype=torch.bfloat16, device=partials.device)
+    latent = torch.empty_like(out) if want_latent else None
+    rc = lib().moe_reduce_rmsnorm(partials.data_ptr(), T, N, D, gamma.data_ptr(), float(eps), _ptr(latent),
+                                  out.data_ptr(), _stream(stream))
+    if rc != OK:
+        raise MoeDecodeError(rc, "moe_reduce_rmsnorm")
+    return latent, out

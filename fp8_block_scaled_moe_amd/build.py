@@ -13,7 +13,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_decode.so")
-SOURCES = ["capi.hip", "route_quant.hip", "expert_gemm.hip", "expert_gemm_wg.hip", "expert_gemm_fp4.hip", "epilogues.hip"]
+SOURCES = ["capi.hip", "route_quant.hip", "expert_gemm.hip", "expert_gemm_wg.hip", "expert_gemm_fp4.hip", "epilogues.hip",
+           "boundary.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -6,8 +6,8 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 "kimi_k3 ... ep.comm" page:
   * EpDispatch: each token's BF16 latent is quantised to MXFP8 (E8M0 scale
     per 32 values, e4m3 elements) before it is sent to the experts' ranks;
-    the scales are stored one byte per 32-block in block order ("the linear
-    layout").
+    the scales are stored one byte per 32-block in plain block
+    order.
   * EpCombine: a token's per-rank BF16 partials are summed in FP32 in rank
     order and rounded once to BF16 (the routed latent), then normalised:
     an FP32 sum of squares, rstd = rsqrt(total / D + eps) with the division

@@ -123,3 +123,34 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(_capi, "LIB_PATH", os.path.join(tempfile.gettempdir(), "no_such_lib.so"))
     with pytest.raises(RuntimeError, match="missing"):
         _capi.lib()
+
+
+def test_boundary_header_compiles_as_c(tmp_path):
+    src = tmp_path / "b.c"
+    src.write_text("#include \"moe_boundary.h\"\nint main(void) { return MOE_BOUNDARY_MAX_D > 0 ? 0 : 1; }\n")
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(tmp_path / "b")], check=True)
+
+
+def test_boundary_argument_errors(L):
+    """Argument checks of the boundary calls return before any device work."""
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: every case fails validation first
+    odd = ctypes.c_void_p(0x1008)
+    # MXFP8: negative T, null or misaligned pointers, D not a multiple of 32 or too long
+    assert L.moe_mxfp8_quantize(fake, -1, 64, fake, fake, None) == _capi.ERR_INVALID_ARG
+    assert L.moe_mxfp8_quantize(None, 1, 64, fake, fake, None) == _capi.ERR_INVALID_ARG
+    assert L.moe_mxfp8_quantize(odd, 1, 64, fake, fake, None) == _capi.ERR_INVALID_ARG
+    assert L.moe_mxfp8_quantize(fake, 1, 48, fake, fake, None) == _capi.ERR_UNSUPPORTED
+    assert L.moe_mxfp8_quantize(fake, 1, 0, fake, fake, None) == _capi.ERR_UNSUPPORTED
+    assert L.moe_mxfp8_quantize(fake, 1, 16384 + 32, fake, fake, None) == _capi.ERR_UNSUPPORTED
+    assert L.moe_mxfp8_quantize(fake, 0, 64, fake, fake, None) == _capi.OK   # empty call
+    # reduce + RMSNorm
+    args = lambda T, N, D, eps=1e-5, lat=fake: (fake, T, N, D, fake, eps, lat, fake, None)  # noqa: E731
+    assert L.moe_reduce_rmsnorm(*args(-1, 1, 64)) == _capi.ERR_INVALID_ARG
+    assert L.moe_reduce_rmsnorm(*args(1, 1, 64, eps=-1.0)) == _capi.ERR_INVALID_ARG
+    assert L.moe_reduce_rmsnorm(*args(1, 1, 64, eps=float("nan"))) == _capi.ERR_INVALID_ARG
+    assert L.moe_reduce_rmsnorm(*args(1, 1, 64, lat=odd)) == _capi.ERR_INVALID_ARG
+    assert L.moe_reduce_rmsnorm(*args(1, 0, 64)) == _capi.ERR_UNSUPPORTED
+    assert L.moe_reduce_rmsnorm(*args(1, 65, 64)) == _capi.ERR_UNSUPPORTED
+    assert L.moe_reduce_rmsnorm(*args(1, 1, 12)) == _capi.ERR_UNSUPPORTED
+    assert L.moe_reduce_rmsnorm(*args(0, 1, 64)) == _capi.OK
