@@ -92,6 +92,7 @@ def parse():
     p.add_argument("--path", default="auto", choices=["auto", "valu_splitk", "mfma_splitk", "mfma"])
     p.add_argument("--splits1", type=int, default=0)
     p.add_argument("--splits2", type=int, default=0)
+    p.add_argument("--launch-mode", default="auto", choices=["auto", "separate", "combine_in_gemm2"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--sweep", default="", help="comma-separated M values: one JSON line each")
     p.add_argument("--calibrate", action="store_true",
@@ -256,7 +257,8 @@ def main():
     moe = MoeDecode(inp_all.w13, inp_all.w13_scale, inp_all.w2, inp_all.w2_scale,
                     top_k=shape.top_k, limit=shape.limit, routed_scale=shape.routed_scale,
                     max_tokens=maxM, logits_dtype=inp_all.logits.dtype, ue8m0_act=shape.ue8m0_act,
-                    gemm_path=args.path, splits1=args.splits1, splits2=args.splits2, **shared, **fmt)
+                    gemm_path=args.path, splits1=args.splits1, splits2=args.splits2,
+                    launch_mode=args.launch_mode, **shared, **fmt)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     for M in Ms:
         sh = base.with_(M=M)
@@ -307,6 +309,7 @@ def main():
                 "gemm_path": {1: "valu_splitk", 2: "mfma_splitk", 3: "mfma", 4: "fp4"}[plan["path"]],
                 "splits": [plan["splits1"], plan["splits2"]],
                 "kparts": [plan["kparts1"], plan["kparts2"]],
+                "launches": plan["launches"],
                 "l2_mall_flush": "1 GiB overwrite before every step, outside the timed layer",
             },
             "roofline": {

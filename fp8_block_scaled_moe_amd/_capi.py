@@ -31,6 +31,7 @@ SCALES_F32 = 0
 SCALES_UE8M0_PACKED = 1
 WEIGHT_FORMATS = {"fp8": 0, "nvfp4": 1}
 GEMM_PATHS = {"auto": 0, "valu_splitk": 1, "mfma_splitk": 2, "mfma": 3, "fp4": 4}
+LAUNCH_MODES = {"auto": 0, "separate": 1, "combine_in_gemm2": 2}
 
 STAGES = {
     "ctrl": 0, "uexp": 1, "uoff": 2, "ucnt": 3, "routes": 4, "x_q": 5, "x_s": 6,
@@ -70,6 +71,7 @@ class MoeDecodeConfig(ctypes.Structure):
         ("weight_format", ctypes.c_int32),
         ("local_begin", ctypes.c_int32),
         ("local_experts", ctypes.c_int32),
+        ("launch_mode", ctypes.c_int32),
     ]
 
 
@@ -180,7 +182,8 @@ class MoeDecode:
                  ue8m0_act: bool = False, gemm_path: str = "auto", splits1: int = 0,
                  splits2: int = 0, sw13=None, sw13_scale=None, sw2=None, sw2_scale=None,
                  shared_limit: Optional[float] = None, shared_ue8m0_act: bool = True,
-                 weight_format: str = "fp8", experts: Optional[int] = None, local_begin: int = 0):
+                 weight_format: str = "fp8", experts: Optional[int] = None, local_begin: int = 0,
+                 launch_mode: str = "auto"):
         self.device = w13.device
         fp4 = weight_format == "nvfp4"
         sdt = _FP8 if fp4 else (torch.float32,)
@@ -208,6 +211,7 @@ class MoeDecode:
         cfg.weight_format = WEIGHT_FORMATS[weight_format]
         cfg.local_begin = local_begin
         cfg.local_experts = 0 if El == E else El
+        cfg.launch_mode = LAUNCH_MODES[launch_mode]
         self.shared_inter = 0
         if sw13 is not None:
             _need(sw13, "sw13", _FP8, self.device)
@@ -279,13 +283,13 @@ class MoeDecode:
         return (ids >= self.local_begin) & (ids < self.local_begin + self.local_experts)
 
     def plan(self, M: int) -> dict:
-        buf = (ctypes.c_int32 * 17)()
-        rc = lib().moe_decode_plan(self._h, M, buf, 17)
+        buf = (ctypes.c_int32 * 18)()
+        rc = lib().moe_decode_plan(self._h, M, buf, 18)
         if rc != OK:
             raise MoeDecodeError(rc, "moe_decode_plan")
         keys = ("path", "splits1", "splits2", "ks1", "ks2", "grid1", "grid2", "rows1", "rows2",
                 "shared_splits1", "shared_splits2", "shared_ks1", "shared_ks2",
-                "shared_units1", "shared_units2", "kparts1", "kparts2")
+                "shared_units1", "shared_units2", "kparts1", "kparts2", "launches")
         return dict(zip(keys, list(buf)))
 
     def stage(self, name: str, dst: torch.Tensor, stream=None) -> torch.Tensor:

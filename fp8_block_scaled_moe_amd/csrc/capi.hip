@@ -18,7 +18,7 @@ using namespace moe;
 namespace {
 
 constexpr int kEvents = 8;
-constexpr int kRegions = 19;
+constexpr int kRegions = 20;
 constexpr int kStages = 5;  // timing slots: route, GEMM1, SwiGLU, GEMM2, combine
 constexpr int kTargetUnits = 4096;  // work units per GEMM launch to aim for (16 per CU)
 constexpr int kDenseTargetUnits = 256;  // units of the shared expert per GEMM launch
@@ -31,6 +31,7 @@ enum {
   kCtrl, kUexp, kUoff, kUcnt, kRoutes, kXq, kXs, kP1, kHq, kHs, kP2,
   kSXq, kSXs, kSP1, kSHq, kSHs, kSP2,
   kJobs, kRjob,  // FP4 form: the job table and each route's job
+  kCount,        // fused GEMM2 + combine: arrivals per (token, column tile)
 };
 
 struct Plan {
@@ -44,6 +45,7 @@ struct Plan {
   int ss1, sks1, ss2, sks2, stpw1, stpw2, sunits1, sunits2;
   // K-in-workgroup path: K parts per row group (routed, shared)
   int kp1, kp2, skp1, skp2;
+  bool fuse_combine;  // the combine runs inside the GEMM2 launch
 };
 
 struct Region {
@@ -181,6 +183,7 @@ Plan make_plan(const moe_decode_config& c, int M, int fp4_wgs1 = 0, int fp4_wgs2
     }
     p.grid1 = p.umax * (2 * c.inter / p.tpw1) + p.sunits1;
     p.grid2 = p.umax * (c.hidden / p.tpw2) + p.sunits2;
+    p.fuse_combine = c.launch_mode == MOE_LAUNCH_COMBINE_IN_GEMM2;
     return p;
   }
   // MFMA costs the same per weight byte for any number of routes of an
@@ -245,6 +248,8 @@ int validate_config(const moe_decode_config* c) {
   if (gemm_wg_lds_bytes(std::max(c->hidden, std::max(c->inter, c->shared_inter)) / kTile) > kMaxWgLds)
     return MOE_DECODE_ERR_UNSUPPORTED;
   if (c->splits1 < 0 || c->splits2 < 0) return MOE_DECODE_ERR_INVALID_ARG;
+  if (c->launch_mode < MOE_LAUNCH_AUTO || c->launch_mode > MOE_LAUNCH_COMBINE_IN_GEMM2)
+    return MOE_DECODE_ERR_UNSUPPORTED;
   {
     const int words = (c->max_tokens + 63) / 64;
     if (route_quant_lds_bytes(c->experts, words, c->max_tokens * c->top_k) > kMaxRouteLds)
@@ -353,6 +358,7 @@ int moe_decode_create(const moe_decode_config* cfg, moe_decode_t* out) {
       sp2 * sizeof(float),            // shared down partials
       fp4 ? Rcap * sizeof(int32_t) * 4 : 0,  // job table (at most one job per route)
       fp4 ? Rcap * sizeof(int32_t) : 0,      // job of each route
+      fp4 ? 0 : T * (H / 16) * sizeof(int32_t),  // arrival counts (at least 16 rows per workgroup)
   };
   moe_decode_handle* h = new (std::nothrow) moe_decode_handle();
   if (!h) return MOE_DECODE_ERR_OUT_OF_MEMORY;
@@ -472,6 +478,7 @@ int moe_decode_plan(moe_decode_t h, int32_t M, int32_t* out, int32_t n) {
     out[15] = p.path == MOE_GEMM_MFMA ? p.kp1 : 1;
     out[16] = p.path == MOE_GEMM_MFMA ? p.kp2 : 1;
   }
+  if (n >= 18) out[17] = p.fuse_combine ? 4 : 5;
   return MOE_DECODE_OK;
 }
 
@@ -663,11 +670,28 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
     g2.p[0].kparts = p.skp2;
     g2.units0 = p.sunits2;
   }
+  if (p.fuse_combine) {
+    CombineFuse& f = g2.cf;
+    f.on = 1;
+    f.counters = reinterpret_cast<int32_t*>(at(kCount));
+    f.ids = ids;
+    f.weights = weights;
+    f.slots = ca.slots;
+    f.combined = ca.combined;
+    f.shared_out = ca.shared_out;
+    f.M = M;
+    f.k = c.top_k;
+    f.lb = lb;
+    f.lc = lc;
+    f.all_local = lb == 0 && lc == c.experts;
+  }
   if (e == hipSuccess) e = launch_gemm(g2, 2, p.grid2 - (shared ? 0 : p.sunits2));
   if (e == hipSuccess) e = mark(3);
 
-  if (e == hipSuccess) e = launch_combine(ca, s);
-  if (e == hipSuccess) e = mark(4);
+  if (!p.fuse_combine) {
+    if (e == hipSuccess) e = launch_combine(ca, s);
+    if (e == hipSuccess) e = mark(4);
+  }
 
   h->timed_run = h->timing;
   h->ev_count = evn;
@@ -675,7 +699,7 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
 }
 
 int moe_decode_debug_stage(moe_decode_t h, int32_t stage, void* dst, size_t bytes, void* stream) {
-  if (!h || !dst || stage < 0 || stage >= kRegions) return MOE_DECODE_ERR_INVALID_ARG;
+  if (!h || !dst || stage < 0 || stage >= kCount) return MOE_DECODE_ERR_INVALID_ARG;
   if (stage >= kSXq && stage <= kSP2 && h->cfg.shared_inter == 0) return MOE_DECODE_ERR_INVALID_ARG;
   if (stage >= kJobs && h->cfg.weight_format != MOE_WEIGHTS_NVFP4) return MOE_DECODE_ERR_INVALID_ARG;
   if (!h->shared_own_quant && (stage == kSXq || stage == kSXs)) stage = stage == kSXq ? kXq : kXs;

@@ -21,6 +21,14 @@
 // pass's 16 routes come straight from L2 into registers in the MFMA layout,
 // so no LDS staging bounds how much of K a workgroup covers. Both streams are
 // requested kDepth steps ahead.
+//
+// GEMM2 can also finish the layer in the same launch (kFuse): its FP32
+// outputs are then stored at device scope, and once a unit's stores have
+// completed it counts one arrival per route on (token, column tile). The
+// arrival that completes a count (the token's local picks) finds every slot
+// value of that tile in memory and writes the tile's BF16 slots and combined
+// values, with the arithmetic of the separate combine kernel (weights applied
+// once, FP32 sum in pick order). No workgroup ever waits for another.
 #include <algorithm>
 
 #include "gemm_device.h"
@@ -33,14 +41,78 @@ constexpr int kDepth = 2;          // 128-K steps in flight per wave (keeps four
 constexpr int kRoutesPerPass = 16;  // MFMA columns
 constexpr int kRedFloats = 4 * kWave * 4;  // the four waves' 16 x 16 results
 
-template <int kRole>
+// Picks of token t whose expert is local.
+__device__ __forceinline__ int local_picks(const CombineFuse& f, int t) {
+  if (f.all_local) return f.k;
+  int n = 0;
+  for (int j = 0; j < f.k; ++j) {
+    const int e = f.ids[(size_t)t * f.k + j] - f.lb;
+    n += e >= 0 && e < f.lc;
+  }
+  return n;
+}
+
+// Whole workgroup: slots and combined values of token t over columns
+// [c0, c0 + w) (w <= 64), reading the FP32 slot values of the local picks at
+// device scope. Each slot is its GEMM output rounded once to BF16, zero for a
+// pick whose expert is not local; combined = BF16(sum_j w[t, j] * slot_j),
+// the FP32 sum in pick order (nvfp4-megamoe-kernel README, slot
+// representation). `lds` holds k * 64 floats. Contains barriers.
+__device__ void combine_tile(const CombineFuse& f, const float* part, int H, int t, int c0, int w, float* lds) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < f.k * w; i += kThreads) {
+    const int j = i / w, c = i - j * w;
+    const size_t r = (size_t)t * f.k + j;
+    const int e = f.ids[r] - f.lb;
+    float v = 0.f;
+    if (e >= 0 && e < f.lc) v += __hip_atomic_load(part + r * H + c0 + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t b = bf16_bits(v);
+    f.slots[r * H + c0 + c] = (uint16_t)b;
+    lds[j * 64 + c] = bf16_value(b);
+  }
+  __syncthreads();
+  if (tid < w) {
+    float acc = 0.f;
+    for (int j = 0; j < f.k; ++j) acc = fmaf(f.weights[(size_t)t * f.k + j], lds[j * 64 + tid], acc);
+    f.combined[(size_t)t * H + c0 + tid] = bf16_bits(acc);
+  }
+  __syncthreads();
+}
+
+// Workgroup 0 of a fused launch: tokens without a local pick get zero slot
+// rows and a zero combined row (no unit counts arrivals for them).
+__device__ void zero_unrouted_tokens(const CombineFuse& f, int H, int* list, int& nlist) {
+  const int tid = threadIdx.x;
+  if (tid == 0) nlist = 0;
+  __syncthreads();
+  for (int t = tid; t < f.M; t += kThreads)
+    if (local_picks(f, t) == 0) list[atomicAdd(&nlist, 1)] = t;
+  __syncthreads();
+  const int n = nlist, row16 = H / 8;  // 16-byte words per BF16 row
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  for (int q = 0; q < n; ++q) {
+    const int t = list[q];
+    for (int i = tid; i < (f.k + 1) * row16; i += kThreads) {
+      const int j = i / row16, c = i - j * row16;
+      uint16_t* row = j < f.k ? f.slots + ((size_t)t * f.k + j) * H : f.combined + (size_t)t * H;
+      reinterpret_cast<u32x4_t*>(row)[c] = zero;
+    }
+  }
+  __syncthreads();
+}
+
+template <int kRole, bool kFuse>
 __global__ __launch_bounds__(kThreads) void gemm_wg_kernel(GemmArgs args) {
   extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int nclaim;
   int unit;
   const GemmProblem a = select_problem(args, unit);
+  const CombineFuse& f = args.cf;
   const int kparts = a.kparts;
   const int rows_wg = kRowsPerWg / kparts;
   const int per_expert = a.N / rows_wg;
+  if (kFuse && !f.all_local && blockIdx.x == 0)
+    zero_unrouted_tokens(f, a.N, reinterpret_cast<int*>(smem + 4 * kTileBytes), nclaim);
   const int U = a.dense ? 1 : a.b.ctrl[1];
   if (unit >= U * per_expert) return;  // past the touched experts: the whole workgroup exits
   const int ui = unit / per_expert, tile = unit - ui * per_expert;
@@ -156,8 +228,43 @@ __global__ __launch_bounds__(kThreads) void gemm_wg_kernel(GemmArgs args) {
     }
     if (kp == 0 && live) {
       float* dst = a.part + (size_t)rts[col] * a.N + row0 + 4 * g;
-      *reinterpret_cast<float4_t*>(dst) = acc;
+      if (kFuse && !a.dense) {  // read back by whichever workgroup completes the tile
+#pragma unroll
+        for (int i = 0; i < 4; ++i) __hip_atomic_store(dst + i, acc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        *reinterpret_cast<float4_t*>(dst) = acc;
+      }
+      if (kFuse && a.dense && f.shared_out) {  // the shared expert's output row, rounded once
+        uint16_t* so = f.shared_out + (size_t)rts[col] * a.N + row0 + 4 * g;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) so[i] = bf16_bits(0.f + acc[i]);
+      }
     }
+  }
+
+  if constexpr (kFuse) {
+    if (a.dense) return;
+    // This unit's outputs were stored at device scope: once those stores have
+    // completed they are visible to the workgroup that completes each count
+    // (the pattern of the routing kernel's arrival counter; no release fence,
+    // which would write back the whole L2).
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int* claimed = reinterpret_cast<int*>(red);  // tokens whose tile this unit completes (<= cnt)
+    if (tid == 0) nclaim = 0;
+    __syncthreads();
+    for (int i = tid; i < cnt; i += kThreads) {
+      const int t = a.b.routes[off + i] / f.k;
+      int32_t* ctr = f.counters + (size_t)t * per_expert + tile;
+      if (__hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == local_picks(f, t) - 1) {
+        __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
+        claimed[atomicAdd(&nclaim, 1)] = t;
+      }
+    }
+    __syncthreads();
+    const int n = nclaim;
+    float* lds = reinterpret_cast<float*>(smem);  // the weight tiles' space: k * 64 floats
+    for (int q = 0; q < n; ++q) combine_tile(f, a.part, a.N, claimed[q], tile * rows_wg, rows_wg, lds);
   }
 }
 
@@ -171,10 +278,17 @@ size_t gemm_wg_lds_bytes(int nkb) {
 hipError_t launch_gemm_wg(const GemmArgs& a, int role, int grid, hipStream_t s) {
   const int nkb = a.units0 ? std::max(a.p[0].nkb, a.p[1].nkb) : a.p[1].nkb;
   const size_t lds = gemm_wg_lds_bytes(nkb);
-  if (role == 1)
-    hipLaunchKernelGGL(gemm_wg_kernel<1>, dim3(grid), dim3(kThreads), lds, s, a);
-  else
-    hipLaunchKernelGGL(gemm_wg_kernel<2>, dim3(grid), dim3(kThreads), lds, s, a);
+  if (a.cf.on) {
+    // the combine's LDS (k x 64 floats) and token list reuse the weight tiles
+    // and the reduction buffer; output rows are H wide
+    if (role != 2 || a.cf.k > kMaxTopK || a.cf.M > kRedFloats || (a.units0 && a.p[0].N != a.p[1].N))
+      return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_wg_kernel<2, true>), dim3(grid), dim3(kThreads), lds, s, a);
+  } else if (role == 1) {
+    hipLaunchKernelGGL((gemm_wg_kernel<1, false>), dim3(grid), dim3(kThreads), lds, s, a);
+  } else {
+    hipLaunchKernelGGL((gemm_wg_kernel<2, false>), dim3(grid), dim3(kThreads), lds, s, a);
+  }
   return hipGetLastError();
 }
 

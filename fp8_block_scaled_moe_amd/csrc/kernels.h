@@ -126,6 +126,23 @@ struct GemmProblem {
   int kparts;           // K-in-workgroup kernel: K ranges per row group (1, 2 or 4); 64 / kparts rows
 };
 
+// The combine carried out inside the GEMM2 launch (K-in-workgroup kernel):
+// each unit, once its outputs are stored at device scope, counts one arrival
+// per route on (token, column tile); the arrival that completes a tile's
+// count (the token's local picks) writes that tile's slots and combined row.
+// Counters reset themselves. Arrays as in CombineArgs.
+struct CombineFuse {
+  int on;               // 0: plain GEMM (combine_kernel follows)
+  int32_t* counters;    // [M, N / rows per workgroup], zero between calls
+  const int32_t* ids;   // [M, k]
+  const float* weights; // [M, k]
+  uint16_t* slots;      // [M*k, H] bf16
+  uint16_t* combined;   // [M, H] bf16
+  uint16_t* shared_out; // [M, H] bf16, written by the dense units (or nullptr)
+  int M, k, lb, lc;
+  int all_local;        // lb == 0 and lc == experts: every token has k local picks
+};
+
 // One GEMM launch: the dense problem's units (if any) come first in the grid,
 // then the routed problem's.
 struct GemmArgs {
@@ -133,6 +150,7 @@ struct GemmArgs {
   int units0;           // work units of p[0]; 0 when there is none
   int pass_routes;      // MFMA path: routes staged per pass (<= 16)
   int stream_wgs;       // FP4 kernel: resident workgroups (stream_map)
+  CombineFuse cf;       // K-in-workgroup GEMM2 only
 };
 
 // FP4 GEMM: a stream of (job, tile, step) items split evenly over the

@@ -77,6 +77,13 @@ extern "C" {
 #define MOE_GEMM_MFMA 3         /* v_mfma_f32_16x16x32_f16, K split among the waves of a workgroup */
 #define MOE_GEMM_FP4 4          /* the MOE_WEIGHTS_NVFP4 kernel (reported by moe_decode_plan; gemm_path stays AUTO) */
 
+/* Launch shapes of run(). Every shape gives bit-identical results. */
+#define MOE_LAUNCH_AUTO 0             /* the shape measured fastest: MOE_LAUNCH_SEPARATE */
+#define MOE_LAUNCH_SEPARATE 1         /* each step a launch of its own (five launches) */
+#define MOE_LAUNCH_COMBINE_IN_GEMM2 2 /* MOE_GEMM_MFMA only: the combine inside the GEMM2 launch
+                                         (the workgroup that completes a token's column tile
+                                         combines it); other paths run MOE_LAUNCH_SEPARATE */
+
 /* Limits of this implementation. */
 #define MOE_DECODE_MAX_EXPERTS 1024
 #define MOE_DECODE_MAX_TOP_K 32
@@ -156,6 +163,9 @@ typedef struct moe_decode_config {
   int32_t weight_format;
   int32_t local_begin;
   int32_t local_experts;
+
+  /* Launch shape (MOE_LAUNCH_*). */
+  int32_t launch_mode;
 } moe_decode_config;
 
 typedef struct moe_decode_handle* moe_decode_t;
@@ -206,7 +216,8 @@ const char* moe_decode_error_string(int code);
  * out[10] = its partial-sum slices, out[11] / out[12] = blocks per split or
  * part, out[13] / out[14] = its work units in the GEMM1 / GEMM2 launches.
  * With n >= 17: out[15] / out[16] = K parts per workgroup in GEMM1 / GEMM2
- * (1 on the split-K paths). On MOE_GEMM_FP4: out[1] / out[2] = the most
+ * (1 on the split-K paths). With n >= 18: out[17] = kernel launches of run()
+ * (5, or 4 when the combine runs inside the GEMM2 launch). On MOE_GEMM_FP4: out[1] / out[2] = the most
  * partial slots a 64-row tile can have, out[3] / out[4] = 128-K blocks of
  * the whole K, out[5] / out[6] = launched workgroups (the resident ones, or
  * one per route when there are more routes). n is the capacity of out
@@ -243,8 +254,9 @@ int moe_decode_debug_stage(moe_decode_t h, int32_t stage, void* dst, size_t byte
  * launches (enable != 0; not for use under graph capture). After a run has
  * completed, moe_decode_last_timing writes the milliseconds of each launch in
  * order: route+quant, GEMM1, SwiGLU+requant, GEMM2, combine (the shared
- * expert, when run, is part of the last four). n is the capacity of ms
- * (>= 5). */
+ * expert, when run, is part of the last four; when the combine runs inside
+ * the GEMM2 launch, its time is GEMM2's and the last entry is 0). n is the
+ * capacity of ms (>= 5). */
 int moe_decode_set_timing(moe_decode_t h, int32_t enable);
 int moe_decode_last_timing(moe_decode_t h, float* ms, int32_t n);
 
