@@ -283,13 +283,14 @@ class MoeDecode:
         return (ids >= self.local_begin) & (ids < self.local_begin + self.local_experts)
 
     def plan(self, M: int) -> dict:
-        buf = (ctypes.c_int32 * 18)()
-        rc = lib().moe_decode_plan(self._h, M, buf, 18)
+        buf = (ctypes.c_int32 * 20)()
+        rc = lib().moe_decode_plan(self._h, M, buf, 20)
         if rc != OK:
             raise MoeDecodeError(rc, "moe_decode_plan")
         keys = ("path", "splits1", "splits2", "ks1", "ks2", "grid1", "grid2", "rows1", "rows2",
                 "shared_splits1", "shared_splits2", "shared_ks1", "shared_ks2",
-                "shared_units1", "shared_units2", "kparts1", "kparts2", "launches")
+                "shared_units1", "shared_units2", "kparts1", "kparts2", "launches",
+                "persist1", "persist2")
         return dict(zip(keys, list(buf)))
 
     def stage(self, name: str, dst: torch.Tensor, stream=None) -> torch.Tensor:

@@ -25,6 +25,12 @@ constexpr int kDenseTargetUnits = 256;  // units of the shared expert per GEMM l
 constexpr int kWgTargetUnits = 4096;    // K-in-workgroup path: units to aim for (16 per CU)
 constexpr int kWgMinPartBlocks = 14;    // shortest per-wave weight stream worth a K part (128-K blocks)
 constexpr int kBadFlagWord = 32;        // word of the control region used by create
+// Most tokens for the persistent K-in-workgroup GEMMs. Measured on MI355X
+// (DeepSeek-V3 shapes, layer µs, one workgroup per unit -> persistent):
+// M=1 83.8 -> 81.3, M=2 137.6 -> 132.2, M=4 209.4 -> 207.5, M=8 313.9 ->
+// 311.3, M=16 441.2 -> 446.4 (units no longer divide evenly over the
+// resident workgroups, and a static share cannot even them out).
+constexpr int kPersistMaxTokens = 8;
 
 // Workspace regions (the debug stages use the same numbering).
 enum {
@@ -46,6 +52,9 @@ struct Plan {
   // K-in-workgroup path: K parts per row group (routed, shared)
   int kp1, kp2, skp1, skp2;
   bool fuse_combine;  // the combine runs inside the GEMM2 launch
+  // K-in-workgroup path: resident workgroups of the persistent GEMM1 / GEMM2
+  // launches (0: one workgroup per unit)
+  int persist1, persist2;
 };
 
 struct Region {
@@ -68,6 +77,7 @@ struct moe_decode_handle {
   const float* s13;
   const float* s2;
   int fp4_wgs1, fp4_wgs2;  // FP4 form: resident workgroups of each GEMM launch
+  int wgp_wgs1, wgp_wgs2;  // FP8 form: resident workgroups of the persistent GEMM kernels
   // FP4 form: the weight scales reordered for the GEMM kernel (owned)
   uint8_t* fp4_s13;
   uint8_t* fp4_s2;
@@ -139,9 +149,10 @@ int choose_kparts(int experts, int N, int nkb, int forced) {
 
 int local_count(const moe_decode_config& c) { return c.local_experts ? c.local_experts : c.experts; }
 
-// fp4_wgs1/2: the FP4 GEMM launches' resident workgroups (unused otherwise;
-// 0 while only sizing the workspace).
-Plan make_plan(const moe_decode_config& c, int M, int fp4_wgs1 = 0, int fp4_wgs2 = 0) {
+// fp4_wgs1/2: the FP4 GEMM launches' resident workgroups, wgp_wgs1/2 those of
+// the persistent FP8 GEMMs (0 while only sizing the workspace).
+Plan make_plan(const moe_decode_config& c, int M, int fp4_wgs1 = 0, int fp4_wgs2 = 0, int wgp_wgs1 = 0,
+               int wgp_wgs2 = 0) {
   Plan p{};
   const int R = M * c.top_k;
   p.umax = std::min(local_count(c), R);
@@ -184,6 +195,15 @@ Plan make_plan(const moe_decode_config& c, int M, int fp4_wgs1 = 0, int fp4_wgs2
     p.grid1 = p.umax * (2 * c.inter / p.tpw1) + p.sunits1;
     p.grid2 = p.umax * (c.hidden / p.tpw2) + p.sunits2;
     p.fuse_combine = c.launch_mode == MOE_LAUNCH_COMBINE_IN_GEMM2;
+    // Persistent workgroups where the kernel's conditions hold (an expert has
+    // at most one route per token, so at most M routes) and up to
+    // kPersistMaxTokens tokens; MOE_GEMM_MFMA asked for by name keeps one
+    // workgroup per unit.
+    if (c.gemm_path == MOE_GEMM_AUTO && c.shared_inter == 0 && M <= kPersistMaxTokens) {
+      if (wgp_wgs1 > 0 && gemm_wgp_fits(c.hidden / kTile, p.kp1, M)) p.persist1 = std::min(p.grid1, wgp_wgs1);
+      if (wgp_wgs2 > 0 && !p.fuse_combine && gemm_wgp_fits(c.inter / kTile, p.kp2, M))
+        p.persist2 = std::min(p.grid2, wgp_wgs2);
+    }
     return p;
   }
   // MFMA costs the same per weight byte for any number of routes of an
@@ -393,6 +413,10 @@ int moe_decode_create(const moe_decode_config* cfg, moe_decode_t* out) {
       return MOE_DECODE_ERR_HIP;
     }
   }
+  if (!fp4) {  // 0 (one workgroup per unit) if the query fails
+    h->wgp_wgs1 = gemm_wgp_resident_wgs(c.hidden / kTile);
+    h->wgp_wgs2 = gemm_wgp_resident_wgs(c.inter / kTile);
+  }
   if (fp4) {
     h->fp4_wgs1 = gemm_fp4_resident_wgs(c.hidden);
     h->fp4_wgs2 = gemm_fp4_resident_wgs(c.inter);
@@ -425,7 +449,7 @@ int moe_decode_create(const moe_decode_config* cfg, moe_decode_t* out) {
     }
   }
   if (std::getenv("MOE_DECODE_DEBUG")) {
-    const Plan p = make_plan(c, c.max_tokens, h->fp4_wgs1, h->fp4_wgs2);
+    const Plan p = make_plan(c, c.max_tokens, h->fp4_wgs1, h->fp4_wgs2, h->wgp_wgs1, h->wgp_wgs2);
     std::fprintf(stderr,
                  "moe_decode: H=%d I=%d E=%d k=%d max_tokens=%d workspace=%zu B; at M=%d: "
                  "path=%d splits1=%d (ks %d) splits2=%d (ks %d) grid1=%d grid2=%d\n",
@@ -455,7 +479,7 @@ void moe_decode_destroy(moe_decode_t h) {
 int moe_decode_plan(moe_decode_t h, int32_t M, int32_t* out, int32_t n) {
   if (!h || !out || n < 9 || M < 1) return MOE_DECODE_ERR_INVALID_ARG;
   if (M > h->cfg.max_tokens) return MOE_DECODE_ERR_TOO_MANY_TOKENS;
-  const Plan p = make_plan(h->cfg, M, h->fp4_wgs1, h->fp4_wgs2);
+  const Plan p = make_plan(h->cfg, M, h->fp4_wgs1, h->fp4_wgs2, h->wgp_wgs1, h->wgp_wgs2);
   out[0] = p.path;
   out[1] = p.s1;
   out[2] = p.s2;
@@ -479,6 +503,10 @@ int moe_decode_plan(moe_decode_t h, int32_t M, int32_t* out, int32_t n) {
     out[16] = p.path == MOE_GEMM_MFMA ? p.kp2 : 1;
   }
   if (n >= 18) out[17] = p.fuse_combine ? 4 : 5;
+  if (n >= 20) {
+    out[18] = p.persist1;
+    out[19] = p.persist2;
+  }
   return MOE_DECODE_OK;
 }
 
@@ -500,7 +528,7 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
 
   const moe_decode_config& c = h->cfg;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const Plan p = make_plan(c, M, h->fp4_wgs1, h->fp4_wgs2);
+  const Plan p = make_plan(c, M, h->fp4_wgs1, h->fp4_wgs2, h->wgp_wgs1, h->wgp_wgs2);
   const int R = M * c.top_k;
   const bool fp4 = c.weight_format == MOE_WEIGHTS_NVFP4;
   const int lb = c.local_begin, lc = local_count(c);
@@ -626,9 +654,11 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
     return q;
   };
   auto launch_gemm = [&](const GemmArgs& g, int role, int grid) {
+    const int persist = role == 1 ? p.persist1 : p.persist2;
     switch (p.path) {
       case MOE_GEMM_FP4: return launch_gemm_fp4(g, role, grid, s);
-      case MOE_GEMM_MFMA: return launch_gemm_wg(g, role, grid, s);
+      case MOE_GEMM_MFMA:
+        return persist ? launch_gemm_wgp(g, role, persist, s) : launch_gemm_wg(g, role, grid, s);
       case MOE_GEMM_MFMA_SPLITK: return launch_gemm_mfma(g, role, grid, s);
       default: return launch_gemm_valu(g, role, grid, s);
     }

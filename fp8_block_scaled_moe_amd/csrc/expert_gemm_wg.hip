@@ -141,21 +141,29 @@ __global__ __launch_bounds__(kThreads) void gemm_wg_kernel(GemmArgs args) {
   float* xsl = wsl + 4 * a.nkb;                                       // [nkb][16]
   int* rts = reinterpret_cast<int*>(xsl + a.nkb * kRoutesPerPass);    // [16]
 
-  const uint8_t* pw = a.w + ((size_t)e * a.N + row0 + rg) * a.K + (size_t)kb0 * kTile + ch * 16;
-  const size_t half_step = (size_t)8 * a.K;
+  // addresses: a uniform base plus a 32-bit offset per lane
+  const uint8_t* pw = a.w + ((size_t)e * a.N + tile * rows_wg) * a.K;
+  const uint32_t w_lane = (uint32_t)((rgrp * 16 + rg) * a.K + kb0 * kTile + ch * 16);
+  const uint32_t half_step = (uint32_t)(8 * a.K);
   u32x4_t wa[kDepth], wb[kDepth], xa[kDepth], xb[kDepth];
   auto load_w = [&](int q, int st) {
-    const uint8_t* p = pw + (size_t)st * kTile;
-    wa[q] = load_stream16(p);
-    wb[q] = load_stream16(p + half_step);
+    const uint32_t o = w_lane + (uint32_t)st * kTile;
+    wa[q] = load_stream16(pw + o);
+    wb[q] = load_stream16(pw + (o + half_step));
   };
 
   for (int c0 = 0; c0 < cnt; c0 += kRoutesPerPass) {
     const int nr = min(kRoutesPerPass, cnt - c0);
     if (c0) __syncthreads();  // the previous pass is done with rts, xsl and red
 #pragma unroll
-    for (int q = 0; q < kDepth; ++q)
-      if (q < nsteps) load_w(q, q);
+    for (int q = 0; q < kDepth; ++q) {  // unconditional (see step): past the last step, row 0 of aq
+      if (q < nsteps) {
+        load_w(q, q);
+      } else {
+        wa[q] = load_stream16(a.aq);
+        wb[q] = load_stream16(a.aq + 64);
+      }
+    }
     if (tid < nr) rts[tid] = a.dense ? c0 + tid : a.b.routes[off + c0 + tid];
     if (c0 == 0) {
       // weight scales of the workgroup's row groups: one 128-row scale block each
@@ -169,15 +177,14 @@ __global__ __launch_bounds__(kThreads) void gemm_wg_kernel(GemmArgs args) {
 
     const bool live = col < nr;
     const int xrow = rts[live ? col : 0] / a.act_div;  // lanes past the routes repeat route 0
-    const uint8_t* px = a.aq + (size_t)xrow * a.K + (size_t)kb0 * kTile + g * 16;
+    const uint32_t px = (uint32_t)(xrow * a.K + kb0 * kTile + g * 16);
     auto load_x = [&](int q, int st) {
-      const uint8_t* p = px + (size_t)st * kTile;
-      xa[q] = *reinterpret_cast<const u32x4_t*>(p);
-      xb[q] = *reinterpret_cast<const u32x4_t*>(p + 64);
+      const uint32_t o = px + (uint32_t)st * kTile;
+      xa[q] = *reinterpret_cast<const u32x4_t*>(a.aq + o);
+      xb[q] = *reinterpret_cast<const u32x4_t*>(a.aq + (o + 64));
     };
 #pragma unroll
-    for (int q = 0; q < kDepth; ++q)
-      if (q < nsteps) load_x(q, q);
+    for (int q = 0; q < kDepth; ++q) load_x(q, q < nsteps ? q : 0);
     for (int i = tid; i < nr * a.nkb; i += kThreads) {
       const int r = i / a.nkb, b = i - r * a.nkb;
       xsl[b * kRoutesPerPass + r] = a.as[(size_t)(rts[r] / a.act_div) * a.nkb + b];
@@ -187,31 +194,42 @@ __global__ __launch_bounds__(kThreads) void gemm_wg_kernel(GemmArgs args) {
     const float* wsr = wsl + rgrp * a.nkb + kb0;
     const float* xsr = xsl + kb0 * kRoutesPerPass + (live ? col : 0);
     float4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int st0 = 0; st0 < nsteps; st0 += kDepth) {
+    // One step. Its loads are issued on every step (branches around them
+    // make the compiler wait for every load in flight): step st + kDepth, or
+    // near the end this lane's activations of step st again (an L2 hit, never
+    // used). Each register set is refilled once its data is consumed
+    // (weights after the LDS write, activations after the MFMA), so no copy
+    // of an in-flight load ties the wait to the newest request.
+    auto step = [&](int st, int q) {
+      // steps stay in order: the scheduler interleaving two steps' MFMAs
+      // needs both steps' activations at once, i.e. a wait for every load
+      __builtin_amdgcn_sched_barrier(0);
+      *reinterpret_cast<u32x4_t*>(tile_lds + rg * kTileStride + ch * 16) = wa[q];
+      *reinterpret_cast<u32x4_t*>(tile_lds + (rg + 8) * kTileStride + ch * 16) = wb[q];
+      const bool ahead = st + kDepth < nsteps;
+      const int lst = ahead ? st + kDepth : st;
+      const uint8_t* wbase = ahead ? pw : a.aq;
+      const uint32_t o = (ahead ? w_lane : px) + (uint32_t)lst * kTile;
+      wa[q] = load_stream16(wbase + o);
+      wb[q] = load_stream16(wbase + (o + (ahead ? half_step : 64u)));
+      wave_lds_fence();
+      const u32x4_t wlo = *reinterpret_cast<const u32x4_t*>(tile_lds + col * kTileStride + g * 16);
+      const u32x4_t whi = *reinterpret_cast<const u32x4_t*>(tile_lds + col * kTileStride + 64 + g * 16);
+      wave_lds_fence();
+      const float4_t p = mfma_block(wlo, whi, xa[q], xb[q]);
+      load_x(q, lst);
+      const float s = wsr[st] * xsr[st * kRoutesPerPass];
+      acc[0] = fmaf(p[0], s, acc[0]);
+      acc[1] = fmaf(p[1], s, acc[1]);
+      acc[2] = fmaf(p[2], s, acc[2]);
+      acc[3] = fmaf(p[3], s, acc[3]);
+    };
+    int st0 = 0;
+    for (; st0 + kDepth <= nsteps; st0 += kDepth) {
 #pragma unroll
-      for (int q = 0; q < kDepth; ++q) {
-        const int st = st0 + q;
-        if (st < nsteps) {
-          *reinterpret_cast<u32x4_t*>(tile_lds + rg * kTileStride + ch * 16) = wa[q];
-          *reinterpret_cast<u32x4_t*>(tile_lds + (rg + 8) * kTileStride + ch * 16) = wb[q];
-          const u32x4_t xlo = xa[q], xhi = xb[q];
-          if (st + kDepth < nsteps) {
-            load_w(q, st + kDepth);
-            load_x(q, st + kDepth);
-          }
-          wave_lds_fence();
-          const u32x4_t wlo = *reinterpret_cast<const u32x4_t*>(tile_lds + col * kTileStride + g * 16);
-          const u32x4_t whi = *reinterpret_cast<const u32x4_t*>(tile_lds + col * kTileStride + 64 + g * 16);
-          wave_lds_fence();
-          const float4_t p = mfma_block(wlo, whi, xlo, xhi);
-          const float s = wsr[st] * xsr[st * kRoutesPerPass];
-          acc[0] = fmaf(p[0], s, acc[0]);
-          acc[1] = fmaf(p[1], s, acc[1]);
-          acc[2] = fmaf(p[2], s, acc[2]);
-          acc[3] = fmaf(p[3], s, acc[3]);
-        }
-      }
+      for (int q = 0; q < kDepth; ++q) step(st0 + q, q);
     }
+    for (int q = 0; st0 + q < nsteps; ++q) step(st0 + q, q);  // fewer than kDepth steps left
 
     if (kparts > 1) {  // K parts of a row group added in a fixed order: part 0, 1, ...
       *reinterpret_cast<float4_t*>(red + (wave * kWave + lane) * 4) = acc;
@@ -268,11 +286,245 @@ __global__ __launch_bounds__(kThreads) void gemm_wg_kernel(GemmArgs args) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Persistent form of the same kernel for the routed problem. The grid is the
+// number of workgroups resident at once (G), and workgroup b takes units b,
+// b + G, b + 2G, ... in turn. Units, their rows, K parts and every sum are as
+// above, so the outputs are bit-identical; what changes is the weight stream.
+// A workgroup that runs one unit spends the start of it with only its first
+// kDepth weight steps in flight (routes and scales are staged first), and the
+// slot stands empty between workgroups. Here the next unit's routes and
+// scales are fetched into registers while the current unit streams, and the
+// next unit's first kDepth steps of weights and activations are requested in
+// the slots the current unit no longer refills, so each wave's stream runs on
+// from one unit into the next. A read probe of this shape (64-row units of
+// 3584 B rows) streamed 1 GiB at 6.78 TB/s as 1024 persistent workgroups and
+// 6.42 TB/s as one workgroup per unit.
+//
+// Conditions, checked by the host: no dense problem, at most 16 routes per
+// expert (one pass), K blocks a multiple of kparts * kDepth (every wave has
+// the same even number of steps) and at most kMaxPersistBlocks of them.
+constexpr int kMaxPersistBlocks = 64;
+constexpr int kSxPerThread = kMaxPersistBlocks * kRoutesPerPass / kThreads;  // activation scales staged per thread
+
+struct UnitRef {
+  int e, cnt, off, tile;
+};
+
+template <int kRole>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void gemm_wgp_kernel(GemmArgs args) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const GemmProblem& a = args.p[1];
+  const int kparts = a.kparts;
+  const int rows_wg = kRowsPerWg / kparts;
+  const int per_expert = a.N / rows_wg;
+  const int total = a.b.ctrl[1] * per_expert;
+  const int G = gridDim.x;
+  int u = blockIdx.x;
+  if (u >= total) return;  // more slots than units: the whole workgroup exits
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int rgrp = wave / kparts, kp = wave - rgrp * kparts;
+  const int nkb = a.nkb;
+  const int nsteps = nkb / kparts;  // the same for every wave (checked by the host)
+  const int kb0 = kp * nsteps;
+  const int rg = lane >> 3, ch = lane & 7;   // load layout
+  const int col = lane & 15, g = lane >> 4;  // MFMA layout
+  const int nsw = (4 / kparts) * nkb;        // weight scales of a unit (row groups x blocks)
+  const int stage_floats = 4 * nkb + nkb * kRoutesPerPass;
+
+  uint8_t* tile_lds = smem + wave * kTileBytes;                 // [4][kTileBytes]
+  float* red = reinterpret_cast<float*>(smem + 4 * kTileBytes);  // [4 waves][64 lanes][4]
+  float* stage = red + kRedFloats;                               // [2][wsl 4 * nkb | xsl nkb * 16]
+
+  auto unit_ref = [&](int v) {
+    UnitRef x;
+    const int ui = v / per_expert;
+    x.tile = v - ui * per_expert;
+    x.e = a.b.uexp[ui];
+    x.cnt = a.b.ucnt[ui];
+    x.off = a.b.uoff[ui];
+    return x;
+  };
+  // Addresses as a uniform base per unit plus a 32-bit offset per lane (a
+  // lane's offset into its unit's weights is the same for every unit).
+  auto weights_of = [&](const UnitRef& x) { return a.w + ((size_t)x.e * a.N + x.tile * rows_wg) * a.K; };
+  const uint32_t w_lane = (uint32_t)((rgrp * 16 + rg) * a.K + kb0 * kTile + ch * 16);
+  const uint32_t half_step = (uint32_t)(8 * a.K);
+
+  // Per-thread staging registers: one weight scale (thread < nsw), and the
+  // activation scales of route col (blocks tid / 16 + 16 j).
+  float sw = 0.f, sx[kSxPerThread];
+  int rt_next = 0, xrow_next = 0;
+  auto fetch_routes = [&](const UnitRef& x) {  // first level: the route of this lane's column
+    rt_next = a.b.routes[x.off + (col < x.cnt ? col : 0)];  // lanes past the routes repeat route 0
+    xrow_next = rt_next / a.act_div;
+    if (tid < nsw) {
+      const int r = tid / nkb, b = tid - r * nkb;
+      sw = a.ws[((size_t)x.e * (a.N / kTile) + (x.tile * rows_wg + r * 16) / kTile) * nkb + b];
+    }
+  };
+  auto fetch_scales = [&](const UnitRef& x) {  // second level: activation scales of those routes
+#pragma unroll
+    for (int j = 0; j < kSxPerThread; ++j) {
+      const int b = tid / kRoutesPerPass + (kThreads / kRoutesPerPass) * j;
+      sx[j] = col < x.cnt && b < nkb ? a.as[(size_t)xrow_next * nkb + b] : 0.f;
+    }
+  };
+  auto commit = [&](float* st, const UnitRef& x) {
+    if (tid < nsw) st[tid] = sw;
+#pragma unroll
+    for (int j = 0; j < kSxPerThread; ++j) {
+      const int b = tid / kRoutesPerPass + (kThreads / kRoutesPerPass) * j;
+      if (col < x.cnt && b < nkb) st[4 * nkb + b * kRoutesPerPass + col] = sx[j];
+    }
+  };
+
+  u32x4_t wa[kDepth], wb[kDepth], xa[kDepth], xb[kDepth];
+  auto load_w = [&](const uint8_t* pw, int q, int st) {
+    const uint32_t o = w_lane + (uint32_t)st * kTile;
+    wa[q] = load_stream16(pw + o);
+    wb[q] = load_stream16(pw + (o + half_step));
+  };
+  auto x_of = [&](int xrow) { return (uint32_t)(xrow * a.K + kb0 * kTile + g * 16); };
+  auto load_x = [&](uint32_t px, int q, int st) {
+    const uint32_t o = px + (uint32_t)st * kTile;
+    xa[q] = *reinterpret_cast<const u32x4_t*>(a.aq + o);
+    xb[q] = *reinterpret_cast<const u32x4_t*>(a.aq + (o + 64));
+  };
+
+  // The first unit: requests, then staging, as the one-unit kernel does.
+  UnitRef cur = unit_ref(u);
+  const uint8_t* pw = weights_of(cur);
+#pragma unroll
+  for (int q = 0; q < kDepth; ++q) load_w(pw, q, q);
+  fetch_routes(cur);
+  int rt = rt_next;
+  uint32_t px = x_of(xrow_next);
+#pragma unroll
+  for (int q = 0; q < kDepth; ++q) load_x(px, q, q);
+  fetch_scales(cur);
+  commit(stage, cur);
+  __syncthreads();
+
+  for (int buf = 0;; buf ^= 1) {
+    const int nu = u + G;
+    const bool more = nu < total;
+    UnitRef nx = cur;
+    if (more) {
+      nx = unit_ref(nu);
+      fetch_routes(nx);
+    }
+    const uint8_t* pwn = weights_of(nx);
+    const uint32_t pxn = x_of(xrow_next);
+    if (more) fetch_scales(nx);
+
+    const float* st_cur = stage + buf * stage_floats;
+    const float* wsr = st_cur + rgrp * nkb + kb0;
+    const bool live = col < cur.cnt;
+    const float* xsr = st_cur + 4 * nkb + kb0 * kRoutesPerPass + (live ? col : 0);
+    float4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int st0 = 0; st0 < nsteps; st0 += kDepth) {
+#pragma unroll
+      for (int q = 0; q < kDepth; ++q) {
+        const int st = st0 + q;
+        *reinterpret_cast<u32x4_t*>(tile_lds + rg * kTileStride + ch * 16) = wa[q];
+        *reinterpret_cast<u32x4_t*>(tile_lds + (rg + 8) * kTileStride + ch * 16) = wb[q];
+        // One load path for every step (separate paths cost a full drain of
+        // the loads in flight): this unit's step st + kDepth, else the next
+        // unit's step q (nsteps is a multiple of kDepth), else, after the last
+        // unit, this lane's activations of step st again in both register
+        // sets (L2 hits; never used; weights, read nontemporally, would come
+        // from HBM again). Each register set is refilled only once its data
+        // is consumed (weights after the LDS write, activations after the
+        // MFMA), so no copy of an in-flight load ties the wait to the newest
+        // request.
+        const bool ahead = st + kDepth < nsteps;
+        const bool idle = !ahead && !more;
+        const uint32_t xsrc = ahead || !more ? px : pxn;
+        const int lst = ahead ? st + kDepth : (more ? q : st);
+        const uint8_t* wbase = idle ? a.aq : (ahead ? pw : pwn);
+        const uint32_t wo = (idle ? px : w_lane) + (uint32_t)lst * kTile;
+        wa[q] = load_stream16(wbase + wo);
+        wb[q] = load_stream16(wbase + (wo + (idle ? 64u : half_step)));
+        wave_lds_fence();
+        const u32x4_t wlo = *reinterpret_cast<const u32x4_t*>(tile_lds + col * kTileStride + g * 16);
+        const u32x4_t whi = *reinterpret_cast<const u32x4_t*>(tile_lds + col * kTileStride + 64 + g * 16);
+        wave_lds_fence();
+        const float4_t p = mfma_block(wlo, whi, xa[q], xb[q]);
+        load_x(xsrc, q, lst);
+        const float s = wsr[st] * xsr[st * kRoutesPerPass];
+        acc[0] = fmaf(p[0], s, acc[0]);
+        acc[1] = fmaf(p[1], s, acc[1]);
+        acc[2] = fmaf(p[2], s, acc[2]);
+        acc[3] = fmaf(p[3], s, acc[3]);
+      }
+    }
+
+    if (kparts > 1) {  // K parts of a row group added in a fixed order: part 0, 1, ...
+      *reinterpret_cast<float4_t*>(red + (wave * kWave + lane) * 4) = acc;
+      __syncthreads();
+      if (kp == 0) {
+        for (int j = 1; j < kparts; ++j) {
+          const float4_t o = *reinterpret_cast<const float4_t*>(red + ((wave + j) * kWave + lane) * 4);
+          acc[0] += o[0];
+          acc[1] += o[1];
+          acc[2] += o[2];
+          acc[3] += o[3];
+        }
+      }
+    }
+    if (kp == 0 && live)
+      *reinterpret_cast<float4_t*>(a.part + (size_t)rt * a.N + cur.tile * rows_wg + rgrp * 16 + 4 * g) = acc;
+    if (!more) break;
+    commit(stage + (buf ^ 1) * stage_floats, nx);
+    __syncthreads();  // the next unit's scales are in place; this unit is done with red and its stage
+    u = nu;
+    cur = nx;
+    pw = pwn;
+    px = pxn;
+    rt = rt_next;
+  }
+}
+
 }  // namespace
 
 size_t gemm_wg_lds_bytes(int nkb) {
   return 4 * (size_t)kTileBytes + kRedFloats * 4 + (size_t)4 * nkb * 4 + (size_t)nkb * kRoutesPerPass * 4 +
          kRoutesPerPass * 4;
+}
+
+size_t gemm_wgp_lds_bytes(int nkb) {
+  return 4 * (size_t)kTileBytes + kRedFloats * 4 + (size_t)2 * (4 * nkb + nkb * kRoutesPerPass) * 4;
+}
+
+bool gemm_wgp_fits(int nkb, int kparts, int max_routes) {
+  return max_routes <= kRoutesPerPass && nkb <= kMaxPersistBlocks && kparts >= 1 && 4 % kparts == 0 &&
+         nkb % (kparts * kDepth) == 0;
+}
+
+int gemm_wgp_resident_wgs(int nkb) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(gemm_wgp_kernel<1>),
+                                                   kThreads, gemm_wgp_lds_bytes(nkb)) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return cus * per_cu;
+}
+
+hipError_t launch_gemm_wgp(const GemmArgs& a, int role, int grid, hipStream_t s) {
+  const GemmProblem& p = a.p[1];
+  if (a.units0 || a.cf.on || grid < 1 || !gemm_wgp_fits(p.nkb, p.kparts, kRoutesPerPass))
+    return hipErrorInvalidValue;
+  const size_t lds = gemm_wgp_lds_bytes(p.nkb);
+  if (role == 1)
+    hipLaunchKernelGGL(gemm_wgp_kernel<1>, dim3(grid), dim3(kThreads), lds, s, a);
+  else
+    hipLaunchKernelGGL(gemm_wgp_kernel<2>, dim3(grid), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_wg(const GemmArgs& a, int role, int grid, hipStream_t s) {

@@ -189,6 +189,13 @@ size_t gemm_mfma_lds_bytes(int pass_routes, int ks);
 // writes one FP32 value per (route, row) to part[0].
 hipError_t launch_gemm_wg(const GemmArgs& a, int role, int grid, hipStream_t s);
 size_t gemm_wg_lds_bytes(int nkb);
+// Its persistent form (routed problem only): `grid` workgroups take the units
+// in turn. gemm_wgp_fits: nkb K blocks, kparts K parts and at most max_routes
+// routes per expert are within its conditions; resident_wgs is 0 on error.
+hipError_t launch_gemm_wgp(const GemmArgs& a, int role, int grid, hipStream_t s);
+size_t gemm_wgp_lds_bytes(int nkb);
+bool gemm_wgp_fits(int nkb, int kparts, int max_routes);
+int gemm_wgp_resident_wgs(int nkb);
 // FP32 [n/128, k/128] scales from packed UE8M0 words int32 [n, ceil(k/512)];
 // *bad is set nonzero when the rows of a 128-row block disagree.
 hipError_t launch_unpack_ue8m0(const int32_t* packed, int n, int k, float* out, int32_t* bad,

@@ -71,10 +71,15 @@ extern "C" {
 /* GEMM kernels. All widen FP8 exactly to F16 and add exact products in FP32.
  * The split-K paths divide K among workgroups and sum FP32 partials in the
  * next kernel; MOE_GEMM_MFMA sums all of K inside one workgroup. */
-#define MOE_GEMM_AUTO 0         /* MOE_GEMM_MFMA */
+#define MOE_GEMM_AUTO 0         /* MOE_GEMM_MFMA, with persistent workgroups where they apply */
 #define MOE_GEMM_VALU_SPLITK 1  /* F16 dot2, split-K over workgroups */
 #define MOE_GEMM_MFMA_SPLITK 2  /* v_mfma_f32_16x16x32_f16 (16 routes at once), split-K over workgroups */
-#define MOE_GEMM_MFMA 3         /* v_mfma_f32_16x16x32_f16, K split among the waves of a workgroup */
+#define MOE_GEMM_MFMA 3         /* v_mfma_f32_16x16x32_f16, K split among the waves of a workgroup;
+                                   asked for by name: one workgroup per unit. Under AUTO, a GEMM
+                                   without a shared expert, with at most 8 tokens and with
+                                   K / 128 a multiple of 2 x its K parts (at most 64 blocks) runs
+                                   on resident workgroups that take the units in turn
+                                   (bit-identical results) */
 #define MOE_GEMM_FP4 4          /* the MOE_WEIGHTS_NVFP4 kernel (reported by moe_decode_plan; gemm_path stays AUTO) */
 
 /* Launch shapes of run(). Every shape gives bit-identical results. */
@@ -217,7 +222,9 @@ const char* moe_decode_error_string(int code);
  * part, out[13] / out[14] = its work units in the GEMM1 / GEMM2 launches.
  * With n >= 17: out[15] / out[16] = K parts per workgroup in GEMM1 / GEMM2
  * (1 on the split-K paths). With n >= 18: out[17] = kernel launches of run()
- * (5, or 4 when the combine runs inside the GEMM2 launch). On MOE_GEMM_FP4: out[1] / out[2] = the most
+ * (5, or 4 when the combine runs inside the GEMM2 launch). With n >= 20:
+ * out[18] / out[19] = workgroups of the persistent GEMM1 / GEMM2 launch on
+ * MOE_GEMM_MFMA (0: one workgroup per unit). On MOE_GEMM_FP4: out[1] / out[2] = the most
  * partial slots a 64-row tile can have, out[3] / out[4] = 128-K blocks of
  * the whole K, out[5] / out[6] = launched workgroups (the resident ones, or
  * one per route when there are more routes). n is the capacity of out

@@ -1,0 +1,113 @@
+"""The persistent form of the K-in-workgroup GEMMs (MOE_GEMM_AUTO, where it
+applies) against one workgroup per unit (MOE_GEMM_MFMA by name).
+
+Both forms cut the work into the same units (expert, 16-64 weight rows, all
+of K) and add every unit's products, K parts and scale factors in the same
+order; the persistent form only changes which workgroup takes a unit and
+when its loads are requested. So every output and every staged value must be
+bit-identical between the two, and the one-unit form is held to the oracle by
+test_gpu_parity.py. Covered: K parts 1, 2 and 4 in either GEMM, several units
+per workgroup (fewer workgroups than units), one routed expert, eight routes
+on one expert, the full DeepSeek-V3-shaped layer at 1 and 4 tokens, and calls
+of different token counts on one handle. The persistent form is planned for
+at most 8 tokens.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from fp8_block_scaled_moe_amd import MoeDecode
+from tests.helpers import assert_rows_close, host, oracle_layer
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def make(inp, path, **kw):
+    s = inp.shape
+    return MoeDecode(inp.w13, inp.w13_scale, inp.w2, inp.w2_scale, top_k=s.top_k, limit=s.limit,
+                     routed_scale=s.routed_scale, max_tokens=kw.pop("max_tokens", s.M),
+                     logits_dtype=inp.logits.dtype, ue8m0_act=s.ue8m0_act, gemm_path=path, **kw)
+
+
+def run(moe, inp, M):
+    out = moe(inp.x[:M].contiguous(), inp.logits[:M].contiguous(), inp.bias)
+    torch.cuda.synchronize()
+    return out
+
+
+def staged(moe, M):
+    s = moe.top_k * M
+    p1 = moe.stage("part1", torch.empty(s * 2 * moe.inter, dtype=torch.float32, device=DEV))
+    p2 = moe.stage("part2", torch.empty(s * moe.hidden, dtype=torch.float32, device=DEV))
+    return p1, p2
+
+
+def compare(inp, M=None, want_persist=(True, True), **kw):
+    M = M or inp.shape.M
+    pers, one = make(inp, "auto", **kw), make(inp, "mfma", **kw)
+    plan = pers.plan(M)
+    assert (plan["persist1"] > 0, plan["persist2"] > 0) == tuple(want_persist), plan
+    assert one.plan(M)["persist1"] == 0 and one.plan(M)["persist2"] == 0
+    a, b = run(pers, inp, M), run(one, inp, M)
+    for name, x, y in zip(("slots", "ids", "weights", "combined"), a, b):
+        assert torch.equal(x, y), name
+    for name, x, y in zip(("part1", "part2"), staged(pers, M), staged(one, M)):
+        assert torch.equal(x, y), name
+    return a, plan
+
+
+@pytest.mark.parametrize("splits", [(0, 0), (1, 1), (2, 2), (4, 4)], ids=["auto", "kp1", "kp2", "kp4"])
+def test_persistent_equals_one_unit(splits):
+    shape = synth.CONFIGS["tiny"].with_(M=6, hidden=1024, inter=1024, experts=12, top_k=4)
+    inp = synth.make_inputs(shape, seed=51, device=DEV)
+    (slots, ids, weights, combined), plan = compare(inp, splits1=splits[0], splits2=splits[1])
+    ref = oracle_layer(inp)
+    assert np.array_equal(ids.cpu().numpy(), ref["ids"])
+    assert_rows_close(host(slots), ref["slots"], what="slots")
+    assert_rows_close(host(combined), ref["combined"], what="combined")
+
+
+def test_persistent_single_expert_eight_routes():
+    """Eight tokens all on expert 0 (the most routes the plan gives it)."""
+    shape = synth.CONFIGS["tiny"].with_(M=8, hidden=512, inter=512, experts=8, top_k=1)
+    inp = synth.make_inputs(shape, seed=52, device=DEV)
+    inp.bias[0] += 50.0
+    compare(inp)
+
+
+def test_persistent_not_taken_past_eight_tokens():
+    """Nine tokens: the one-unit kernel runs (and gives the same results)."""
+    shape = synth.CONFIGS["tiny"].with_(M=9, hidden=512, inter=512, experts=8, top_k=2)
+    inp = synth.make_inputs(shape, seed=53, device=DEV)
+    compare(inp, want_persist=(False, False))
+
+
+def test_persistent_odd_steps_fall_back():
+    """K / 128 = 3 blocks cannot give every wave an even number of steps."""
+    shape = synth.CONFIGS["tiny"].with_(M=3, hidden=384, inter=256, experts=6, top_k=2)
+    inp = synth.make_inputs(shape, seed=54, device=DEV)
+    compare(inp, want_persist=(False, True))
+
+
+def test_persistent_token_counts_on_one_handle():
+    shape = synth.CONFIGS["tiny"].with_(M=9, hidden=2048, inter=1024, experts=32, top_k=6)
+    inp = synth.make_inputs(shape, seed=55, device=DEV)
+    pers, one = make(inp, "auto"), make(inp, "mfma")
+    for M in (9, 1, 4, 8, 9):
+        for name, x, y in zip(("slots", "ids", "weights", "combined"), run(pers, inp, M), run(one, inp, M)):
+            assert torch.equal(x, y), (M, name)
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_persistent_dsv3(M):
+    """The DeepSeek-V3-shaped layer: thousands of units on the resident
+    workgroups."""
+    inp = synth.make_inputs(synth.CONFIGS["dsv3"], seed=0, device=DEV)
+    _, plan = compare(inp, M=M)
+    assert plan["persist1"] < plan["grid1"]  # several units per workgroup
