@@ -10,7 +10,7 @@
 // e4m3.
 //
 // Launch: one 1024-thread workgroup per 4 tokens; waves 0..3 (one per SIMD)
-// each route one token, then all 16 waves quantise. With one workgroup the
+// each route one token while waves 4..15 quantise the four tokens' x. With one workgroup the
 // routes are grouped by expert right away (by one wave when there are at most
 // 64 routes, else through LDS); with several, the last workgroup to arrive
 // (atomic counter, reset by that workgroup) does it.
@@ -137,13 +137,13 @@ __device__ void route_token_any(const RouteQuantArgs& a, int t, int lane, int* i
   else route_token<16>(a, t, lane, ids_l);
 }
 
-// All threads: the 128-blocks of tokens [t0, t0 + ntok), eight lanes per
-// block and sixteen values per lane; loads of up to four blocks per lane are
-// issued before any is used.
-__device__ void quant_tokens(const RouteQuantArgs& a, int t0, int ntok) {
-  constexpr int kGroups = kThreads / 8;
+// Threads tid0.. (tid0 a multiple of the wave size): the 128-blocks of tokens
+// [t0, t0 + ntok), eight lanes per block and sixteen values per lane; loads
+// of up to four blocks per lane are issued before any is used.
+__device__ void quant_tokens(const RouteQuantArgs& a, int t0, int ntok, int tid0) {
+  const int kGroups = (kThreads - tid0) / 8;
   constexpr int kBatch = 4;
-  const int group = threadIdx.x / 8, sub = threadIdx.x % 8;
+  const int group = (threadIdx.x - tid0) / 8, sub = threadIdx.x % 8;
   const int nblk = a.H / kTile;
   const int items = ntok * nblk;
   for (int base = 0; base < items; base += kBatch * kGroups) {
@@ -392,8 +392,12 @@ __global__ __launch_bounds__(kThreads) void route_quant_kernel(RouteQuantArgs a)
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int t0 = blockIdx.x * kTokensPerWg;
   const int ntok = min(kTokensPerWg, a.M - t0);
-  if (wave < ntok) route_token_any(a, t0 + wave, lane, l.ids);
-  quant_tokens(a, t0, ntok);
+  // the routing waves (one per token) and the quantising waves run side by side
+  if (wave < kTokensPerWg) {
+    if (wave < ntok) route_token_any(a, t0 + wave, lane, l.ids);
+  } else {
+    quant_tokens(a, t0, ntok, kTokensPerWg * kWave);
+  }
   if (gridDim.x == 1) {
     __syncthreads();
     bucket_any(a, l);
