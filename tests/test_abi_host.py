@@ -70,6 +70,9 @@ _SHARED = dict(sw13=8192, sw13_scale=8192, sw2=8192, sw2_scale=8192, shared_limi
     (dict(experts=64, top_k=33), _capi.ERR_UNSUPPORTED),
     (dict(max_tokens=0), _capi.ERR_INVALID_ARG),
     (dict(max_tokens=257), _capi.ERR_UNSUPPORTED),
+    # each limit alone is allowed; together the routing kernel's LDS (token
+    # masks of 1024 experts x 4 words, 8192 routes) exceeds 64 KiB
+    (dict(max_tokens=256, experts=1024, top_k=32), _capi.ERR_UNSUPPORTED),
     (dict(logits_dtype=7), _capi.ERR_UNSUPPORTED),
     (dict(limit=0.0), _capi.ERR_INVALID_ARG),
     (dict(w13=None), _capi.ERR_INVALID_ARG),

@@ -193,6 +193,30 @@ def test_shapes(name, over, path):
     full_check(moe, inp)
 
 
+# The largest sizes the library takes together: 256 tokens (four 64-bit token
+# mask words per expert), top-32 and 512 experts (8,192 routes bucketed
+# through LDS by the last of 64 routing workgroups); and 1024 experts with
+# top-32.
+LIMITS = [
+    ("m256_e512_k32", dict(M=256, hidden=256, inter=128, experts=512, top_k=32)),
+    ("m16_e1024_k32", dict(M=16, hidden=256, inter=256, experts=1024, top_k=32)),
+]
+
+
+@pytest.mark.parametrize("path", ["auto", "mfma_splitk"])
+@pytest.mark.parametrize("name,over", LIMITS, ids=[s[0] for s in LIMITS])
+def test_limits(name, over, path):
+    shape = synth.CONFIGS["tiny"].with_(name=name, **over)
+    inp = synth.make_inputs(shape, seed=17, device=DEV)
+    moe = make(inp, gemm_path=path)
+    slots, ids, weights, combined = run(moe, inp)
+    ref = oracle_layer(inp)
+    check_routing(ids, weights, ref)
+    check_buckets(moe, ids)
+    assert_rows_close(host(slots), ref["slots"], what="slots")
+    assert_rows_close(host(combined), ref["combined"], what="combined")
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_skewed_routing_many_routes_per_expert(path):
     """Two experts taken by every token: 40 routes on one expert, more than one
