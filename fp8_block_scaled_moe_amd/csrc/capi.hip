@@ -31,6 +31,12 @@ constexpr int kBadFlagWord = 32;        // word of the control region used by cr
 // 311.3, M=16 441.2 -> 446.4 (units no longer divide evenly over the
 // resident workgroups, and a static share cannot even them out).
 constexpr int kPersistMaxTokens = 8;
+// Beyond that, a GEMM whose K is at most this many 128-blocks still runs
+// persistent: its units are short next to the per-unit staging. Measured on
+// the latent shape (H=3584, I=1024, E=896, top-16, M=64), GEMM2 (8 blocks)
+// took 157.4 µs with one workgroup per unit and 139.1 µs persistent; GEMM2
+// of the DeepSeek-V3 shape (16 blocks) was even at M=16..64.
+constexpr int kPersistShortBlocks = 8;
 
 // Workspace regions (the debug stages use the same numbering).
 enum {
@@ -195,13 +201,15 @@ Plan make_plan(const moe_decode_config& c, int M, int fp4_wgs1 = 0, int fp4_wgs2
     p.grid1 = p.umax * (2 * c.inter / p.tpw1) + p.sunits1;
     p.grid2 = p.umax * (c.hidden / p.tpw2) + p.sunits2;
     p.fuse_combine = c.launch_mode == MOE_LAUNCH_COMBINE_IN_GEMM2;
-    // Persistent workgroups where the kernel's conditions hold (an expert has
-    // at most one route per token, so at most M routes) and up to
-    // kPersistMaxTokens tokens; MOE_GEMM_MFMA asked for by name keeps one
-    // workgroup per unit.
-    if (c.gemm_path == MOE_GEMM_AUTO && c.shared_inter == 0 && M <= kPersistMaxTokens) {
-      if (wgp_wgs1 > 0 && gemm_wgp_fits(c.hidden / kTile, p.kp1, M)) p.persist1 = std::min(p.grid1, wgp_wgs1);
-      if (wgp_wgs2 > 0 && !p.fuse_combine && gemm_wgp_fits(c.inter / kTile, p.kp2, M))
+    // Persistent workgroups where the kernel's conditions hold, for up to
+    // kPersistMaxTokens tokens or short K; MOE_GEMM_MFMA asked for by name
+    // keeps one workgroup per unit.
+    if (c.gemm_path == MOE_GEMM_AUTO && c.shared_inter == 0) {
+      const int nkb1 = c.hidden / kTile, nkb2 = c.inter / kTile;
+      const bool few = M <= kPersistMaxTokens;
+      if (wgp_wgs1 > 0 && (few || nkb1 <= kPersistShortBlocks) && gemm_wgp_fits(nkb1, p.kp1))
+        p.persist1 = std::min(p.grid1, wgp_wgs1);
+      if (wgp_wgs2 > 0 && !p.fuse_combine && (few || nkb2 <= kPersistShortBlocks) && gemm_wgp_fits(nkb2, p.kp2))
         p.persist2 = std::min(p.grid2, wgp_wgs2);
     }
     return p;
@@ -376,8 +384,8 @@ int moe_decode_create(const moe_decode_config* cfg, moe_decode_t* out) {
       T * Is,                         // shared h_q
       T * (Is / kTile) * sizeof(float),  // shared h_s
       sp2 * sizeof(float),            // shared down partials
-      fp4 ? Rcap * sizeof(int32_t) * 4 : 0,  // job table (at most one job per route)
-      fp4 ? Rcap * sizeof(int32_t) : 0,      // job of each route
+      Rcap * sizeof(int32_t) * 4,     // job table (at most one job per route)
+      Rcap * sizeof(int32_t),         // job of each route
       fp4 ? 0 : T * (H / 16) * sizeof(int32_t),  // arrival counts (at least 16 rows per workgroup)
   };
   moe_decode_handle* h = new (std::nothrow) moe_decode_handle();
@@ -584,7 +592,8 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   ra.ue8m0_2 = c.shared_ue8m0_act;
   ra.fp4 = fp4;
   ra.xs4 = at(kXs);
-  ra.job_routes = fp4 ? kFp4JobRoutes : 0;
+  // jobs: the FP4 GEMM's units, and the persistent FP8 GEMMs' (one MFMA pass each)
+  ra.job_routes = fp4 ? kFp4JobRoutes : (p.persist1 || p.persist2 ? kMfmaRoutes : 0);
   ra.lb = lb;
   ra.lc = lc;
   ra.b = b;

@@ -301,9 +301,14 @@ __global__ __launch_bounds__(kThreads) void gemm_wg_kernel(GemmArgs args) {
 // 3584 B rows) streamed 1 GiB at 6.78 TB/s as 1024 persistent workgroups and
 // 6.42 TB/s as one workgroup per unit.
 //
-// Conditions, checked by the host: no dense problem, at most 16 routes per
-// expert (one pass), K blocks a multiple of kparts * kDepth (every wave has
-// the same even number of steps) and at most kMaxPersistBlocks of them.
+// Its units are (job, rows) rather than (expert, rows): the routing kernel
+// cuts each expert's routes into jobs of at most 16 (one MFMA pass), so an
+// expert with more routes is several jobs, each streaming its weights once,
+// as the one-unit kernel's passes do.
+//
+// Conditions, checked by the host: no dense problem, K blocks a multiple of
+// kparts * kDepth (every wave has the same even number of steps) and at most
+// kMaxPersistBlocks of them.
 constexpr int kMaxPersistBlocks = 64;
 constexpr int kSxPerThread = kMaxPersistBlocks * kRoutesPerPass / kThreads;  // activation scales staged per thread
 
@@ -318,7 +323,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   const int kparts = a.kparts;
   const int rows_wg = kRowsPerWg / kparts;
   const int per_expert = a.N / rows_wg;
-  const int total = a.b.ctrl[1] * per_expert;
+  const int total = a.b.ctrl[2] * per_expert;  // jobs x units per job
   const int G = gridDim.x;
   int u = blockIdx.x;
   if (u >= total) return;  // more slots than units: the whole workgroup exits
@@ -339,11 +344,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
 
   auto unit_ref = [&](int v) {
     UnitRef x;
-    const int ui = v / per_expert;
-    x.tile = v - ui * per_expert;
-    x.e = a.b.uexp[ui];
-    x.cnt = a.b.ucnt[ui];
-    x.off = a.b.uoff[ui];
+    const int j = v / per_expert;
+    x.tile = v - j * per_expert;
+    const int4 job = a.b.jobs[j];  // {local expert, first index in routes, count <= 16, 0}
+    x.e = job.x;
+    x.off = job.y;
+    x.cnt = job.z;
     return x;
   };
   // Addresses as a uniform base per unit plus a 32-bit offset per lane (a
@@ -498,9 +504,8 @@ size_t gemm_wgp_lds_bytes(int nkb) {
   return 4 * (size_t)kTileBytes + kRedFloats * 4 + (size_t)2 * (4 * nkb + nkb * kRoutesPerPass) * 4;
 }
 
-bool gemm_wgp_fits(int nkb, int kparts, int max_routes) {
-  return max_routes <= kRoutesPerPass && nkb <= kMaxPersistBlocks && kparts >= 1 && 4 % kparts == 0 &&
-         nkb % (kparts * kDepth) == 0;
+bool gemm_wgp_fits(int nkb, int kparts) {
+  return nkb <= kMaxPersistBlocks && kparts >= 1 && 4 % kparts == 0 && nkb % (kparts * kDepth) == 0;
 }
 
 int gemm_wgp_resident_wgs(int nkb) {
@@ -517,7 +522,7 @@ int gemm_wgp_resident_wgs(int nkb) {
 
 hipError_t launch_gemm_wgp(const GemmArgs& a, int role, int grid, hipStream_t s) {
   const GemmProblem& p = a.p[1];
-  if (a.units0 || a.cf.on || grid < 1 || !gemm_wgp_fits(p.nkb, p.kparts, kRoutesPerPass))
+  if (a.units0 || a.cf.on || grid < 1 || !gemm_wgp_fits(p.nkb, p.kparts))
     return hipErrorInvalidValue;
   const size_t lds = gemm_wgp_lds_bytes(p.nkb);
   if (role == 1)

@@ -13,13 +13,13 @@ constexpr int kMaxTopK = 32;
 // Distinct-expert buckets built by the routing kernel (device memory).
 struct Buckets {
   int32_t* ctrl;     // [0] arrival counter (self-resetting), [1] U = distinct experts,
-                     // [2] J = jobs (FP4 form)
+                     // [2] J = jobs (when job_routes > 0)
   int32_t* uexp;     // [U] expert ids, ascending
   int32_t* uoff;     // [U] first index of the expert's routes in `routes`
   int32_t* ucnt;     // [U] number of routes of the expert
   int32_t* routes;   // [M*k] route indices (t*k + j) grouped by expert, ascending t
-  // FP4 form: each expert's routes cut into jobs of at most job_routes
-  // consecutive entries of `routes`, experts ascending.
+  // Each expert's routes cut into jobs of at most job_routes consecutive
+  // entries of `routes`, experts ascending (FP4 form; persistent FP8 GEMMs).
   int4* jobs;        // [J] {local expert, first index in routes, count, 0}
   int32_t* rjob;     // [M*k] job of each local route
 };
@@ -189,12 +189,13 @@ size_t gemm_mfma_lds_bytes(int pass_routes, int ks);
 // writes one FP32 value per (route, row) to part[0].
 hipError_t launch_gemm_wg(const GemmArgs& a, int role, int grid, hipStream_t s);
 size_t gemm_wg_lds_bytes(int nkb);
-// Its persistent form (routed problem only): `grid` workgroups take the units
-// in turn. gemm_wgp_fits: nkb K blocks, kparts K parts and at most max_routes
-// routes per expert are within its conditions; resident_wgs is 0 on error.
+// Its persistent form (routed problem only; its units are the routing
+// kernel's jobs of at most kMfmaRoutes routes x rows): `grid` workgroups take
+// the units in turn. gemm_wgp_fits: nkb K blocks and kparts K parts are
+// within its conditions; resident_wgs is 0 on error.
 hipError_t launch_gemm_wgp(const GemmArgs& a, int role, int grid, hipStream_t s);
 size_t gemm_wgp_lds_bytes(int nkb);
-bool gemm_wgp_fits(int nkb, int kparts, int max_routes);
+bool gemm_wgp_fits(int nkb, int kparts);
 int gemm_wgp_resident_wgs(int nkb);
 // FP32 [n/128, k/128] scales from packed UE8M0 words int32 [n, ceil(k/512)];
 // *bad is set nonzero when the rows of a 128-row block disagree.

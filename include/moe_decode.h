@@ -76,10 +76,10 @@ extern "C" {
 #define MOE_GEMM_MFMA_SPLITK 2  /* v_mfma_f32_16x16x32_f16 (16 routes at once), split-K over workgroups */
 #define MOE_GEMM_MFMA 3         /* v_mfma_f32_16x16x32_f16, K split among the waves of a workgroup;
                                    asked for by name: one workgroup per unit. Under AUTO, a GEMM
-                                   without a shared expert, with at most 8 tokens and with
-                                   K / 128 a multiple of 2 x its K parts (at most 64 blocks) runs
-                                   on resident workgroups that take the units in turn
-                                   (bit-identical results) */
+                                   without a shared expert, with at most 8 tokens or K <= 1024,
+                                   and with K / 128 a multiple of 2 x its K parts (at most 64
+                                   blocks) runs on resident workgroups that take the units in
+                                   turn (bit-identical results) */
 #define MOE_GEMM_FP4 4          /* the MOE_WEIGHTS_NVFP4 kernel (reported by moe_decode_plan; gemm_path stays AUTO) */
 
 /* Launch shapes of run(). Every shape gives bit-identical results. */

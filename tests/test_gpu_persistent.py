@@ -8,9 +8,10 @@ when its loads are requested. So every output and every staged value must be
 bit-identical between the two, and the one-unit form is held to the oracle by
 test_gpu_parity.py. Covered: K parts 1, 2 and 4 in either GEMM, several units
 per workgroup (fewer workgroups than units), one routed expert, eight routes
-on one expert, the full DeepSeek-V3-shaped layer at 1 and 4 tokens, and calls
-of different token counts on one handle. The persistent form is planned for
-at most 8 tokens.
+on one expert, experts with more than 16 routes (several jobs), the full
+DeepSeek-V3-shaped layer at 1 and 4 tokens, and calls of different token
+counts on one handle. The persistent form is planned for at most 8 tokens, or
+any number when K is at most 1024.
 """
 
 from __future__ import annotations
@@ -82,10 +83,22 @@ def test_persistent_single_expert_eight_routes():
 
 
 def test_persistent_not_taken_past_eight_tokens():
-    """Nine tokens: the one-unit kernel runs (and gives the same results)."""
-    shape = synth.CONFIGS["tiny"].with_(M=9, hidden=512, inter=512, experts=8, top_k=2)
+    """Nine tokens and K = 2048: the one-unit kernel runs (and gives the same
+    results)."""
+    shape = synth.CONFIGS["tiny"].with_(M=9, hidden=2048, inter=2048, experts=8, top_k=2)
     inp = synth.make_inputs(shape, seed=53, device=DEV)
     compare(inp, want_persist=(False, False))
+
+
+def test_persistent_short_k_many_tokens_and_jobs():
+    """Past 8 tokens a GEMM with K <= 1024 still runs persistent. Forty
+    tokens on the same two experts: each has 40 routes, three jobs of at most
+    16 (one MFMA pass each), as the one-unit kernel's three passes."""
+    shape = synth.CONFIGS["tiny"].with_(M=40, hidden=1024, inter=512, experts=32, top_k=4)
+    inp = synth.make_inputs(shape, seed=56, device=DEV)
+    inp.bias[:2] += 50.0
+    (_, ids, _, _), plan = compare(inp, want_persist=(True, True))
+    assert (ids[:, :2].sort(dim=1).values.cpu().numpy() == [0, 1]).all()
 
 
 def test_persistent_odd_steps_fall_back():
