@@ -9,8 +9,9 @@
 // power of two after flooring it at 1e-10, then v * (1 / scale) encoded to
 // e4m3.
 //
-// Launch: one 1024-thread workgroup per 4 tokens; waves 0..3 (one per SIMD)
-// each route one token while waves 4..15 quantise the four tokens' x. With one workgroup the
+// Launch: one 1024-thread workgroup per 4 tokens (2 when there are more than
+// 4); waves 0..3 (or 0..1, on their own SIMDs) each route one token while the
+// other waves quantise the workgroup's tokens' x. With one workgroup the
 // routes are grouped by expert right away (by one wave when there are at most
 // 64 routes, else through LDS); with several, the last workgroup to arrive
 // (atomic counter, reset by that workgroup) does it.
@@ -26,8 +27,14 @@ constexpr int kWaves = kThreads / kWave;  // 16
 // Tokens per workgroup, one routing wave each, one per SIMD: routing is
 // VALU-issue bound (FP64 sigmoid, 64-bit DPP maxima), so two routing waves
 // on a SIMD take twice as long (measured on MI355X at M = 8: 11.6 us as two
-// workgroups against 13.0 us as one).
+// workgroups against 13.0 us as one). Up to 4 tokens run in one workgroup
+// (no cross-workgroup handoff); more run 2 to a workgroup: on one GPU's FP4
+// share (M = 16, E = 384, top-6) the kernel took 17.0 us at 4 tokens per
+// workgroup and 13.6 us at 2, and the DeepSeek-V3 shapes at M = 8..64 were
+// even (measured on MI355X).
 constexpr int kTokensPerWg = 4;
+constexpr int kTokensPerWgMany = 2;
+__host__ __device__ inline int tokens_per_wg(int M) { return M <= kTokensPerWg ? kTokensPerWg : kTokensPerWgMany; }
 
 // Monotone image of an FP32 value in uint32: a > b as floats (with -0 < +0)
 // iff key(a) > key(b). Negatives flip every bit, the rest flip the sign bit.
@@ -390,13 +397,14 @@ __global__ __launch_bounds__(kThreads) void route_quant_kernel(RouteQuantArgs a)
   __shared__ int is_last;
   const Lds l = carve(lds, a.E, a.words, a.M * a.k);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int t0 = blockIdx.x * kTokensPerWg;
-  const int ntok = min(kTokensPerWg, a.M - t0);
+  const int tpw = tokens_per_wg(a.M);
+  const int t0 = blockIdx.x * tpw;
+  const int ntok = min(tpw, a.M - t0);
   // the routing waves (one per token) and the quantising waves run side by side
-  if (wave < kTokensPerWg) {
+  if (wave < tpw) {
     if (wave < ntok) route_token_any(a, t0 + wave, lane, l.ids);
   } else {
-    quant_tokens(a, t0, ntok, kTokensPerWg * kWave);
+    quant_tokens(a, t0, ntok, tpw * kWave);
   }
   if (gridDim.x == 1) {
     __syncthreads();
@@ -442,7 +450,8 @@ size_t route_quant_lds_bytes(int E, int words, int routes) {
 }
 
 hipError_t launch_route_quant(const RouteQuantArgs& a, hipStream_t s) {
-  const int grid = (a.M + kTokensPerWg - 1) / kTokensPerWg;
+  const int tpw = tokens_per_wg(a.M);
+  const int grid = (a.M + tpw - 1) / tpw;
   hipLaunchKernelGGL(route_quant_kernel, dim3(grid), dim3(kThreads),
                      route_quant_lds_bytes(a.E, a.words, a.M * a.k), s, a);
   return hipGetLastError();
