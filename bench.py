@@ -41,18 +41,18 @@ GEMM1_TRAFFIC = [
                  "fp8_block_scaled_moe_amd/csrc/gemm_device.h",
                  "fp8_block_scaled_moe_amd/csrc/device_common.h",
                  "fp8_block_scaled_moe_amd/csrc/kernels.h"],
-     "sources_sha256_16": "6d9775338b154034",
+     "sources_sha256_16": "b86a0f9345b7b4c9",
      "workload": "dsv3", "M": 4, "seed": 0, "unique_experts": 27,
      # medians per dispatch (KiB) and the copy kernel's reading of 256 MiB
-     "fetch_kib": 387782.06, "write_kib": 512.0, "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0},
+     "fetch_kib": 387781.5, "write_kib": 512.0, "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0},
     {"sources": ["fp8_block_scaled_moe_amd/csrc/expert_gemm_fp4.hip",
                  "fp8_block_scaled_moe_amd/csrc/fp4_device.h",
                  "fp8_block_scaled_moe_amd/csrc/stream_device.h",
                  "fp8_block_scaled_moe_amd/csrc/device_common.h",
                  "fp8_block_scaled_moe_amd/csrc/kernels.h"],
-     "sources_sha256_16": "df9e746bb215cddd",
+     "sources_sha256_16": "1d1a5c3506ea9c7e",
      "workload": "fp4_share", "M": 16, "seed": 0, "unique_experts": 4,
-     "fetch_kib": 57210.31, "write_kib": 560.0, "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0},
+     "fetch_kib": 56962.28, "write_kib": 560.0, "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0},
 ]
 
 
