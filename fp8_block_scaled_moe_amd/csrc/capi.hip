@@ -42,7 +42,7 @@ constexpr int kPersistShortBlocks = 8;
 enum {
   kCtrl, kUexp, kUoff, kUcnt, kRoutes, kXq, kXs, kP1, kHq, kHs, kP2,
   kSXq, kSXs, kSP1, kSHq, kSHs, kSP2,
-  kJobs, kRjob,  // FP4 form: the job table and each route's job
+  kJobs, kRjob,  // the job table and each route's job (FP4 form, persistent FP8 GEMMs)
   kCount,        // fused GEMM2 + combine: arrivals per (token, column tile)
 };
 
