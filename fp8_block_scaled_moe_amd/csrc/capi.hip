@@ -207,8 +207,25 @@ Plan make_plan(const moe_decode_config& c, int M, int fp4_wgs1 = 0, int fp4_wgs2
     if (c.gemm_path == MOE_GEMM_AUTO && c.shared_inter == 0) {
       const int nkb1 = c.hidden / kTile, nkb2 = c.inter / kTile;
       const bool few = M <= kPersistMaxTokens;
-      if (wgp_wgs1 > 0 && (few || nkb1 <= kPersistShortBlocks) && gemm_wgp_fits(nkb1, p.kp1))
+      if (wgp_wgs1 > 0 && (few || nkb1 <= kPersistShortBlocks) && gemm_wgp_fits(nkb1, p.kp1)) {
+        // On resident workgroups the units' count no longer sets the grid:
+        // the most K parts that keep kWgMinPartBlocks blocks each give finer
+        // units and so an even last round (measured on MI355X, DeepSeek-V3
+        // M=4: GEMM1 123.9 µs at 2 K parts, 118.5 at 4; M=8: 189.2 at 1,
+        // 187.1 at 4).
+        if (c.splits1 <= 0) {
+          for (int kp = 4; kp > p.kp1; kp /= 2) {
+            if (nkb1 / kp >= kWgMinPartBlocks && gemm_wgp_fits(nkb1, kp)) {
+              p.kp1 = kp;
+              p.ks1 = ceil_div(nkb1, kp);
+              p.tpw1 = kRowsPerWg / kp;
+              p.grid1 = p.umax * (2 * c.inter / p.tpw1);
+              break;
+            }
+          }
+        }
         p.persist1 = std::min(p.grid1, wgp_wgs1);
+      }
       if (wgp_wgs2 > 0 && !p.fuse_combine && (few || nkb2 <= kPersistShortBlocks) && gemm_wgp_fits(nkb2, p.kp2))
         p.persist2 = std::min(p.grid2, wgp_wgs2);
     }

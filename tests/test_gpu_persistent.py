@@ -50,9 +50,13 @@ def staged(moe, M):
 
 
 def compare(inp, M=None, want_persist=(True, True), **kw):
+    """The persistent plan at M against the one-unit kernel with the same K
+    parts (the persistent plan may take more of them)."""
     M = M or inp.shape.M
-    pers, one = make(inp, "auto", **kw), make(inp, "mfma", **kw)
+    pers = make(inp, "auto", **kw)
     plan = pers.plan(M)
+    kw = dict(kw, splits1=plan["kparts1"], splits2=plan["kparts2"])
+    one = make(inp, "mfma", **kw)
     assert (plan["persist1"] > 0, plan["persist2"] > 0) == tuple(want_persist), plan
     assert one.plan(M)["persist1"] == 0 and one.plan(M)["persist2"] == 0
     a, b = run(pers, inp, M), run(one, inp, M)
@@ -111,16 +115,21 @@ def test_persistent_odd_steps_fall_back():
 def test_persistent_token_counts_on_one_handle():
     shape = synth.CONFIGS["tiny"].with_(M=9, hidden=2048, inter=1024, experts=32, top_k=6)
     inp = synth.make_inputs(shape, seed=55, device=DEV)
-    pers, one = make(inp, "auto"), make(inp, "mfma")
+    pers, one = make(inp, "auto", splits1=2, splits2=1), make(inp, "mfma", splits1=2, splits2=1)
     for M in (9, 1, 4, 8, 9):
         for name, x, y in zip(("slots", "ids", "weights", "combined"), run(pers, inp, M), run(one, inp, M)):
             assert torch.equal(x, y), (M, name)
 
 
-@pytest.mark.parametrize("M", [1, 4])
-def test_persistent_dsv3(M):
+@pytest.fixture(scope="module")
+def dsv3_m8():
+    return synth.make_inputs(synth.CONFIGS["dsv3"].with_(M=8), seed=0, device=DEV)
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_persistent_dsv3(dsv3_m8, M):
     """The DeepSeek-V3-shaped layer: thousands of units on the resident
-    workgroups."""
-    inp = synth.make_inputs(synth.CONFIGS["dsv3"], seed=0, device=DEV)
-    _, plan = compare(inp, M=M)
+    workgroups; GEMM1 in 4 K parts (16-row units)."""
+    _, plan = compare(dsv3_m8, M=M)
     assert plan["persist1"] < plan["grid1"]  # several units per workgroup
+    assert plan["kparts1"] == 4
