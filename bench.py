@@ -40,19 +40,21 @@ GEMM1_TRAFFIC = [
     {"sources": ["fp8_block_scaled_moe_amd/csrc/expert_gemm_wg.hip",
                  "fp8_block_scaled_moe_amd/csrc/gemm_device.h",
                  "fp8_block_scaled_moe_amd/csrc/device_common.h",
-                 "fp8_block_scaled_moe_amd/csrc/kernels.h"],
-     "sources_sha256_16": "b86a0f9345b7b4c9",
+                 "fp8_block_scaled_moe_amd/csrc/kernels.h",
+                 "fp8_block_scaled_moe_amd/csrc/capi.hip"],  # the plan (K parts, grids)
+     "sources_sha256_16": "8cab333a5c875c97",
      "workload": "dsv3", "M": 4, "seed": 0, "unique_experts": 27,
      # medians per dispatch (KiB) and the copy kernel's reading of 256 MiB
-     "fetch_kib": 387781.5, "write_kib": 512.0, "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0},
+     "fetch_kib": 387997.0, "write_kib": 512.0, "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0},
     {"sources": ["fp8_block_scaled_moe_amd/csrc/expert_gemm_fp4.hip",
                  "fp8_block_scaled_moe_amd/csrc/fp4_device.h",
                  "fp8_block_scaled_moe_amd/csrc/stream_device.h",
                  "fp8_block_scaled_moe_amd/csrc/device_common.h",
-                 "fp8_block_scaled_moe_amd/csrc/kernels.h"],
-     "sources_sha256_16": "1d1a5c3506ea9c7e",
+                 "fp8_block_scaled_moe_amd/csrc/kernels.h",
+                 "fp8_block_scaled_moe_amd/csrc/capi.hip"],
+     "sources_sha256_16": "6e22324b695ddb0d",
      "workload": "fp4_share", "M": 16, "seed": 0, "unique_experts": 4,
-     "fetch_kib": 56962.28, "write_kib": 560.0, "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0},
+     "fetch_kib": 56899.88, "write_kib": 560.0, "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0},
 ]
 
 
