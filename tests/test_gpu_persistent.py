@@ -105,6 +105,31 @@ def test_persistent_short_k_many_tokens_and_jobs():
     assert (ids[:, :2].sort(dim=1).values.cpu().numpy() == [0, 1]).all()
 
 
+def test_persistent_local_share():
+    """One GPU's share of the experts (local experts 10..19 of 32): the jobs
+    hold local routes only; the other slots stay zero."""
+    full = synth.CONFIGS["tiny"].with_(M=7, hidden=1024, inter=512, experts=32, top_k=4)
+    inp = synth.make_inputs(full, seed=57, device=DEV)
+    lb, lc = 10, 10
+    w = [t[lb:lb + lc].clone() for t in (inp.w13, inp.w13_scale, inp.w2, inp.w2_scale)]
+    outs = []
+    for path in ("auto", "mfma"):
+        moe = MoeDecode(*w, top_k=full.top_k, limit=full.limit, routed_scale=full.routed_scale,
+                        max_tokens=full.M, experts=full.experts, local_begin=lb, gemm_path=path,
+                        splits1=1, splits2=1)
+        plan = moe.plan(full.M)
+        assert (plan["persist1"] > 0) == (path == "auto") and (plan["persist2"] > 0) == (path == "auto")
+        outs.append(run(moe, inp, full.M))
+    for name, x, y in zip(("slots", "ids", "weights", "combined"), *outs):
+        assert torch.equal(x, y), name
+    ids = outs[0][1].cpu().numpy().reshape(-1)
+    local = (ids >= lb) & (ids < lb + lc)
+    assert local.any() and (~local).any()
+    assert not outs[0][0].float().cpu().numpy()[~local].any()
+    ref = oracle_layer(inp)
+    assert_rows_close(host(outs[0][0])[local], ref["slots"][local], what="slots")
+
+
 def test_persistent_odd_steps_fall_back():
     """K / 128 = 3 blocks cannot give every wave an even number of steps."""
     shape = synth.CONFIGS["tiny"].with_(M=3, hidden=384, inter=256, experts=6, top_k=2)
