@@ -298,8 +298,8 @@ __global__ __launch_bounds__(kThreads) void gemm_wg_kernel(GemmArgs args) {
 // next unit's first kDepth steps of weights and activations are requested in
 // the slots the current unit no longer refills, so each wave's stream runs on
 // from one unit into the next. A read probe of this shape (64-row units of
-// 3584 B rows) streamed 1 GiB at 6.78 TB/s as 1024 persistent workgroups and
-// 6.42 TB/s as one workgroup per unit.
+// 3584 B rows, 800 MB) streamed at 6.78 TB/s on 1024 persistent workgroups
+// and 6.42 TB/s with one workgroup per unit.
 //
 // Its units are (job, rows) rather than (expert, rows): the routing kernel
 // cuts each expert's routes into jobs of at most 16 (one MFMA pass), so an
