@@ -42,7 +42,7 @@ GEMM1_TRAFFIC = [
                  "fp8_block_scaled_moe_amd/csrc/device_common.h",
                  "fp8_block_scaled_moe_amd/csrc/kernels.h",
                  "fp8_block_scaled_moe_amd/csrc/capi.hip"],  # the plan (K parts, grids)
-     "sources_sha256_16": "6c343f378a7ab6dd",
+     "sources_sha256_16": "48ff860d8afd5860",
      "workload": "dsv3", "M": 4, "seed": 0, "unique_experts": 27,
      # medians per dispatch (KiB) and the copy kernel's reading of 256 MiB
      "fetch_kib": 387997.0, "write_kib": 512.0, "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0},
@@ -52,7 +52,7 @@ GEMM1_TRAFFIC = [
                  "fp8_block_scaled_moe_amd/csrc/device_common.h",
                  "fp8_block_scaled_moe_amd/csrc/kernels.h",
                  "fp8_block_scaled_moe_amd/csrc/capi.hip"],
-     "sources_sha256_16": "6e22324b695ddb0d",
+     "sources_sha256_16": "255f6392716bb5dc",
      "workload": "fp4_share", "M": 16, "seed": 0, "unique_experts": 4,
      "fetch_kib": 56899.88, "write_kib": 560.0, "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0},
 ]
@@ -94,7 +94,8 @@ def parse():
     p.add_argument("--path", default="auto", choices=["auto", "valu_splitk", "mfma_splitk", "mfma"])
     p.add_argument("--splits1", type=int, default=0)
     p.add_argument("--splits2", type=int, default=0)
-    p.add_argument("--launch-mode", default="auto", choices=["auto", "separate", "combine_in_gemm2"])
+    p.add_argument("--launch-mode", default="auto",
+                   choices=["auto", "separate", "combine_in_gemm2", "swiglu_in_gemm1"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--sweep", default="", help="comma-separated M values: one JSON line each")
     p.add_argument("--calibrate", action="store_true",

@@ -18,7 +18,7 @@ using namespace moe;
 namespace {
 
 constexpr int kEvents = 8;
-constexpr int kRegions = 20;
+constexpr int kRegions = 21;
 constexpr int kStages = 5;  // timing slots: route, GEMM1, SwiGLU, GEMM2, combine
 constexpr int kTargetUnits = 4096;  // work units per GEMM launch to aim for (16 per CU)
 constexpr int kDenseTargetUnits = 256;  // units of the shared expert per GEMM launch
@@ -44,6 +44,7 @@ enum {
   kSXq, kSXs, kSP1, kSHq, kSHs, kSP2,
   kJobs, kRjob,  // the job table and each route's job (FP4 form, persistent FP8 GEMMs)
   kCount,        // fused GEMM2 + combine: arrivals per (token, column tile)
+  kSwCount,      // fused GEMM1 + SwiGLU: arrivals per (route, 128-column block)
 };
 
 struct Plan {
@@ -58,6 +59,7 @@ struct Plan {
   // K-in-workgroup path: K parts per row group (routed, shared)
   int kp1, kp2, skp1, skp2;
   bool fuse_combine;  // the combine runs inside the GEMM2 launch
+  bool fuse_swiglu;   // the SwiGLU runs inside the (persistent) GEMM1 launch
   // K-in-workgroup path: resident workgroups of the persistent GEMM1 / GEMM2
   // launches (0: one workgroup per unit)
   int persist1, persist2;
@@ -225,6 +227,7 @@ Plan make_plan(const moe_decode_config& c, int M, int fp4_wgs1 = 0, int fp4_wgs2
           }
         }
         p.persist1 = std::min(p.grid1, wgp_wgs1);
+        p.fuse_swiglu = c.launch_mode == MOE_LAUNCH_SWIGLU_IN_GEMM1;
       }
       if (wgp_wgs2 > 0 && !p.fuse_combine && (few || nkb2 <= kPersistShortBlocks) && gemm_wgp_fits(nkb2, p.kp2))
         p.persist2 = std::min(p.grid2, wgp_wgs2);
@@ -293,7 +296,7 @@ int validate_config(const moe_decode_config* c) {
   if (gemm_wg_lds_bytes(std::max(c->hidden, std::max(c->inter, c->shared_inter)) / kTile) > kMaxWgLds)
     return MOE_DECODE_ERR_UNSUPPORTED;
   if (c->splits1 < 0 || c->splits2 < 0) return MOE_DECODE_ERR_INVALID_ARG;
-  if (c->launch_mode < MOE_LAUNCH_AUTO || c->launch_mode > MOE_LAUNCH_COMBINE_IN_GEMM2)
+  if (c->launch_mode < MOE_LAUNCH_AUTO || c->launch_mode > MOE_LAUNCH_SWIGLU_IN_GEMM1)
     return MOE_DECODE_ERR_UNSUPPORTED;
   {
     const int words = (c->max_tokens + 63) / 64;
@@ -404,6 +407,7 @@ int moe_decode_create(const moe_decode_config* cfg, moe_decode_t* out) {
       Rcap * sizeof(int32_t) * 4,     // job table (at most one job per route)
       Rcap * sizeof(int32_t),         // job of each route
       fp4 ? 0 : T * (H / 16) * sizeof(int32_t),  // arrival counts (at least 16 rows per workgroup)
+      fp4 ? 0 : Rcap * (I / kTile) * sizeof(int32_t),  // arrival counts per (route, hidden block)
   };
   moe_decode_handle* h = new (std::nothrow) moe_decode_handle();
   if (!h) return MOE_DECODE_ERR_OUT_OF_MEMORY;
@@ -527,7 +531,7 @@ int moe_decode_plan(moe_decode_t h, int32_t M, int32_t* out, int32_t n) {
     out[15] = p.path == MOE_GEMM_MFMA ? p.kp1 : 1;
     out[16] = p.path == MOE_GEMM_MFMA ? p.kp2 : 1;
   }
-  if (n >= 18) out[17] = p.fuse_combine ? 4 : 5;
+  if (n >= 18) out[17] = 5 - (p.fuse_combine ? 1 : 0) - (p.fuse_swiglu ? 1 : 0);
   if (n >= 20) {
     out[18] = p.persist1;
     out[19] = p.persist2;
@@ -705,11 +709,22 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
     g1.p[0].kparts = p.skp1;
     g1.units0 = p.sunits1;
   }
+  if (p.fuse_swiglu) {
+    SwigluFuse& f = g1.sf;
+    f.on = 1;
+    f.counters = reinterpret_cast<int32_t*>(at(kSwCount));
+    f.I = c.inter;
+    f.limit = c.limit;
+    f.hq = hq;
+    f.hs = hs;
+  }
   if (e == hipSuccess) e = launch_gemm(g1, 1, p.grid1 - (shared ? 0 : p.sunits1));
   if (e == hipSuccess) e = mark(1);
 
-  if (e == hipSuccess) e = launch_swiglu_requant(sa, s);
-  if (e == hipSuccess) e = mark(2);
+  if (!p.fuse_swiglu) {
+    if (e == hipSuccess) e = launch_swiglu_requant(sa, s);
+    if (e == hipSuccess) e = mark(2);
+  }
 
   GemmArgs g2{};
   g2.p[1] = problem(c.w2, c.w2_scale, hq, hs, p2, c.hidden, c.inter, p.s2, p.ks2, R, 1, p.tpw2);

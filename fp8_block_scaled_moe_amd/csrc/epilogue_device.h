@@ -11,14 +11,36 @@ namespace moe {
 
 __device__ __forceinline__ float bf16_round(float v) { return bf16_value(bf16_bits(v)); }
 
-// One wave: the fixed-order sum of GEMM1's split partials for route r and
-// 128-block c of the hidden, the clamped SwiGLU and the FP8 hidden block
-// (vLLM "mega_moe" page, hidden_block): up = clamp(u, -L, L),
-// gate = min(g, L), act = (gate / (1 + exp(-gate))) * up in FP32 operations
-// with the exp correctly rounded, scale = max(amax, 1e-10) / 448,
-// q = e4m3(act / scale). Rows 0..I-1 of GEMM1 are up, I..2I-1 gate.
+// One wave: the clamped SwiGLU and the FP8 hidden block of route r, columns
+// 128c + 2 lane and + 1, from the GEMM1 sums of its up and gate rows (vLLM
+// "mega_moe" page, hidden_block): up = clamp(u, -L, L), gate = min(g, L),
+// act = (gate / (1 + exp(-gate))) * up in FP32 operations with the exp
+// correctly rounded, scale = max(amax, 1e-10) / 448 over the wave's 128
+// values, q = e4m3(act / scale). Used by the separate kernel and by the
+// GEMM1 launch that finishes the step itself.
+__device__ __forceinline__ void swiglu_finish(float up0, float up1, float g0, float g1, float L, int I,
+                                              uint8_t* hq, float* hs, int r, int c, int lane) {
+  const int nblk = I / kTile;
+  const int j = c * kTile + 2 * lane;
+  up0 = fminf(fmaxf(up0, -L), L);
+  up1 = fminf(fmaxf(up1, -L), L);
+  g0 = fminf(g0, L);
+  g1 = fminf(g1, L);
+  // exp rounded once to FP32 from FP64, then the add, divide and product in
+  // FP32 in this order: the FP8 codes below are decided from these values.
+  const float e0 = (float)exp(-(double)g0), e1 = (float)exp(-(double)g1);
+  const float act0 = (g0 / (1.f + e0)) * up0;
+  const float act1 = (g1 / (1.f + e1)) * up1;
+  const float amax = group_max<kWave>(fmaxf(fabsf(act0), fabsf(act1)));
+  const float s = fmaxf(amax, kAmaxFloor) / kFp8Max;
+  const uint32_t q = e4m3x2_encode(act0 / s, act1 / s);
+  *reinterpret_cast<uint16_t*>(hq + (size_t)r * I + j) = (uint16_t)q;
+  if (lane == 0) hs[(size_t)r * nblk + c] = s;
+}
+
+// One wave: route r, 128-block c of the hidden, from the fixed-order sum of
+// GEMM1's split partials. Rows 0..I-1 of GEMM1 are up, I..2I-1 gate.
 __device__ __forceinline__ void swiglu_route_block(const SwigluArgs& a, int r, int c, int lane) {
-  const int nblk = a.I / kTile;
   const int j = c * kTile + 2 * lane;
   const size_t row = (size_t)2 * a.I;
   float up0 = 0.f, up1 = 0.f, g0 = 0.f, g1 = 0.f;
@@ -32,21 +54,7 @@ __device__ __forceinline__ void swiglu_route_block(const SwigluArgs& a, int r, i
     g0 += g.x;
     g1 += g.y;
   }
-  const float L = a.limit;
-  up0 = fminf(fmaxf(up0, -L), L);
-  up1 = fminf(fmaxf(up1, -L), L);
-  g0 = fminf(g0, L);
-  g1 = fminf(g1, L);
-  // exp rounded once to FP32 from FP64, then the add, divide and product in
-  // FP32 in this order: the FP8 codes below are decided from these values.
-  const float e0 = (float)exp(-(double)g0), e1 = (float)exp(-(double)g1);
-  const float act0 = (g0 / (1.f + e0)) * up0;
-  const float act1 = (g1 / (1.f + e1)) * up1;
-  const float amax = group_max<kWave>(fmaxf(fabsf(act0), fabsf(act1)));
-  const float s = fmaxf(amax, kAmaxFloor) / kFp8Max;
-  const uint32_t q = e4m3x2_encode(act0 / s, act1 / s);
-  *reinterpret_cast<uint16_t*>(a.hq + (size_t)r * a.I + j) = (uint16_t)q;
-  if (lane == 0) a.hs[(size_t)r * nblk + c] = s;
+  swiglu_finish(up0, up1, g0, g1, a.limit, a.I, a.hq, a.hs, r, c, lane);
 }
 
 // One wave, shared expert ("shared_expert" page, _DownKernel and

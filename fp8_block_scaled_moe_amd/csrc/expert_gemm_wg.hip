@@ -31,6 +31,7 @@
 // once, FP32 sum in pick order). No workgroup ever waits for another.
 #include <algorithm>
 
+#include "epilogue_device.h"
 #include "gemm_device.h"
 
 namespace moe {
@@ -316,9 +317,50 @@ struct UnitRef {
   int e, cnt, off, tile;
 };
 
-template <int kRole>
+// Whole workgroup, after a GEMM1 unit of rows [row0, row0 + rows_wg) has
+// stored its sums at device scope: one arrival per route of the unit on
+// (route, 128-column block); for each count this unit completes, one wave
+// reads the block's up and gate sums at device scope and writes its
+// activation and FP8 codes (the arithmetic of the separate kernel, its split
+// sum of one slice included). Contains barriers.
+__device__ void finish_swiglu_blocks(const SwigluFuse& f, const GemmProblem& a, const UnitRef& u, int rows_wg,
+                                     int* claimed, int& nclaim) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  // These stores are at the device coherence point once they complete (the
+  // next unit's first requests, issued before them, complete too).
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) nclaim = 0;
+  __syncthreads();
+  const int row0 = u.tile * rows_wg;
+  const int c = (row0 < f.I ? row0 : row0 - f.I) / kTile;  // the unit's rows lie in one 128-row block
+  const int nblk = f.I / kTile, target = 2 * (kTile / rows_wg);
+  if (tid < u.cnt) {
+    const int r = a.b.routes[u.off + tid];
+    int32_t* ctr = f.counters + (size_t)r * nblk + c;
+    if (__hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == target - 1) {
+      __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
+      claimed[atomicAdd(&nclaim, 1)] = r;
+    }
+  }
+  __syncthreads();
+  const int n = nclaim;
+  for (int q = wave; q < n; q += kThreads / kWave) {
+    const int r = claimed[q];
+    const float* p = a.part + (size_t)r * a.N + c * kTile + 2 * lane;
+    const float u0 = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float u1 = __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float g0 = __hip_atomic_load(p + f.I, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float g1 = __hip_atomic_load(p + f.I + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    swiglu_finish(0.f + u0, 0.f + u1, 0.f + g0, 0.f + g1, f.limit, f.I, f.hq, f.hs, r, c, lane);
+  }
+}
+
+template <int kRole, bool kSwiglu>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void gemm_wgp_kernel(GemmArgs args) {
   extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int claimed[kRoutesPerPass];
+  __shared__ int nclaim;
   const GemmProblem& a = args.p[1];
   const int kparts = a.kparts;
   const int rows_wg = kRowsPerWg / kparts;
@@ -480,8 +522,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
         }
       }
     }
-    if (kp == 0 && live)
-      *reinterpret_cast<float4_t*>(a.part + (size_t)rt * a.N + cur.tile * rows_wg + rgrp * 16 + 4 * g) = acc;
+    if (kp == 0 && live) {
+      float* dst = a.part + (size_t)rt * a.N + cur.tile * rows_wg + rgrp * 16 + 4 * g;
+      if constexpr (kSwiglu) {  // read back by whichever workgroup completes the block
+#pragma unroll
+        for (int i = 0; i < 4; ++i) __hip_atomic_store(dst + i, acc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        *reinterpret_cast<float4_t*>(dst) = acc;
+      }
+    }
+    if constexpr (kSwiglu) finish_swiglu_blocks(args.sf, a, cur, rows_wg, claimed, nclaim);
     if (!more) break;
     commit(stage + (buf ^ 1) * stage_floats, nx);
     __syncthreads();  // the next unit's scales are in place; this unit is done with red and its stage
@@ -512,7 +562,7 @@ int gemm_wgp_resident_wgs(int nkb) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(gemm_wgp_kernel<1>),
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(gemm_wgp_kernel<1, false>),
                                                    kThreads, gemm_wgp_lds_bytes(nkb)) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
@@ -525,10 +575,15 @@ hipError_t launch_gemm_wgp(const GemmArgs& a, int role, int grid, hipStream_t s)
   if (a.units0 || a.cf.on || grid < 1 || !gemm_wgp_fits(p.nkb, p.kparts))
     return hipErrorInvalidValue;
   const size_t lds = gemm_wgp_lds_bytes(p.nkb);
-  if (role == 1)
-    hipLaunchKernelGGL(gemm_wgp_kernel<1>, dim3(grid), dim3(kThreads), lds, s, a);
-  else
-    hipLaunchKernelGGL(gemm_wgp_kernel<2>, dim3(grid), dim3(kThreads), lds, s, a);
+  if (a.sf.on) {
+    // the unit's rows must lie in one 128-column block of up or of gate
+    if (role != 1 || p.N != 2 * a.sf.I || kTile % (kRowsPerWg / p.kparts) != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_wgp_kernel<1, true>), dim3(grid), dim3(kThreads), lds, s, a);
+  } else if (role == 1) {
+    hipLaunchKernelGGL((gemm_wgp_kernel<1, false>), dim3(grid), dim3(kThreads), lds, s, a);
+  } else {
+    hipLaunchKernelGGL((gemm_wgp_kernel<2, false>), dim3(grid), dim3(kThreads), lds, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -143,6 +143,20 @@ struct CombineFuse {
   int all_local;        // lb == 0 and lc == experts: every token has k local picks
 };
 
+// The SwiGLU carried out inside the persistent GEMM1 launch: each unit, once
+// its outputs are stored at device scope, counts one arrival per route on
+// (route, 128-column block of the hidden); the arrival that completes a
+// count (the 2 x 128 / rows units holding the block's up and gate rows)
+// computes that block's activation and FP8 codes. Counters reset themselves.
+struct SwigluFuse {
+  int on;               // 0: plain GEMM1 (swiglu_requant_kernel follows)
+  int32_t* counters;    // [R, I/128], zero between calls
+  int I;
+  float limit;
+  uint8_t* hq;          // [R, I] e4m3
+  float* hs;            // [R, I/128]
+};
+
 // One GEMM launch: the dense problem's units (if any) come first in the grid,
 // then the routed problem's.
 struct GemmArgs {
@@ -151,6 +165,7 @@ struct GemmArgs {
   int pass_routes;      // MFMA path: routes staged per pass (<= 16)
   int stream_wgs;       // FP4 kernel: resident workgroups (stream_map)
   CombineFuse cf;       // K-in-workgroup GEMM2 only
+  SwigluFuse sf;        // persistent GEMM1 only
 };
 
 // FP4 GEMM: a stream of (job, tile, step) items split evenly over the

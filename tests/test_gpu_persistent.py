@@ -158,3 +158,58 @@ def test_persistent_dsv3(dsv3_m8, M):
     _, plan = compare(dsv3_m8, M=M)
     assert plan["persist1"] < plan["grid1"]  # several units per workgroup
     assert plan["kparts1"] == 4
+
+
+# -- the SwiGLU inside the persistent GEMM1 launch (MOE_LAUNCH_SWIGLU_IN_GEMM1) --
+
+def make_mode(inp, mode, **kw):
+    return make(inp, "auto", launch_mode=mode, **kw)
+
+
+def swiglu_pair(inp, M, **kw):
+    """The same layer with the SwiGLU inside GEMM1 and as its own launch: every
+    output and the staged FP8 hidden and its scales bit-identical."""
+    fused, sep = make_mode(inp, "swiglu_in_gemm1", **kw), make_mode(inp, "separate", **kw)
+    assert fused.plan(M)["launches"] == 4 and sep.plan(M)["launches"] == 5
+    for moe in (fused, sep):
+        assert moe.plan(M)["persist1"] > 0
+    a, b = run(fused, inp, M), run(sep, inp, M)
+    for name, x, y in zip(("slots", "ids", "weights", "combined"), a, b):
+        assert torch.equal(x, y), name
+    R, I = M * inp.shape.top_k, inp.shape.inter
+    for st, n, dt in (("h_q", R * I, torch.uint8), ("h_s", R * (I // 128), torch.float32)):
+        x = fused.stage(st, torch.empty(n, dtype=dt, device=DEV))
+        y = sep.stage(st, torch.empty(n, dtype=dt, device=DEV))
+        assert torch.equal(x, y), st
+    return fused, sep
+
+
+@pytest.mark.parametrize("splits1", [1, 2, 4], ids=["64rows", "32rows", "16rows"])
+def test_swiglu_in_gemm1_equals_separate(splits1):
+    shape = synth.CONFIGS["tiny"].with_(M=6, hidden=1024, inter=512, experts=12, top_k=4)
+    inp = synth.make_inputs(shape, seed=58, device=DEV)
+    fused, _ = swiglu_pair(inp, shape.M, splits1=splits1)
+    assert fused.plan(shape.M)["kparts1"] == splits1
+    slots, ids, _, combined = run(fused, inp, shape.M)
+    ref = oracle_layer(inp)
+    assert np.array_equal(ids.cpu().numpy(), ref["ids"])
+    assert_rows_close(host(slots), ref["slots"], what="slots")
+    assert_rows_close(host(combined), ref["combined"], what="combined")
+
+
+def test_swiglu_in_gemm1_counters_reset_and_jobs():
+    """Calls of 8, 1, 5 and 8 tokens on one handle (each block's count must
+    be back at zero), experts with more than 16 routes (K <= 1024 keeps the
+    GEMMs persistent past 8 tokens)."""
+    shape = synth.CONFIGS["tiny"].with_(M=40, hidden=1024, inter=512, experts=32, top_k=4)
+    inp = synth.make_inputs(shape, seed=59, device=DEV)
+    inp.bias[:2] += 50.0
+    fused, sep = make_mode(inp, "swiglu_in_gemm1"), make_mode(inp, "separate")
+    for M in (8, 1, 40, 5, 40):
+        for name, x, y in zip(("slots", "ids", "weights", "combined"), run(fused, inp, M), run(sep, inp, M)):
+            assert torch.equal(x, y), (M, name)
+
+
+def test_swiglu_in_gemm1_dsv3(dsv3_m8):
+    for M in (1, 4, 8):
+        swiglu_pair(dsv3_m8, M)
