@@ -33,7 +33,9 @@
  *  - Everything is enqueued on the HIP stream passed in (a hipStream_t, given
  *    as void* so that this header needs no HIP headers; NULL is the default
  *    stream). No call synchronises the host, and moe_decode_run allocates
- *    nothing, so it may be captured in a HIP graph.
+ *    nothing, so it may be captured in a HIP graph: a replay reads the
+ *    inputs and writes the outputs at the addresses captured, for the M
+ *    captured, and replays of one handle's graph must be ordered like calls.
  *  - Return value: MOE_DECODE_OK (0) or a negative MOE_DECODE_ERR_* code.
  *    An argument error leaves the handle valid and enqueues nothing.
  *
