@@ -9,12 +9,16 @@
 // power of two after flooring it at 1e-10, then v * (1 / scale) encoded to
 // e4m3.
 //
-// Launch: one 1024-thread workgroup per 4 tokens (2 when there are more than
-// 4); waves 0..3 (or 0..1, on their own SIMDs) each route one token while the
-// other waves quantise the workgroup's tokens' x. With one workgroup the
-// routes are grouped by expert right away (by one wave when there are at most
-// 64 routes, else through LDS); with several, the last workgroup to arrive
-// (atomic counter, reset by that workgroup) does it.
+// Launch: one 1024-thread routing workgroup per 4 tokens (2 when there are
+// more than 4); its waves 0..3 (or 0..1, on their own SIMDs) each route one
+// token while its other waves quantise. Workgroups that only quantise follow
+// when there are few routing workgroups; all quantising waves share out the
+// 128-blocks of every token. With one routing workgroup the routes are
+// grouped by expert right away (by one wave when there are at most 64
+// routes, else through LDS); with several, the last routing workgroup to
+// arrive (atomic counter, reset by that workgroup) does it.
+#include <algorithm>
+
 #include "kernels.h"
 #include "device_common.h"
 #include "fp4_device.h"
@@ -35,6 +39,17 @@ constexpr int kWaves = kThreads / kWave;  // 16
 constexpr int kTokensPerWg = 4;
 constexpr int kTokensPerWgMany = 2;
 __host__ __device__ inline int tokens_per_wg(int M) { return M <= kTokensPerWg ? kTokensPerWg : kTokensPerWgMany; }
+__host__ __device__ inline int routing_wgs(int M) { return (M + tokens_per_wg(M) - 1) / tokens_per_wg(M); }
+// Workgroups that only quantise, launched after the routing ones when the
+// routing workgroups' quantising waves would take more than one 128-block
+// per eight lanes (at most 4 tokens on one workgroup, 56 blocks each at
+// H = 7168, against 96 groups of eight lanes).
+constexpr int kMaxQuantWgs = 16;
+inline int quant_wgs(int M, int H) {
+  const int have = routing_wgs(M) * (kThreads - tokens_per_wg(M) * kWave) / 8;
+  const int items = M * (H / kTile);
+  return items > have ? std::min((items - have + kThreads / 8 - 1) / (kThreads / 8), kMaxQuantWgs) : 0;
+}
 
 // Monotone image of an FP32 value in uint32: a > b as floats (with -0 < +0)
 // iff key(a) > key(b). Negatives flip every bit, the rest flip the sign bit.
@@ -144,29 +159,28 @@ __device__ void route_token_any(const RouteQuantArgs& a, int t, int lane, int* i
   else route_token<16>(a, t, lane, ids_l);
 }
 
-// Threads tid0.. (tid0 a multiple of the wave size): the 128-blocks of tokens
-// [t0, t0 + ntok), eight lanes per block and sixteen values per lane; loads
-// of up to four blocks per lane are issued before any is used.
-__device__ void quant_tokens(const RouteQuantArgs& a, int t0, int ntok, int tid0) {
-  const int kGroups = (kThreads - tid0) / 8;
+// The 128-blocks of all M tokens, eight lanes per block and sixteen values
+// per lane: group g of `groups` takes blocks g, g + groups, ...; loads of up
+// to four blocks per lane are issued before any is used.
+__device__ void quant_blocks(const RouteQuantArgs& a, int group, int groups) {
   constexpr int kBatch = 4;
-  const int group = (threadIdx.x - tid0) / 8, sub = threadIdx.x % 8;
+  const int sub = threadIdx.x % 8;
   const int nblk = a.H / kTile;
-  const int items = ntok * nblk;
-  for (int base = 0; base < items; base += kBatch * kGroups) {
+  const int items = a.M * nblk;
+  for (int base = 0; base < items; base += kBatch * groups) {
     u32x4_t lo[kBatch], hi[kBatch];
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
-      const int item = base + q * kGroups + group;
+      const int item = base + q * groups + group;
       if (item < items) {
-        const size_t at = (size_t)(t0 + item / nblk) * a.H + (size_t)(item % nblk) * kTile + sub * 16;
+        const size_t at = (size_t)(item / nblk) * a.H + (size_t)(item % nblk) * kTile + sub * 16;
         lo[q] = *reinterpret_cast<const u32x4_t*>(a.x + at);
         hi[q] = *reinterpret_cast<const u32x4_t*>(a.x + at + 8);
       }
     }
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
-      const int item = base + q * kGroups + group;
+      const int item = base + q * groups + group;
       if (item < items) {  // the same for all eight lanes of a group
         float v[16];
 #pragma unroll
@@ -176,7 +190,7 @@ __device__ void quant_tokens(const RouteQuantArgs& a, int t0, int ntok, int tid0
           v[8 + 2 * i] = bf16_value(hi[q][i] & 0xFFFFu);
           v[8 + 2 * i + 1] = bf16_value(hi[q][i] >> 16);
         }
-        const int t = t0 + item / nblk, blk = item % nblk;
+        const int t = item / nblk, blk = item % nblk;
         const size_t at = (size_t)t * a.H + (size_t)blk * kTile + sub * 16;
         if (a.fp4) {  // this lane's 16 values are one FP4 group
           uint32_t packed[2];
@@ -314,73 +328,57 @@ __device__ void bucket_routes(const RouteQuantArgs& a, const Lds& l) {
   }
 }
 
-// The same grouping by one wave when there are at most 64 routes: lane r
-// holds (local expert << 16) | r (non-local routes sort last as padding), a
-// bitonic network over the wave sorts the keys (experts ascending, routes
-// ascending within an expert), and the first lane of each expert's run
-// writes its bucket. No LDS, no barrier.
+// The same grouping by one wave when there are at most 64 routes, without
+// moving data between lanes. Lane r holds route r's local expert e. One
+// ballot per bit of e, from the top bit down, narrows two masks per lane:
+// the lanes whose expert equals e so far (eq) and those already known to be
+// smaller (lt). Then the route's place in (expert, route) order is
+// popc(lt) + popc(eq below the lane), the first lane of each expert's run
+// (none of eq below it) writes the bucket, and the bucket's index is the
+// number of smaller experts' first lanes. Non-local routes take no part.
 __device__ void bucket_routes_wave(const RouteQuantArgs& a, const int* ids, int lane) {
-  const int e_own = lane < a.M * a.k ? ids[lane] - a.lb : -1;
-  const bool mine = e_own >= 0 && e_own < a.lc;
-  const int R = __popcll(__ballot(mine));  // local routes
-  uint32_t v = mine ? ((uint32_t)e_own << 16) | (uint32_t)lane : 0xFFFFFFFFu;
-#pragma unroll
-  for (int k = 2; k <= kWave; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const uint32_t w = (uint32_t)__shfl_xor((int)v, j, kWave);
-      const bool ascending = (lane & k) == 0;
-      const bool lower = (lane & j) == 0;
-      v = (lower == ascending) ? min(v, w) : max(v, w);
-    }
+  const int e = lane < a.M * a.k ? ids[lane] - a.lb : -1;
+  const bool mine = e >= 0 && e < a.lc;
+  const uint64_t below = (1ull << lane) - 1ull;
+  uint64_t eq = __ballot(mine), lt = 0;
+  const int bits = 32 - __builtin_clz((unsigned)max(a.lc - 1, 1));
+  for (int b = bits - 1; b >= 0; --b) {
+    const bool one = mine && ((e >> b) & 1);
+    const uint64_t ones = __ballot(one);
+    lt |= one ? eq & ~ones : 0ull;
+    eq &= one ? ones : ~ones;
   }
-  const int e = (int)(v >> 16);
-  const int prev = __shfl_up(e, 1, kWave);
-  const bool valid = lane < R;
-  const bool first = valid && (lane == 0 || e != prev);
+  const int pos = __popcll(eq & below);  // place in the expert's run
+  const int off = __popcll(lt);          // routes of smaller experts
+  const int cnt = __popcll(eq);
+  const bool first = mine && pos == 0;
   const uint64_t starts = __ballot(first);
-  const int route = (int)(v & 0xFFFFu);
-  if (valid) a.b.routes[lane] = route;
-  const uint64_t later = lane == kWave - 1 ? 0ull : starts >> (lane + 1);
-  const int next = later ? lane + 1 + __builtin_ctzll(later) : R;  // end of the run (first lanes)
+  if (mine) a.b.routes[off + pos] = lane;
   if (first) {
-    const int u = __popcll(starts & ((1ull << lane) - 1ull));
+    const int u = __popcll(starts & lt);
     a.b.uexp[u] = e;
-    a.b.uoff[u] = lane;
-    a.b.ucnt[u] = next - lane;
+    a.b.uoff[u] = off;
+    a.b.ucnt[u] = cnt;
   }
   if (lane == 0) a.b.ctrl[1] = __popcll(starts);
   const int jr = a.job_routes;
   if (jr > 0) {
-    // each run cut into jobs of jr entries: a scan of the runs' job counts
-    // gives their first jobs; the run's start, end and first job then reach
-    // every lane of the run through an inclusive max-scan (all three rise
-    // from run to run)
-    const int nj = first ? (next - lane + jr - 1) / jr : 0;
-    int inc = nj;
-    int rs = first ? lane : -1, re = first ? next : -1;
+    // each run cut into jobs of jr routes; a run's first job is the sum of
+    // the smaller experts' job counts, taken one bit of the counts at a
+    // time (a count is at most 64)
+    const int nj = (cnt + jr - 1) / jr;
+    int jb = 0, total = 0;
 #pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int up = __shfl_up(inc, o, kWave);
-      if (lane >= o) inc += up;
+    for (int b = 0; b < 7; ++b) {
+      const uint64_t has = __ballot(first && ((nj >> b) & 1));
+      jb += __popcll(has & lt) << b;
+      total += __popcll(has) << b;
     }
-    int rb = first ? inc - nj : -1;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int up_s = __shfl_up(rs, o, kWave), up_e = __shfl_up(re, o, kWave), up_b = __shfl_up(rb, o, kWave);
-      if (lane >= o) {
-        rs = max(rs, up_s);
-        re = max(re, up_e);
-        rb = max(rb, up_b);
-      }
+    if (mine) {
+      a.b.rjob[lane] = jb + pos / jr;
+      if (pos % jr == 0) a.b.jobs[jb + pos / jr] = make_int4(e, off + pos, min(jr, cnt - pos), 0);
     }
-    if (valid) {
-      const int pos = lane - rs, j = rb + pos / jr;
-      a.b.rjob[route] = j;
-      if (pos % jr == 0) a.b.jobs[j] = make_int4(e, lane, min(jr, re - lane), 0);
-    }
-    const int jobs = __shfl(inc, kWave - 1, kWave);
-    if (lane == 0) a.b.ctrl[2] = jobs;
+    if (lane == 0) a.b.ctrl[2] = total;
   }
 }
 
@@ -395,18 +393,27 @@ __device__ __forceinline__ void bucket_any(const RouteQuantArgs& a, const Lds& l
 __global__ __launch_bounds__(kThreads) void route_quant_kernel(RouteQuantArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   __shared__ int is_last;
+  // Every line of the argument block is read here, under one wait: read at
+  // first use, the bucketing's pointers and the grid size each cost a memory
+  // round trip in the middle of the kernel.
+  asm volatile("" ::"s"(a.logits), "s"(a.lc), "s"(a.b.rjob), "s"(gridDim.x));
   const Lds l = carve(lds, a.E, a.words, a.M * a.k);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int tpw = tokens_per_wg(a.M);
-  const int t0 = blockIdx.x * tpw;
-  const int ntok = min(tpw, a.M - t0);
-  // the routing waves (one per token) and the quantising waves run side by side
-  if (wave < tpw) {
-    if (wave < ntok) route_token_any(a, t0 + wave, lane, l.ids);
+  const int gr = routing_wgs(a.M);
+  const bool routing = (int)blockIdx.x < gr;
+  // the routing waves (one per token) and the quantising waves run side by
+  // side; the quantising waves of every workgroup share out the blocks
+  if (routing && wave < tpw) {
+    const int t = blockIdx.x * tpw + wave;
+    if (t < a.M) route_token_any(a, t, lane, l.ids);
   } else {
-    quant_tokens(a, t0, ntok, tpw * kWave);
+    const int qw = kWaves - tpw;  // quantising waves of a routing workgroup
+    const int w = routing ? blockIdx.x * qw + wave - tpw : gr * qw + (blockIdx.x - gr) * kWaves + wave;
+    quant_blocks(a, w * (kWave / 8) + lane / 8, (gr * qw + (gridDim.x - gr) * kWaves) * (kWave / 8));
   }
-  if (gridDim.x == 1) {
+  if (!routing) return;
+  if (gr == 1) {
     __syncthreads();
     bucket_any(a, l);
     return;
@@ -419,8 +426,7 @@ __global__ __launch_bounds__(kThreads) void route_quant_kernel(RouteQuantArgs a)
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0)
-    is_last = __hip_atomic_fetch_add(a.b.ctrl, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              (int)gridDim.x - 1;
+    is_last = __hip_atomic_fetch_add(a.b.ctrl, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gr - 1;
   __syncthreads();
   if (!is_last) return;
   if (threadIdx.x == 0) __hip_atomic_store(a.b.ctrl, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -450,8 +456,7 @@ size_t route_quant_lds_bytes(int E, int words, int routes) {
 }
 
 hipError_t launch_route_quant(const RouteQuantArgs& a, hipStream_t s) {
-  const int tpw = tokens_per_wg(a.M);
-  const int grid = (a.M + tpw - 1) / tpw;
+  const int grid = routing_wgs(a.M) + quant_wgs(a.M, a.H);
   hipLaunchKernelGGL(route_quant_kernel, dim3(grid), dim3(kThreads),
                      route_quant_lds_bytes(a.E, a.words, a.M * a.k), s, a);
   return hipGetLastError();
