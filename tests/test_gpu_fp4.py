@@ -150,6 +150,25 @@ def check_jobs(moe, shape, ids):
     assert np.array_equal(routes[:local.sum()], np.concatenate([np.nonzero(e_loc == e)[0] for e in experts]))
 
 
+def test_fp4_jobs_one_wave():
+    """At most 64 routes, so one wave groups them (ballot ranking): several
+    jobs per expert, and routes outside the local range left out."""
+    shape = TINY.with_(M=12, hidden=512, inter=256, experts=10, top_k=4, local_begin=3, local_count=5)
+    inp = synth.make_inputs(shape, seed=35, device=DEV)
+    inp.bias[[3, 5]] += 10.0  # experts 3 and 5 take every token: 12 routes, 6 jobs each
+    moe = make_fp4(inp)
+    ref, _ = check_fp4_layer(moe, inp)
+    check_jobs(moe, shape, ref["ids"])
+
+
+def test_fp4_quantising_workgroups():
+    """3 tokens of H = 7168: the x staging is shared with a workgroup that
+    only quantises; the staged codes and scales bit-exact."""
+    shape = TINY.with_(M=3, hidden=7168, inter=256, experts=8, top_k=3, local_begin=0, local_count=8)
+    inp = synth.make_inputs(shape, seed=36, device=DEV)
+    check_fp4_layer(make_fp4(inp), inp)
+
+
 def test_fp4_jobs_and_slots():
     """Many routes per expert (several jobs, so several passes over its
     weights) and a local range covering all experts; the job table bit-exact."""

@@ -181,6 +181,13 @@ SHAPES = [
     ("bf16_logits", dict(M=6, hidden=512, inter=256, experts=40, top_k=5, logits_dtype="bf16")),
     ("ue8m0", dict(M=4, hidden=512, inter=256, experts=12, top_k=4, ue8m0_act=True)),
     ("wide_k", dict(M=3, hidden=2304, inter=640, experts=24, top_k=4)),
+    # 3 x 56 blocks of x: more than the routing workgroup's quantising waves
+    # take one each, so a workgroup that only quantises joins
+    ("quant_wgs_m3", dict(M=3, hidden=7168, inter=256, experts=12, top_k=4)),
+    # the largest hidden the GEMM workgroup's LDS takes (652 blocks per
+    # token): the quantising-only workgroups stop at sixteen, so some groups
+    # of eight lanes take two blocks
+    ("max_hidden_m4", dict(M=4, hidden=83456, inter=128, experts=4, top_k=2)),
 ]
 
 
