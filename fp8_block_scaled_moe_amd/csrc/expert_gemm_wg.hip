@@ -362,12 +362,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   __shared__ int claimed[kRoutesPerPass];
   __shared__ int nclaim;
   const GemmProblem& a = args.p[1];
-  const int kparts = a.kparts;
+  // The argument lines the first unit needs are read under one wait, and
+  // the first unit's job beside the job count: read at first use, each
+  // would add a memory round trip before the first weight request. The job
+  // index is clamped to the routes (jobs never outnumber them), so the early
+  // read stays inside the table; past the count it is not used.
+  int kparts = a.kparts;  // passed through the read below, so nothing computes ahead of it
+  asm volatile("" : "+s"(kparts) : "s"(a.w), "s"(a.b.jobs), "s"(a.b.ctrl), "s"(a.R));
   const int rows_wg = kRowsPerWg / kparts;
   const int per_expert = a.N / rows_wg;
-  const int total = a.b.ctrl[2] * per_expert;  // jobs x units per job
-  const int G = gridDim.x;
   int u = blockIdx.x;
+  const int j0 = u / per_expert;
+  const int4 job0 = a.b.jobs[min(j0, a.R - 1)];
+  const int total = a.b.ctrl[2] * per_expert;  // jobs x units per job
+  asm volatile("" ::"v"(job0.x), "v"(job0.y), "v"(job0.z));  // keeps the read above the exit
+  const int G = gridDim.x;
   if (u >= total) return;  // more slots than units: the whole workgroup exits
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -442,7 +451,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   };
 
   // The first unit: requests, then staging, as the one-unit kernel does.
-  UnitRef cur = unit_ref(u);
+  UnitRef cur;
+  cur.tile = u - j0 * per_expert;
+  cur.e = job0.x;
+  cur.off = job0.y;
+  cur.cnt = job0.z;
   const uint8_t* pw = weights_of(cur);
 #pragma unroll
   for (int q = 0; q < kDepth; ++q) load_w(pw, q, q);
