@@ -38,21 +38,28 @@ __device__ __forceinline__ void swiglu_finish(float up0, float up1, float g0, fl
   if (lane == 0) hs[(size_t)r * nblk + c] = s;
 }
 
-// One wave: route r, 128-block c of the hidden, from the fixed-order sum of
-// GEMM1's split partials. Rows 0..I-1 of GEMM1 are up, I..2I-1 gate.
-__device__ __forceinline__ void swiglu_route_block(const SwigluArgs& a, int r, int c, int lane) {
+// Split s of GEMM1's partials for route r, 128-block c of the hidden, this
+// lane's two columns: (up, up, gate, gate). Rows 0..I-1 of GEMM1 are up,
+// I..2I-1 gate.
+__device__ __forceinline__ float4 swiglu_split(const SwigluArgs& a, int r, int c, int lane, int s) {
   const int j = c * kTile + 2 * lane;
-  const size_t row = (size_t)2 * a.I;
-  float up0 = 0.f, up1 = 0.f, g0 = 0.f, g1 = 0.f;
+  const float* p = a.part + ((size_t)s * a.R + r) * (size_t)(2 * a.I);
+  const float2 u = *reinterpret_cast<const float2*>(p + j);
+  const float2 g = *reinterpret_cast<const float2*>(p + a.I + j);
+  return make_float4(u.x, u.y, g.x, g.y);
+}
+
+// One wave: route r, 128-block c of the hidden, from the fixed-order sum of
+// GEMM1's split partials; `first` is split 0, read by the caller.
+__device__ __forceinline__ void swiglu_route_block(const SwigluArgs& a, int r, int c, int lane, float4 first) {
+  float up0 = 0.f + first.x, up1 = 0.f + first.y, g0 = 0.f + first.z, g1 = 0.f + first.w;
 #pragma unroll 4
-  for (int s = 0; s < a.splits; ++s) {
-    const float* p = a.part + ((size_t)s * a.R + r) * row;
-    const float2 u = *reinterpret_cast<const float2*>(p + j);
-    const float2 g = *reinterpret_cast<const float2*>(p + a.I + j);
-    up0 += u.x;
-    up1 += u.y;
-    g0 += g.x;
-    g1 += g.y;
+  for (int s = 1; s < a.splits; ++s) {
+    const float4 v = swiglu_split(a, r, c, lane, s);
+    up0 += v.x;
+    up1 += v.y;
+    g0 += v.z;
+    g1 += v.w;
   }
   swiglu_finish(up0, up1, g0, g1, a.limit, a.I, a.hq, a.hs, r, c, lane);
 }
@@ -148,29 +155,45 @@ __device__ __forceinline__ void swiglu_fp4_block(const SwigluArgs& a, int r, int
 // (nvfp4-megamoe-kernel README, slot representation). Slots whose expert is
 // not local are zero and add nothing. With a shared expert, the otherwise
 // idle second wave writes its BF16 output for the same columns. `lds` holds
-// k * 64 floats. Contains a barrier: every thread of the workgroup must call
-// it.
-__device__ __forceinline__ void combine_token_tile(const CombineArgs& a, int t, int col0, float* lds) {
+// k * 64 floats and `wl` k floats. Contains a barrier: every thread of the
+// workgroup must call it.
+//
+// Reads that do not depend on each other are issued together: the token's
+// routing weights at the start (into `wl` before the barrier), and a pick's
+// first split beside its expert id (the row exists for every route; a
+// non-local pick, and the FP4 form, which finds its splits through the
+// stream, drop it).
+__device__ __forceinline__ void combine_token_tile(const CombineArgs& a, int t, int col0, float* lds, float* wl) {
   const int tid = threadIdx.x;
   const int c = tid & 63, jg = tid >> 6;
   const int R = a.M * a.k;
+  const float w_own = tid < a.k ? a.weights[(size_t)t * a.k + tid] : 0.f;
   for (int j = jg; j < a.k; j += 4) {
     const int r = t * a.k + j;
+    const float first = a.part[(size_t)r * a.H + col0 + c];  // split 0 (slot 0 in the FP4 form)
     const int e = a.ids[r] - a.lb;
+    asm volatile("" ::"v"(first));  // keeps the read beside the id's
     float v = 0.f;  // non-local experts: a zero slot, nothing added below
     if (e >= 0 && e < a.lc) {
-      const int splits = a.fp4 ? stream_slots(a.stream, r, col0 + c) : a.splits;
+      if (a.fp4) {
+        const int splits = stream_slots(a.stream, r, col0 + c);
 #pragma unroll 4
-      for (int s = 0; s < splits; ++s) v += a.part[((size_t)s * R + r) * a.H + col0 + c];
+        for (int s = 0; s < splits; ++s) v += a.part[((size_t)s * R + r) * a.H + col0 + c];
+      } else {
+        v += first;
+#pragma unroll 4
+        for (int s = 1; s < a.splits; ++s) v += a.part[((size_t)s * R + r) * a.H + col0 + c];
+      }
     }
     const uint32_t b = bf16_bits(v);
     a.slots[(size_t)r * a.H + col0 + c] = (uint16_t)b;
     lds[j * 64 + c] = bf16_value(b);
   }
+  if (tid < a.k) wl[tid] = w_own;
   __syncthreads();
   if (tid < 64) {
     float acc = 0.f;
-    for (int j = 0; j < a.k; ++j) acc = fmaf(a.weights[(size_t)t * a.k + j], lds[j * 64 + c], acc);
+    for (int j = 0; j < a.k; ++j) acc = fmaf(wl[j], lds[j * 64 + c], acc);
     a.combined[(size_t)t * a.H + col0 + c] = (uint16_t)bf16_bits(acc);
   } else if (tid < 128 && a.spart) {
     // the shared expert's output: fixed-order split sum rounded once to BF16

@@ -11,18 +11,28 @@ constexpr int kThreads = 256;
 // One wave per (route, 128-block of the hidden), then one per (token,
 // 128-block of the shared hidden).
 __global__ __launch_bounds__(kThreads) void swiglu_requant_kernel(SwigluArgs a) {
+  // every line of the argument block under one wait (the ids pointer sits in
+  // the last): read at first use, a line costs a memory round trip
+  asm volatile("" ::"s"(a.part), "s"(a.sue8m0), "s"(a.ids));
   const int nblk = a.I / kTile;
   const int gw = blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int routed = a.R * nblk;
   if (gw < routed) {
-    const int r = gw / nblk;
+    const int r = gw / nblk, c = gw % nblk;
+    if (a.fp4) {
+      const int e = a.ids[r] - a.lb;
+      if (e < 0 || e >= a.lc) return;  // a route of another GPU's expert: nothing to compute
+      swiglu_fp4_block(a, r, c, lane);
+      return;
+    }
+    // the first split is read beside the expert id, not after it (its row
+    // exists for every route; a route of another GPU's expert drops it)
+    const float4 first = swiglu_split(a, r, c, lane, 0);
     const int e = a.ids[r] - a.lb;
-    if (e < 0 || e >= a.lc) return;  // a route of another GPU's expert: nothing to compute
-    if (a.fp4)
-      swiglu_fp4_block(a, r, gw % nblk, lane);
-    else
-      swiglu_route_block(a, r, gw % nblk, lane);
+    asm volatile("" ::"v"(first.x), "v"(first.y), "v"(first.z), "v"(first.w));  // keeps the read above the exit
+    if (e < 0 || e >= a.lc) return;
+    swiglu_route_block(a, r, c, lane, first);
     return;
   }
   if (!a.spart) return;
@@ -50,8 +60,10 @@ __global__ void unpack_ue8m0_kernel(const int32_t* packed, int n, int k, float* 
 // One workgroup per (token, 64 hidden columns).
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   __shared__ float lds[kMaxTopK * 64];
+  __shared__ float wl[kMaxTopK];
+  asm volatile("" ::"s"(a.part), "s"(a.ids), "s"(a.stream.wgs));  // the argument block under one wait
   const int tiles = a.H / 64;
-  combine_token_tile(a, blockIdx.x / tiles, (blockIdx.x % tiles) * 64, lds);
+  combine_token_tile(a, blockIdx.x / tiles, (blockIdx.x % tiles) * 64, lds, wl);
 }
 
 }  // namespace
