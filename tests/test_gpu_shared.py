@@ -127,6 +127,25 @@ def test_shared_small(path, packed):
         assert torch.equal(a, b)
 
 
+def test_shared_own_quant_with_quantising_workgroups():
+    """3 tokens of H = 7168 with the shared expert on its own scale rule
+    (UE8M0, the routed x on plain FP32 scales): both quantisations of x are
+    shared with a workgroup that only quantises, and both are bit-exact."""
+    shape = SMALL.with_(M=3, hidden=7168, inter=256, experts=8, top_k=2, shared_inter=256)
+    inp = synth.make_inputs(shape, seed=25, device=DEV)
+    moe = make(inp)
+    slots, ids, weights, combined, shared_out = run(moe, inp)
+    ref = oracle_shared(inp)
+    check_shared_quant(moe, inp, ref, shape.M)
+    lref = oracle_layer(inp)
+    xq = stage(moe, "x_q", shape.M * shape.hidden, torch.uint8).cpu().numpy().reshape(shape.M, -1)
+    xs = host(stage(moe, "x_s", shape.M * (shape.hidden // 128), torch.float32)).reshape(shape.M, -1)
+    assert np.array_equal(xq, lref["x_q"]) and np.array_equal(xs, lref["x_s"])
+    assert np.array_equal(ids.cpu().numpy(), lref["ids"])
+    assert_rows_close(host(combined), lref["combined"], what="combined")
+    assert_rows_close(host(shared_out), ref["out"], what="shared_out")
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_shared_exact_pow2(path):
     """Integer weights and activations with power-of-two scales: every gate_up
