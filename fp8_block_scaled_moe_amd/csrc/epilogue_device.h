@@ -155,45 +155,29 @@ __device__ __forceinline__ void swiglu_fp4_block(const SwigluArgs& a, int r, int
 // (nvfp4-megamoe-kernel README, slot representation). Slots whose expert is
 // not local are zero and add nothing. With a shared expert, the otherwise
 // idle second wave writes its BF16 output for the same columns. `lds` holds
-// k * 64 floats and `wl` k floats. Contains a barrier: every thread of the
-// workgroup must call it.
-//
-// Reads that do not depend on each other are issued together: the token's
-// routing weights at the start (into `wl` before the barrier), and a pick's
-// first split beside its expert id (the row exists for every route; a
-// non-local pick, and the FP4 form, which finds its splits through the
-// stream, drop it).
-__device__ __forceinline__ void combine_token_tile(const CombineArgs& a, int t, int col0, float* lds, float* wl) {
+// k * 64 floats. Contains a barrier: every thread of the workgroup must call
+// it.
+__device__ __forceinline__ void combine_token_tile(const CombineArgs& a, int t, int col0, float* lds) {
   const int tid = threadIdx.x;
   const int c = tid & 63, jg = tid >> 6;
   const int R = a.M * a.k;
-  const float w_own = tid < a.k ? a.weights[(size_t)t * a.k + tid] : 0.f;
   for (int j = jg; j < a.k; j += 4) {
     const int r = t * a.k + j;
-    const float first = a.part[(size_t)r * a.H + col0 + c];  // split 0 (slot 0 in the FP4 form)
     const int e = a.ids[r] - a.lb;
-    asm volatile("" ::"v"(first));  // keeps the read beside the id's
     float v = 0.f;  // non-local experts: a zero slot, nothing added below
     if (e >= 0 && e < a.lc) {
-      if (a.fp4) {
-        const int splits = stream_slots(a.stream, r, col0 + c);
+      const int splits = a.fp4 ? stream_slots(a.stream, r, col0 + c) : a.splits;
 #pragma unroll 4
-        for (int s = 0; s < splits; ++s) v += a.part[((size_t)s * R + r) * a.H + col0 + c];
-      } else {
-        v += first;
-#pragma unroll 4
-        for (int s = 1; s < a.splits; ++s) v += a.part[((size_t)s * R + r) * a.H + col0 + c];
-      }
+      for (int s = 0; s < splits; ++s) v += a.part[((size_t)s * R + r) * a.H + col0 + c];
     }
     const uint32_t b = bf16_bits(v);
     a.slots[(size_t)r * a.H + col0 + c] = (uint16_t)b;
     lds[j * 64 + c] = bf16_value(b);
   }
-  if (tid < a.k) wl[tid] = w_own;
   __syncthreads();
   if (tid < 64) {
     float acc = 0.f;
-    for (int j = 0; j < a.k; ++j) acc = fmaf(wl[j], lds[j * 64 + c], acc);
+    for (int j = 0; j < a.k; ++j) acc = fmaf(a.weights[(size_t)t * a.k + j], lds[j * 64 + c], acc);
     a.combined[(size_t)t * a.H + col0 + c] = (uint16_t)bf16_bits(acc);
   } else if (tid < 128 && a.spart) {
     // the shared expert's output: fixed-order split sum rounded once to BF16

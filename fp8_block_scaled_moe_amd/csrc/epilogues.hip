@@ -60,10 +60,8 @@ __global__ void unpack_ue8m0_kernel(const int32_t* packed, int n, int k, float* 
 // One workgroup per (token, 64 hidden columns).
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   __shared__ float lds[kMaxTopK * 64];
-  __shared__ float wl[kMaxTopK];
-  asm volatile("" ::"s"(a.part), "s"(a.ids), "s"(a.stream.wgs));  // the argument block under one wait
   const int tiles = a.H / 64;
-  combine_token_tile(a, blockIdx.x / tiles, (blockIdx.x % tiles) * 64, lds, wl);
+  combine_token_tile(a, blockIdx.x / tiles, (blockIdx.x % tiles) * 64, lds);
 }
 
 }  // namespace
