@@ -272,6 +272,24 @@ def test_zero_inputs():
     assert not slots.float().abs().max().item() and not combined.float().abs().max().item()
 
 
+@pytest.mark.parametrize("E,k", [(896, 16), (256, 8), (1024, 32)])
+def test_routing_ties_and_infinities(E, k):
+    """Logits from {-inf, -1, 0, 1, +inf} and biases from {0, 0.5}: most
+    keys tie, across lanes and across the experts a lane holds, so the picks
+    are decided by the lower-index rule throughout; +inf and -inf logits give
+    scores of exactly 1 and 0."""
+    shape = synth.CONFIGS["tiny"].with_(M=5, hidden=256, inter=128, experts=E, top_k=k)
+    inp = synth.make_inputs(shape, seed=18, device=DEV)
+    g = torch.Generator().manual_seed(19)
+    vals = torch.tensor([-float("inf"), -1.0, 0.0, 1.0, float("inf")])
+    inp.logits.copy_(vals[torch.randint(0, 5, (shape.M, E), generator=g)])
+    inp.bias.copy_(torch.tensor([0.0, 0.5])[torch.randint(0, 2, (E,), generator=g)])
+    slots, ids, weights, combined = run(make(inp), inp)
+    ref = oracle_layer(inp)
+    check_routing(ids, weights, ref)
+    assert_rows_close(host(combined), ref["combined"], what="combined")
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_deterministic_and_token_independent(path):
     shape = synth.CONFIGS["tiny"].with_(M=9, hidden=512, inter=256, experts=20, top_k=4)
