@@ -147,13 +147,15 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
 
 
-def _need(t: torch.Tensor, name: str, dtypes, dev) -> None:
+def _need(t: torch.Tensor, name: str, dtypes, dev, align: int = 16) -> None:
     if t.device != dev:
         raise ValueError(f"{name} must be on {dev}, got {t.device}")
     if t.dtype not in dtypes:
         raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if t.data_ptr() % align:
+        raise ValueError(f"{name} must start on a {align}-byte boundary (a slice can be copied with .clone())")
 
 
 _FP8 = (torch.uint8, torch.float8_e4m3fn)
@@ -270,7 +272,7 @@ class MoeDecode:
         has a shared expert."""
         _need(x, "x", (torch.bfloat16,), self.device)
         _need(logits, "logits", (self.logits_dtype,), self.device)
-        _need(bias, "bias", (torch.float32,), self.device)
+        _need(bias, "bias", (torch.float32,), self.device, align=4)
         out = self.outputs(x.shape[0])
         shared = None
         if self.shared_inter:
