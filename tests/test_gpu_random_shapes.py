@@ -57,3 +57,37 @@ def test_random_configuration(i):
     want = np.where(local[:, None], ref["slots"], 0.0)
     assert_rows_close(host(slots), want, what=f"slots ({path}, {mode})")
     assert_rows_close(host(combined), oracle.combine(want, ref["weights"]), what=f"combined ({path}, {mode})")
+
+
+def draw_fp4(i):
+    rng = np.random.default_rng(3000 + i)
+    E = int(rng.choice([4, 9, 24, 64, 384]))
+    k = int(rng.integers(1, min(E, 8) + 1))
+    lb = int(rng.integers(0, E))
+    lc = int(rng.integers(1, E - lb + 1))
+    shape = synth.CONFIGS["fp4_share"].with_(
+        name=f"random_fp4_{i}", M=int(rng.choice([1, 2, 5, 8, 16, 33])),
+        hidden=256 * int(rng.integers(1, 9)), inter=256 * int(rng.integers(1, 5)), experts=E, top_k=k,
+        local_begin=lb, local_count=lc, logits_dtype=str(rng.choice(["f32", "bf16"])))
+    return shape
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_fp4_configuration(i):
+    from tests.helpers import oracle_layer_fp4
+    shape = draw_fp4(i)
+    inp = synth.make_inputs(shape, seed=4000 + i, device=DEV)
+    moe = MoeDecode(inp.w13, inp.w13_scale, inp.w2, inp.w2_scale, top_k=shape.top_k, limit=shape.limit,
+                    routed_scale=shape.routed_scale, max_tokens=shape.M, logits_dtype=inp.logits.dtype,
+                    weight_format="nvfp4", experts=shape.experts, local_begin=shape.local_begin)
+    slots, ids, weights, combined = moe(inp.x, inp.logits, inp.bias)
+    torch.cuda.synchronize()
+    ref = oracle_layer_fp4(inp)
+    assert np.array_equal(ids.cpu().numpy(), ref["ids"]), f"{shape}"
+    np.testing.assert_allclose(host(weights), ref["weights"], rtol=WEIGHT_RTOL, atol=0)
+    local = ref["local"]
+    got = host(slots)
+    assert not got[~local].any(), "slots of non-local experts must be zero"
+    if local.any():
+        assert_rows_close(got[local], ref["slots"][local], what="slots")
+    assert_rows_close(host(combined), ref["combined"], what="combined")
