@@ -242,18 +242,26 @@ def moe_decode(x, logits, bias, expert: ExpertFn, *, top_k: int, routed_scale: f
 # --------------------------------------------------------------------------
 
 def unpack_ue8m0(packed, n: int, k: int) -> np.ndarray:
-    """FP32 [n/128, k/128] scales from DeepGEMM's packed UE8M0 words
-    (int32 [n, k/512], byte g % 4 of word g // 4 = biased exponent of K group g;
-    every row of a 128-row block must carry the same exponent)
-    ("shared_expert" page, block_scales)."""
-    p = np.asarray(packed).astype(np.int64) & 0xFFFFFFFF
-    groups = k // TILE
-    g = np.arange(groups)
-    exps = (p[:, g // 4] >> (8 * (g % 4))) & 0xFF          # [n, groups]
-    rows = exps.reshape(n // TILE, TILE, groups)
-    if not np.all(rows == rows[:, :1]):
-        raise ValueError("scales vary inside a 128-row block")
-    return np.ldexp(1.0, rows[:, 0] - 127)
+    """FP32 [n/128, k/128] block scales from packed UE8M0 words.
+
+    Layout ("shared_expert" page, block_scales docstring): an int32 word per
+    row and per four K blocks of 128; the exponent byte of K block b sits in
+    bits 8*(b%4)..8*(b%4)+7 of word b//4. The scale of a (128-row, K) block is
+    the binary32 whose bit pattern is that byte shifted into the exponent field
+    (byte << 23), so byte 0 gives +0.0, 127 gives 1.0 and 255 gives +inf. The
+    page takes the byte of the block's first row and requires the other 127
+    rows to repeat it; a block where they differ is rejected (ValueError)."""
+    words = np.asarray(packed).astype(np.int64) & 0xFFFFFFFF
+    nblocks = k // TILE
+    out = np.empty((n // TILE, nblocks), np.float64)
+    for b in range(nblocks):
+        byte = (words[:, b // 4] >> (8 * (b % 4))) & 0xFF       # one per row
+        by_block = byte.reshape(n // TILE, TILE)
+        if np.any(by_block != by_block[:, :1]):
+            raise ValueError(f"UE8M0 exponent byte not uniform over a 128-row block (K block {b})")
+        bits = (by_block[:, 0] << 23).astype(np.uint32)
+        out[:, b] = bits.view(np.float32)
+    return out
 
 
 def shared_expert(x, sw13, sw13_scale, sw2, sw2_scale, *, limit: float,

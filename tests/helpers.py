@@ -73,3 +73,24 @@ def assert_rows_close(got, ref, rtol=ROW_RTOL, what="rows"):
     bad = np.nonzero(e > rtol)[0]
     assert bad.size == 0, f"{what}: {bad.size} rows over {rtol} x rms (worst {e.max():.3g} at row {int(e.argmax())})"
     return float(e.max()) if e.size else 0.0
+
+
+def bf16_step(v):
+    """Spacing of BF16 values at |v| (the smallest normal spacing below 2**-126)."""
+    _, e = np.frexp(np.maximum(np.abs(v), 2.0**-126))
+    return np.ldexp(1.0, e - 8)
+
+
+def check_combine(slots, weights, combined, max_differ=1e-3):
+    """The GPU's combine against the oracle's combine of the GPU's own slot rows
+    and weights: within one BF16 step everywhere and bit-exact on all but
+    max_differ of the elements (an FP32 sum in another order may round to the
+    neighbouring BF16 value). Rounding the weights, or applying them twice or
+    not at all, fails."""
+    got = host(combined)
+    want = oracle.combine(host(slots), host(weights))
+    diff = got != want
+    step = bf16_step(np.maximum(np.abs(got), np.abs(want)))
+    far = np.abs(got - want) > step
+    assert not far.any(), f"combine: {far.sum()} elements beyond one BF16 step"
+    assert diff.mean() <= max_differ, f"combine: {diff.mean():.3%} of elements differ"

@@ -280,3 +280,25 @@ def test_shared_gate_rows_first():
     assert np.all(r["gate_up"][0, :Is] < -50)
     assert np.max(np.abs(r["act"])) < 1e-6
     assert np.max(np.abs(base["act"][:1])) > 1e-2
+
+
+def test_combine_check_catches_rounded_or_repeated_weights():
+    """The GPU tests' combine check (the oracle's combine of the GPU's own slots
+    and weights, one BF16 step, >= 99.9% bit-exact) fails a combine that rounds
+    the weights to BF16 or applies them twice, and passes the FP32 sum in
+    pick order rounded once."""
+    from tests.helpers import check_combine
+    rng = np.random.default_rng(31)
+    M, k, H = 16, 8, 1024
+    slots = torch.from_numpy(bf16_round(rng.standard_normal((M * k, H)))).to(torch.bfloat16)
+    w = torch.from_numpy(f32(rng.uniform(0.05, 0.6, (M, k)))).float()
+    rows = slots.float().view(M, k, H)
+    acc = torch.zeros(M, H)
+    for j in range(k):                      # FP32 multiply-add in pick order
+        acc = acc + w[:, j:j + 1] * rows[:, j]
+    check_combine(slots, w, acc.to(torch.bfloat16))
+    wb = w.to(torch.bfloat16).float()
+    with pytest.raises(AssertionError):
+        check_combine(slots, w, torch.einsum("tk,tkh->th", wb, rows).to(torch.bfloat16))
+    with pytest.raises(AssertionError):
+        check_combine(slots, w, torch.einsum("tk,tkh->th", w * w, rows).to(torch.bfloat16))
