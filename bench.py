@@ -9,7 +9,8 @@ the 256 MB MALL; the flush is outside the per-layer events. Counted bytes =
 distinct experts touched x (W13 + W2 FP8 bytes + FP32 scales), plus the shared
 expert's weights and scales for a workload that has one. Prints one JSON line
 (one per M with --sweep). The default workload is the DeepSeek-V3-shaped decode
-at M=4.
+at M=4; its line also carries config.sweep, the same metric at M = 1, 2, 4, 8,
+16, 32 and 64 (one 64-token handle; the step at M runs its first M tokens).
 """
 
 from __future__ import annotations
@@ -98,6 +99,8 @@ def parse():
                    choices=["auto", "separate", "combine_in_gemm2", "swiglu_in_gemm1"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--sweep", default="", help="comma-separated M values: one JSON line each")
+    p.add_argument("--no-sweep", action="store_true",
+                   help="leave out config.sweep (M = 1..64) of the default dsv3 line")
     p.add_argument("--calibrate", action="store_true",
                    help="time a plain 1 GiB device copy and a 4 GiB read-only sum instead")
     p.add_argument("--with-copy", action="store_true",
@@ -190,7 +193,7 @@ def cpu_baseline(inp, counted_bytes: int, min_seconds: float = 10.0, max_runs: i
                       f"host memory"}
 
 
-def run_one(args, shape, inp, moe, flush):
+def run_one(args, shape, inp, moe, flush, per_kernel=True):
     dev = inp.x.device
     k = shape.top_k
     slots, ids, weights, combined = moe.outputs(shape.M)
@@ -226,14 +229,16 @@ def run_one(args, shape, inp, moe, flush):
     layer_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
 
     # pass 2: per-kernel times from events the library records between launches
-    moe.set_timing(True)
-    per = []
-    for i in range(args.steps):
-        flush.zero_()
-        step()
-        per.append(moe.last_timing()[:len(KERNELS)])
-    moe.set_timing(False)
-    per = np.array(per)
+    per = np.zeros((1, len(KERNELS)))
+    if per_kernel:
+        moe.set_timing(True)
+        per = []
+        for i in range(args.steps):
+            flush.zero_()
+            step()
+            per.append(moe.last_timing()[:len(KERNELS)])
+        moe.set_timing(False)
+        per = np.array(per)
     torch.cuda.synchronize()
     return dict(U=U, counted=counted, layer_ms=layer_ms, per_kernel_ms=per, wall_s=wall, ids=ids)
 
@@ -265,6 +270,43 @@ def boundary_steps_us(dev, reps: int = 200) -> dict:
         out[name] = round(a.elapsed_time(b) * 1e3 / reps, 2)
     out["shape"] = "T=5 tokens, D=3584, N=16 partials; calls back to back on the device, inputs L2-resident"
     return out
+
+
+SWEEP_MS = (1, 2, 4, 8, 16, 32, 64)
+
+
+def sweep(args, base, dev, flush) -> dict:
+    """The metric over M = 1..64: one handle for 64 tokens on the workload's
+    seeded inputs at M = 64; the step at M takes the first M tokens. Same
+    flush and timing as the headline (HIP events around each layer, median)."""
+    shape = base.with_(M=max(SWEEP_MS))
+    inp_all = synth.make_inputs(shape, seed=args.seed, device=dev)
+    moe = MoeDecode(inp_all.w13, inp_all.w13_scale, inp_all.w2, inp_all.w2_scale,
+                    top_k=shape.top_k, limit=shape.limit, routed_scale=shape.routed_scale,
+                    max_tokens=shape.M, logits_dtype=inp_all.logits.dtype,
+                    ue8m0_act=shape.ue8m0_act)
+    points = []
+    for M in SWEEP_MS:
+        sh = base.with_(M=M)
+        inp = synth.MoeInputs(shape=sh, seed=args.seed, x=inp_all.x[:M].contiguous(),
+                              logits=inp_all.logits[:M].contiguous(), bias=inp_all.bias,
+                              w13=inp_all.w13, w13_scale=inp_all.w13_scale, w2=inp_all.w2,
+                              w2_scale=inp_all.w2_scale)
+        r = run_one(args, sh, inp, moe, flush, per_kernel=False)
+        ms = float(np.median(r["layer_ms"]))
+        gbs = r["counted"] / (ms * 1e-3) / 1e9
+        points.append({"M": M, "unique_experts": r["U"], "counted_bytes": r["counted"],
+                       "us_per_layer": round(ms * 1e3, 2),
+                       "us_p10_p90": [round(float(np.quantile(r["layer_ms"], q)) * 1e3, 2)
+                                      for q in (0.1, 0.9)],
+                       "GB/s": round(gbs, 1), "pct_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2)})
+        print(f"# sweep M={M}: {ms * 1e3:.1f} us, {100 * gbs / PEAK_HBM_GBS:.1f}% of peak",
+              file=sys.stderr, flush=True)
+    moe.close()
+    del inp_all
+    return {"workload": f"{base.name} at M=64, seed {args.seed}; step M runs its first M tokens "
+                        "on one handle",
+            "points": points}
 
 
 def main():
@@ -367,6 +409,11 @@ def main():
             line["config"]["boundary_steps_us"] = boundary_steps_us(dev)
         if not args.no_cpu_baseline and M == Ms[0]:
             line["cpu_baseline"] = cpu_baseline(inp, r["counted"])
+        if not args.sweep and not args.no_sweep and args.workload == "dsv3":
+            moe.close()
+            del inp, inp_all
+            torch.cuda.empty_cache()
+            line["config"]["sweep"] = sweep(args, base, dev, flush)
         print(json.dumps(line), flush=True)
     moe.close()
     if args.with_copy:

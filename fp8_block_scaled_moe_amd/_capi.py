@@ -38,6 +38,7 @@ STAGES = {
     "part1": 7, "h_q": 8, "h_s": 9, "part2": 10,
     "shared_x_q": 11, "shared_x_s": 12, "shared_part1": 13, "shared_h_q": 14,
     "shared_h_s": 15, "shared_part2": 16, "jobs": 17, "route_jobs": 18,
+    "shared_scale13": 19, "shared_scale2": 20,
 }
 TIMING_SLOTS = ("route_quant", "gemm1", "swiglu_requant", "gemm2", "combine")
 
@@ -147,7 +148,20 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
 
 
-def _need(t: torch.Tensor, name: str, dtypes, dev, align: int = 16) -> None:
+def _need(t: torch.Tensor, name: str, dtypes, dev, align: int = 16, shape=None,
+          min_rows: bool = False) -> None:
+    """Device, dtype, contiguity, alignment and shape of one buffer. With
+    min_rows the first dimension may exceed shape[0] (a buffer with room for
+    more rows than this call uses); the others must match."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor, got {type(t).__name__}")
+    if shape is not None:
+        have = tuple(t.shape)
+        ok = (len(have) == len(shape) and have[1:] == tuple(shape[1:]) and
+              (have[0] >= shape[0] if min_rows else have[0] == shape[0]))
+        if not ok:
+            more = " (or more rows)" if min_rows else ""
+            raise ValueError(f"{name} has shape {have}, expected {tuple(shape)}{more}")
     if t.device != dev:
         raise ValueError(f"{name} must be on {dev}, got {t.device}")
     if t.dtype not in dtypes:
@@ -187,15 +201,27 @@ class MoeDecode:
                  weight_format: str = "fp8", experts: Optional[int] = None, local_begin: int = 0,
                  launch_mode: str = "auto"):
         self.device = w13.device
+        if weight_format not in WEIGHT_FORMATS:
+            raise ValueError(f"weight_format must be one of {sorted(WEIGHT_FORMATS)}")
         fp4 = weight_format == "nvfp4"
-        sdt = _FP8 if fp4 else (torch.float32,)
-        for t, n, d in ((w13, "w13", _FP8), (w2, "w2", _FP8), (w13_scale, "w13_scale", sdt),
-                        (w2_scale, "w2_scale", sdt)):
-            _need(t, n, d, self.device)
+        if w13.dim() != 3 or w13.shape[1] % 2:
+            raise ValueError(f"w13 must be [E, 2I, {'H/2' if fp4 else 'H'}], got {tuple(w13.shape)}")
         El, N1, H = w13.shape
         if fp4:
             H *= 2
+        I = N1 // 2
+        if fp4:   # packed E2M1 two per byte, a UE4M3 byte per 16 values along K
+            shapes = ((El, 2 * I, H // 2), (El, 2 * I, H // 16), (El, H, I // 2), (El, H, I // 16))
+        else:     # e4m3 bytes, FP32 per 128 x 128 block
+            shapes = ((El, 2 * I, H), (El, 2 * I // 128, H // 128), (El, H, I),
+                      (El, H // 128, I // 128))
+        sdt = _FP8 if fp4 else (torch.float32,)
+        for t, n, d, want in zip((w13, w13_scale, w2, w2_scale), ("w13", "w13_scale", "w2", "w2_scale"),
+                                 (_FP8, sdt, _FP8, sdt), shapes):
+            _need(t, n, d, self.device, shape=want)
         E = El if experts is None else experts
+        if not 0 <= local_begin or local_begin + El > E:
+            raise ValueError(f"local experts [{local_begin}, {local_begin + El}) must lie in [0, {E})")
         self.experts, self.hidden, self.inter, self.top_k = E, H, N1 // 2, top_k
         self.local_begin, self.local_experts = local_begin, El
         self.max_tokens = max_tokens
@@ -224,7 +250,7 @@ class MoeDecode:
             if sw13_scale.dtype != sw2_scale.dtype:
                 raise ValueError("sw13_scale and sw2_scale must have the same format")
             Is = sw13.shape[0] // 2
-            if tuple(sw13.shape) != (2 * Is, H) or tuple(sw2.shape) != (H, Is):
+            if sw13.dim() != 2 or tuple(sw13.shape) != (2 * Is, H) or tuple(sw2.shape) != (H, Is):
                 raise ValueError(f"shared weights must be [2Is, {H}] and [{H}, Is]")
             if sw13_scale.dtype == torch.float32:
                 want13, want2 = (2 * Is // 128, H // 128), (H // 128, Is // 128)
@@ -250,9 +276,31 @@ class MoeDecode:
         self._h = h
 
     # -- calls --------------------------------------------------------------
+    def check_run_args(self, x, logits, bias, slots, ids, weights, combined, shared_out=None):
+        """Device, dtype, contiguity, alignment and shape of every run buffer
+        (the C ABI receives bare pointers and cannot check sizes). Raises
+        ValueError; nothing has been launched then."""
+        dev, H, k, E = self.device, self.hidden, self.top_k, self.experts
+        if not isinstance(x, torch.Tensor) or x.dim() != 2:
+            raise ValueError("x must be a [M, H] tensor")
+        M = x.shape[0]
+        bf16 = (torch.bfloat16,)
+        _need(x, "x", bf16, dev, shape=(M, H))
+        _need(logits, "logits", (self.logits_dtype,), dev, shape=(M, E), min_rows=True)
+        _need(bias, "bias", (torch.float32,), dev, align=4, shape=(E,))
+        _need(slots, "slots", bf16, dev, shape=(M * k, H), min_rows=True)
+        _need(ids, "ids", (torch.int32,), dev, align=4, shape=(M, k), min_rows=True)
+        _need(weights, "weights", (torch.float32,), dev, align=4, shape=(M, k), min_rows=True)
+        _need(combined, "combined", bf16, dev, shape=(M, H), min_rows=True)
+        if shared_out is not None:
+            if not self.shared_inter:
+                raise ValueError("shared_out given, but the handle has no shared expert")
+            _need(shared_out, "shared_out", bf16, dev, shape=(M, H), min_rows=True)
+        return M
+
     def run_into(self, x, logits, bias, slots, ids, weights, combined, shared_out=None,
                  stream=None) -> None:
-        M = x.shape[0]
+        M = self.check_run_args(x, logits, bias, slots, ids, weights, combined, shared_out)
         rc = lib().moe_decode_run(self._h, M, _ptr(x), _ptr(logits), _ptr(bias), _ptr(slots),
                                   _ptr(ids), _ptr(weights), _ptr(combined), _ptr(shared_out),
                                   _stream(stream))
@@ -270,9 +318,8 @@ class MoeDecode:
         """(slots [M*k, H] bf16, ids [M, k] int32, weights [M, k] f32,
         combined [M, H] bf16), plus shared_out [M, H] bf16 when the handle
         has a shared expert."""
-        _need(x, "x", (torch.bfloat16,), self.device)
-        _need(logits, "logits", (self.logits_dtype,), self.device)
-        _need(bias, "bias", (torch.float32,), self.device, align=4)
+        if not isinstance(x, torch.Tensor) or x.dim() != 2:
+            raise ValueError("x must be a [M, H] tensor")
         out = self.outputs(x.shape[0])
         shared = None
         if self.shared_inter:

@@ -25,6 +25,8 @@ constexpr int kDenseTargetUnits = 256;  // units of the shared expert per GEMM l
 constexpr int kWgTargetUnits = 4096;    // K-in-workgroup path: units to aim for (16 per CU)
 constexpr int kWgMinPartBlocks = 14;    // shortest per-wave weight stream worth a K part (128-K blocks)
 constexpr int kBadFlagWord = 32;        // word of the control region used by create
+// Debug stages past the workspace regions: the shared expert's FP32 scales.
+constexpr int kStageSharedScale13 = 19, kStageSharedScale2 = 20;
 // Most tokens for the persistent K-in-workgroup GEMMs. Measured on MI355X
 // (DeepSeek-V3 shapes, layer µs, one workgroup per unit -> persistent):
 // M=1 83.8 -> 81.3, M=2 137.6 -> 132.2, M=4 209.4 -> 207.5, M=8 313.9 ->
@@ -342,7 +344,7 @@ int prepare_shared_scales(moe_decode_handle* h) {
       hipMemcpy(&flag, bad, sizeof(flag), hipMemcpyDeviceToHost) != hipSuccess ||
       hipMemset(bad, 0, sizeof(int32_t)) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
     return MOE_DECODE_ERR_HIP;
-  if (flag) return MOE_DECODE_ERR_INVALID_ARG;  // scales vary inside a 128-row block
+  if (flag) return MOE_DECODE_ERR_INVALID_ARG;  // a 128-row block mixes exponent bytes
   h->s13 = h->s13_owned;
   h->s2 = h->s2_owned;
   return MOE_DECODE_OK;
@@ -770,7 +772,19 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
 }
 
 int moe_decode_debug_stage(moe_decode_t h, int32_t stage, void* dst, size_t bytes, void* stream) {
-  if (!h || !dst || stage < 0 || stage >= kCount) return MOE_DECODE_ERR_INVALID_ARG;
+  if (!h || !dst || stage < 0) return MOE_DECODE_ERR_INVALID_ARG;
+  if (stage == kStageSharedScale13 || stage == kStageSharedScale2) {
+    // The shared expert's FP32 block scales as the kernels read them.
+    const moe_decode_config& c = h->cfg;
+    if (c.shared_inter == 0) return MOE_DECODE_ERR_INVALID_ARG;
+    const size_t H = c.hidden / kTile, Is = c.shared_inter / kTile;
+    const size_t full = (stage == kStageSharedScale13 ? 2 * Is * H : H * Is) * sizeof(float);
+    const hipError_t e = hipMemcpyAsync(dst, stage == kStageSharedScale13 ? h->s13 : h->s2,
+                                        std::min(bytes, full), hipMemcpyDeviceToDevice,
+                                        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_DECODE_OK : MOE_DECODE_ERR_HIP;
+  }
+  if (stage >= kCount) return MOE_DECODE_ERR_INVALID_ARG;
   if (stage >= kSXq && stage <= kSP2 && h->cfg.shared_inter == 0) return MOE_DECODE_ERR_INVALID_ARG;
   if (stage >= kJobs && h->cfg.weight_format != MOE_WEIGHTS_NVFP4) return MOE_DECODE_ERR_INVALID_ARG;
   if (!h->shared_own_quant && (stage == kSXq || stage == kSXs)) stage = stage == kSXq ? kXq : kXs;

@@ -282,6 +282,7 @@ __global__ __launch_bounds__(kThreads) void gemm_wg_kernel(GemmArgs args) {
     }
     __syncthreads();
     const int n = nclaim;
+    if (n > 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // reads after the completed count
     float* lds = reinterpret_cast<float*>(smem);  // the weight tiles' space: k * 64 floats
     for (int q = 0; q < n; ++q) combine_tile(f, a.part, a.N, claimed[q], tile * rows_wg, rows_wg, lds);
   }
@@ -345,6 +346,7 @@ __device__ void finish_swiglu_blocks(const SwigluFuse& f, const GemmProblem& a, 
   }
   __syncthreads();
   const int n = nclaim;
+  if (n > 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // reads after the completed count
   for (int q = wave; q < n; q += kThreads / kWave) {
     const int r = claimed[q];
     const float* p = a.part + (size_t)r * a.N + c * kTile + 2 * lane;

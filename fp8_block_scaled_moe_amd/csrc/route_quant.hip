@@ -429,6 +429,9 @@ __global__ __launch_bounds__(kThreads) void route_quant_kernel(RouteQuantArgs a)
     is_last = __hip_atomic_fetch_add(a.b.ctrl, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gr - 1;
   __syncthreads();
   if (!is_last) return;
+  // Acquire at agent scope: the reads below may not be served from before the
+  // count was observed (it invalidates this CU's caches, writes nothing back).
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (threadIdx.x == 0) __hip_atomic_store(a.b.ctrl, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (int r = threadIdx.x; r < a.M * a.k; r += kThreads) {
     const int id = __hip_atomic_load(a.ids + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -21,7 +21,9 @@ extern "C" {
 
 #define MOE_BOUNDARY_MAX_D 16384 /* longest row either call takes */
 
-/* MXFP8 quantisation of T BF16 rows of length D (EpDispatch: the latent is
+/* Passage: "kimi_k3 ... ep.comm" page, EpDispatch (the sender quantises each
+ * token's latent to MXFP8, one E8M0 scale per 32 values, before the copy).
+ * MXFP8 quantisation of T BF16 rows of length D (EpDispatch: the latent is
  * quantised per 32 values before it is sent). Per 32-value block b of row t:
  * shared = floor(log2(max |x|)) - 8 kept within [-127, 127] (-127 for an
  * all-zero block), sf[t, b] = shared + 127, and q[t, 32b + i] =
@@ -37,7 +39,10 @@ extern "C" {
  * misaligned pointer is INVALID_ARG. Nothing is enqueued on an error. */
 int moe_mxfp8_quantize(const void* x, int32_t T, int32_t D, void* q, void* sf, void* stream);
 
-/* The combine's reduce and RMSNorm (EpCombine, rms_rstd): for each token t,
+/* Passage: "kimi_k3 ... ep.comm" page, EpCombine (the owner sums the ranks'
+ * partial rows in FP32 in rank order, rounds once, then applies RMSNorm) and
+ * rms_rstd (an IEEE divide by D, then the reciprocal square root).
+ * The combine's reduce and RMSNorm (EpCombine, rms_rstd): for each token t,
  *   latent[t] = BF16(sum over n in 0..N-1, in that order, of partials[t, n])
  *               with the sum in FP32, rounded once;
  *   rstd      = 1 / sqrt(sum_i latent[t, i]^2 / D + eps), in FP32 with the

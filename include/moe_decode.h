@@ -181,14 +181,31 @@ typedef struct moe_decode_config {
 
 typedef struct moe_decode_handle* moe_decode_t;
 
-/* Validates cfg, allocates the handle's workspace for cfg->max_tokens on the
+/* Passage: vLLM "mega_moe" page, MegaExperts.__init__ (the layer object holds
+ * the expert weights and scales it was built with, and fixes hidden, inter,
+ * experts, top_k, limit, routed scale and the UE8M0 flag) and
+ * MegaExperts.prepare (all per-shape set-up happens before the first call, so
+ * that calls can be captured in a graph); "shared_expert" page,
+ * SharedExpert.__init__ (packed UE8M0 scales converted once, block_scales).
+ * Ownership follows the nvfp4-megamoe-kernel README ("SFB ... NOT Cached"):
+ * the handle keeps no cache keyed on caller memory that it might evict or
+ * outlive; what it derives from the weights (FP32 shared scales, reordered
+ * FP4 scales) it copies once, here, into memory it owns until destroy.
+ *
+ * Validates cfg, allocates the handle's workspace for cfg->max_tokens on the
  * current device, and converts packed shared-expert scales. Weight pointers
  * are borrowed, not copied. On success *out receives the handle.
  * Errors: INVALID_ARG (null cfg/out/weights, limit <= 0, max_tokens out of
  * range), UNSUPPORTED (shape limits above), OUT_OF_MEMORY, HIP. */
 int moe_decode_create(const moe_decode_config* cfg, moe_decode_t* out);
 
-/* One routed-expert decode step for M tokens, 0 <= M <= max_tokens.
+/* Passage: vLLM "mega_moe" page, MegaExperts.__call__ (x [M, hidden] BF16,
+ * logits [M, experts], bias [experts] FP32 in; BF16 [M * top_k, hidden] route
+ * outputs, int32 [M, top_k] experts and FP32 [M, top_k] weights out) and the
+ * nvfp4-megamoe-kernel README, "slot representation" (weights applied once,
+ * in the final combine).
+ *
+ * One routed-expert decode step for M tokens, 0 <= M <= max_tokens.
  *   x          [M, H] BF16
  *   logits     [M, E] FP32 or BF16 (per logits_dtype)
  *   bias       [E] FP32 score-correction bias (selects, does not weigh)
@@ -208,15 +225,22 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
                    const float* bias, void* slots, int32_t* ids, float* weights,
                    void* combined, void* shared_out, void* stream);
 
-/* Frees the workspace (after synchronising the device). NULL is a no-op. */
+/* Passage: the ownership rule of moe_decode_create (the pages' layer objects
+ * release what they allocated when they go away; borrowed weights are left
+ * to the caller).
+ * Frees the workspace and the handle's own copies (after synchronising the
+ * device). The caller's weights are untouched. NULL is a no-op. */
 void moe_decode_destroy(moe_decode_t h);
 
-/* Static description of an error code. */
+/* The text of an error code (the pages report these conditions with Python
+ * assertions, e.g. the "mega_moe" page's _MegaKernel checks of experts and
+ * hidden; here they are return codes). Static storage; never NULL. */
 const char* moe_decode_error_string(int code);
 
 /* ---- Introspection (tests and benchmarks) ------------------------------ */
 
-/* The launch plan run() uses for M tokens: out[0] = GEMM path used
+/* Test and benchmark introspection (no passage: it describes this library's
+ * own launches). The launch plan run() uses for M tokens: out[0] = GEMM path used
  * (MOE_GEMM_*, never AUTO), out[1] / out[2] = partial-sum slices GEMM1 /
  * GEMM2 write (the K splits of the split-K paths; 1 on MOE_GEMM_MFMA),
  * out[3] / out[4] = 128-K blocks per split or per K part, out[5] / out[6] =
@@ -237,7 +261,11 @@ const char* moe_decode_error_string(int code);
  * (>= 9). */
 int moe_decode_plan(moe_decode_t h, int32_t M, int32_t* out, int32_t n);
 
-/* Stage read-back: copies workspace region `stage` of the last run into the
+/* Passage: the intermediate results named by the "mega_moe" page's kernel
+ * (routing picks, the FP8 activation and its scales, GEMM1 sums, the FP8
+ * hidden and its scales, GEMM2 sums; epilogue and hidden_block) and by the
+ * "shared_expert" page's _GateUpKernel and _DownKernel; for tests.
+ * Stage read-back: copies workspace region `stage` of the last run into the
  * device buffer dst (bytes = capacity of dst) on stream. Stages:
  *  0 control words int32[3] (arrival counter, distinct experts U, jobs J)
  *  1 distinct experts, ascending int32[U]   2 their first index into stage 4
@@ -252,6 +280,11 @@ int moe_decode_plan(moe_decode_t h, int32_t M, int32_t* out, int32_t n);
  * 13 gate_up split partials FP32 [splits, M, 2Is]
  * 14 h_q [M, Is] e4m3                      15 h_s [M, Is/128] FP32
  * 16 down split partials FP32 [splits, M, H]
+ * 19 the shared expert's FP32 W13 block scales [2Is/128, H/128] as the kernels
+ *    read them (for MOE_SCALES_UE8M0_PACKED, the conversion done by create:
+ *    bit pattern byte << 23, so byte 0 is +0.0 and byte 255 +inf, the
+ *    "shared_expert" page's block_scales)
+ * 20 the same for W2 [H/128, Is/128]
  * MOE_WEIGHTS_NVFP4 handles: stages 5 / 8 hold packed E2M1 ([M, H/2],
  * [M*k, I/2]) and 6 / 9 UE4M3 bytes ([M, H/16], [M*k, I/16]); stages 7 / 10
  * hold the GEMMs' partial slots ([slots, M*k, N], out[1] / out[2] of
@@ -263,7 +296,8 @@ int moe_decode_plan(moe_decode_t h, int32_t M, int32_t* out, int32_t n);
 int moe_decode_debug_stage(moe_decode_t h, int32_t stage, void* dst, size_t bytes,
                            void* stream);
 
-/* Per-kernel timing of subsequent runs with HIP events recorded between the
+/* Benchmark support (no passage: it times this library's own launches).
+ * Per-kernel timing of subsequent runs with HIP events recorded between the
  * launches (enable != 0; not for use under graph capture). After a run has
  * completed, moe_decode_last_timing writes the milliseconds of each launch in
  * order: route+quant, GEMM1, SwiGLU+requant, GEMM2, combine (the shared
@@ -273,13 +307,18 @@ int moe_decode_debug_stage(moe_decode_t h, int32_t stage, void* dst, size_t byte
 int moe_decode_set_timing(moe_decode_t h, int32_t enable);
 int moe_decode_last_timing(moe_decode_t h, float* ms, int32_t n);
 
-/* Codec self-check of the device code: q[i] = e4m3 encoding of in[i] with the
+/* Passage: the FP8 encode of the "mega_moe" page's epilogue and hidden_block
+ * (pack_fp8 of scaled values; read here as OCP e4m3, nearest even,
+ * saturating). For tests.
+ * Codec self-check of the device code: q[i] = e4m3 encoding of in[i] with the
  * library's quantiser (nearest, ties to even, saturating), and dq[i] = the
  * value the GEMM inner products read for code (i & 255) through the path's
  * FP8 -> F16 conversion. in, q and dq are device buffers of n elements. */
 int moe_decode_debug_codec(const float* in, uint8_t* q, float* dq, int32_t n, void* stream);
 
-/* The same for E2M1: q[i] = the library's E2M1 code of in[i] (nearest, ties
+/* Passage: nvfp4-megamoe-kernel README, "Data Formats" (E2M1 values, two per
+ * byte) and bug 2 (activation staging). For tests.
+ * The same for E2M1: q[i] = the library's E2M1 code of in[i] (nearest, ties
  * to even, saturating at +-6), and dq[i] = the value the FP4 GEMM reads for
  * code (i & 15) through its FP4 -> F16 widening (with the code placed in
  * each nibble and byte position of a word in turn). */

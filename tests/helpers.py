@@ -68,11 +68,39 @@ def row_errors(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
     return out
 
 
-def assert_rows_close(got, ref, rtol=ROW_RTOL, what="rows"):
+def assert_rows_close(got, ref, rtol=ROW_RTOL, what="rows", valid=None):
+    """Every row within rtol x the RMS of the oracle's row (max |err|).
+
+    valid(rows) -> bool [len(rows), cols], optional: which elements of those
+    rows are the correct BF16 rounding of a valid FP32 result of the GPU's own
+    inputs to the step (rounding_valid below). A BF16 output has two correct
+    values when its exact value lies within the FP32 accumulation bound of the
+    midpoint between two BF16 numbers (the summation order is not fixed by the
+    pages); an element that is valid and one BF16 step from the oracle's is
+    then no error. It is only consulted for rows over the bar."""
+    got = np.asarray(got, np.float64).reshape(np.shape(ref)[0], -1)
+    ref = np.asarray(ref, np.float64).reshape(np.shape(ref)[0], -1)
     e = row_errors(got, ref)
     bad = np.nonzero(e > rtol)[0]
+    if bad.size and valid is not None:
+        ok = valid(bad)
+        step = bf16_step(np.maximum(np.abs(got[bad]), np.abs(ref[bad])))
+        tie = ok & (np.abs(got[bad] - ref[bad]) <= step)
+        g = np.where(tie, ref[bad], got[bad])
+        e = e.copy()
+        e[bad] = row_errors(g, ref[bad])
+        bad = np.nonzero(e > rtol)[0]
     assert bad.size == 0, f"{what}: {bad.size} rows over {rtol} x rms (worst {e.max():.3g} at row {int(e.argmax())})"
     return float(e.max()) if e.size else 0.0
+
+
+def rounding_valid(got_bf16, exact, bound):
+    """got is bf16(v) for some v with |v - exact| <= bound (BF16 rounding of
+    FP32 values is monotone, so the valid outputs are the interval between the
+    roundings of exact - bound and exact + bound)."""
+    lo = oracle.bf16_round(exact - bound)
+    hi = oracle.bf16_round(exact + bound)
+    return (got_bf16 >= lo) & (got_bf16 <= hi)
 
 
 def bf16_step(v):
@@ -81,16 +109,30 @@ def bf16_step(v):
     return np.ldexp(1.0, e - 8)
 
 
+FP32_U = 2.0**-24
+
+
+def combine_bound(slots, weights):
+    """Error bound of a k-term FP32 multiply-add chain: gamma_k * sum |w * slot|
+    (gamma_k = k u / (1 - k u), u = 2**-24), per combined element."""
+    w = np.asarray(weights, np.float64)
+    M, k = w.shape
+    rows = np.abs(np.asarray(slots, np.float64)).reshape(M, k, -1)
+    gamma = k * FP32_U / (1 - k * FP32_U)
+    return gamma * np.einsum("tk,tkh->th", np.abs(w), rows)
+
+
 def check_combine(slots, weights, combined, max_differ=1e-3):
     """The GPU's combine against the oracle's combine of the GPU's own slot rows
-    and weights: within one BF16 step everywhere and bit-exact on all but
-    max_differ of the elements (an FP32 sum in another order may round to the
-    neighbouring BF16 value). Rounding the weights, or applying them twice or
-    not at all, fails."""
+    and weights: every element the BF16 rounding of a value within the FP32
+    summation bound of the exact weighted sum (within one BF16 step of it
+    beyond that bound), and bit-exact on all but max_differ of the elements.
+    Rounding the weights, or applying them twice or not at all, fails."""
     got = host(combined)
-    want = oracle.combine(host(slots), host(weights))
+    s, w = host(slots), host(weights)
+    exact = np.einsum("tk,tkh->th", w, s.reshape(w.shape[0], w.shape[1], -1))
+    want = oracle.combine(s, w)
     diff = got != want
-    step = bf16_step(np.maximum(np.abs(got), np.abs(want)))
-    far = np.abs(got - want) > step
-    assert not far.any(), f"combine: {far.sum()} elements beyond one BF16 step"
+    ok = rounding_valid(got, exact, combine_bound(s, w))
+    assert ok.all(), f"combine: {np.count_nonzero(~ok)} elements not a rounding of the FP32 sum"
     assert diff.mean() <= max_differ, f"combine: {diff.mean():.3%} of elements differ"

@@ -18,7 +18,8 @@ import torch
 import oracle
 import synth
 from fp8_block_scaled_moe_amd import MoeDecode, MoeDecodeError, _capi
-from tests.helpers import (WEIGHT_RTOL, assert_rows_close, host, oracle_layer, oracle_shared)
+from tests.helpers import (WEIGHT_RTOL, assert_rows_close, check_combine, host, oracle_layer,
+                           oracle_shared)
 
 pytestmark = pytest.mark.gpu
 
@@ -218,10 +219,11 @@ def test_shared_skipped_without_output():
         assert torch.equal(a, b)
 
 
+@pytest.mark.timeout(600)
 def test_shared_dsv3_m32():
     """DeepSeek-V3 shapes at M = 32 with the shared expert (gate_up [4096, 7168],
-    down [7168, 2048], UE8M0 scales): every shared_out row against the oracle;
-    the routed outputs on sampled tokens, routing on all of them."""
+    down [7168, 2048], UE8M0 scales): every shared_out row and every routed
+    token (about 83 touched experts) against the oracle."""
     inp = synth.make_inputs(synth.CONFIGS["dsv3_m32_shared"], seed=0, device=DEV)
     moe = make(inp)
     M = inp.shape.M
@@ -230,14 +232,40 @@ def test_shared_dsv3_m32():
     check_shared_quant(moe, inp, ref, M)
     check_shared_hidden(moe, inp, M, gpu_gate_up(moe, M, inp.shape.shared_inter))
     assert_rows_close(host(shared_out), ref["out"], what="shared_out")
-    sample = [0, 17, 31]
-    sub = synth.MoeInputs(shape=inp.shape.with_(M=len(sample), shared_inter=0), seed=0,
-                          x=inp.x[sample], logits=inp.logits[sample], bias=inp.bias, w13=inp.w13,
-                          w13_scale=inp.w13_scale, w2=inp.w2, w2_scale=inp.w2_scale)
-    lref = oracle_layer(sub)
-    k = inp.shape.top_k
-    rows = np.concatenate([np.arange(t * k, (t + 1) * k) for t in sample])
-    assert np.array_equal(ids.cpu().numpy()[sample], lref["ids"])
-    np.testing.assert_allclose(host(weights)[sample], lref["weights"], rtol=WEIGHT_RTOL, atol=0)
-    assert_rows_close(host(slots)[rows], lref["slots"], what="slots")
-    assert_rows_close(host(combined)[sample], lref["combined"], what="combined")
+    lref = oracle_layer(inp)   # the routed part: the shared expert is not in it
+    assert np.array_equal(ids.cpu().numpy(), lref["ids"])
+    np.testing.assert_allclose(host(weights), lref["weights"], rtol=WEIGHT_RTOL, atol=0)
+    assert_rows_close(host(slots), lref["slots"], what="slots")
+    assert_rows_close(host(combined), lref["combined"], what="combined")
+    check_combine(slots, weights, combined)
+
+
+def test_shared_ue8m0_every_byte():
+    """Packed UE8M0 scales holding every exponent byte 0..255 (one per 128 x 128
+    block of a [4096, 2048] gate_up): the FP32 scales create converts them to
+    are the oracle's, bit for bit: byte << 23, so 0 is +0.0 and 255 is +inf
+    ("shared_expert" page, block_scales). The handle is only created."""
+    s = synth.CONFIGS["tiny"].with_(M=1, hidden=2048, shared_inter=2048)
+    inp = synth.make_inputs(s, seed=27, device=DEV)
+    H, Is = s.hidden, s.shared_inter
+    nb = (2 * Is // 128) * (H // 128)
+    assert nb == 512
+    # block b carries exponent byte b % 256: the binary32 with bits byte << 23
+    byte = torch.arange(nb, dtype=torch.int32, device=DEV) % 256
+    bits = (byte << 23).view(2 * Is // 128, H // 128)
+    packed13 = synth.pack_ue8m0(bits.view(torch.float32), 2 * Is, H)
+    packed2 = synth.pack_ue8m0(inp.sw2_scale, H, Is)
+    moe = MoeDecode(inp.w13, inp.w13_scale, inp.w2, inp.w2_scale, top_k=s.top_k, limit=s.limit,
+                    routed_scale=s.routed_scale, max_tokens=1, sw13=inp.sw13,
+                    sw13_scale=packed13.contiguous(), sw2=inp.sw2, sw2_scale=packed2)
+    got = stage(moe, "shared_scale13", nb, torch.float32)
+    torch.cuda.synchronize()
+    want = oracle.unpack_ue8m0(packed13.cpu().numpy(), 2 * Is, H)
+    g = got.cpu().numpy().astype(np.float64).reshape(want.shape)
+    assert np.array_equal(g.view(np.int64), want.view(np.int64))
+    flat = g.reshape(-1)
+    assert flat[0] == 0.0 and np.isposinf(flat[255]) and flat[127] == 1.0
+    got2 = stage(moe, "shared_scale2", (H // 128) * (Is // 128), torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(got2).reshape(H // 128, Is // 128), host(inp.sw2_scale))
+    moe.close()
