@@ -24,6 +24,7 @@ ERR_UNSUPPORTED = -2
 ERR_TOO_MANY_TOKENS = -3
 ERR_HIP = -4
 ERR_OUT_OF_MEMORY = -5
+ERR_SCRATCH_TOO_SMALL = -6
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
@@ -110,6 +111,9 @@ def lib() -> ctypes.CDLL:
     L.moe_decode_create.restype = ctypes.c_int
     L.moe_decode_run.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.moe_decode_run.restype = ctypes.c_int
+    L.moe_decode_run_noalloc.argtypes = [ctypes.POINTER(MoeDecodeConfig), i32, vp, vp, vp, vp, vp, vp, vp,
+                                         vp, vp]
+    L.moe_decode_run_noalloc.restype = ctypes.c_int
     L.moe_decode_destroy.argtypes = [vp]
     L.moe_decode_destroy.restype = None
     L.moe_decode_error_string.argtypes = [ctypes.c_int]
@@ -306,6 +310,18 @@ class MoeDecode:
                                   _stream(stream))
         if rc != OK:
             raise MoeDecodeError(rc, "moe_decode_run")
+
+    def run_noalloc(self, x, logits, bias, slots, ids, weights, combined, shared_out=None,
+                    stream=None) -> None:
+        """moe_decode_run_noalloc with this handle's configuration: the same
+        step, its workspace in the library's fixed per-GPU buffer instead of
+        the handle's (nothing allocated; calls overlapping on one GPU race)."""
+        M = self.check_run_args(x, logits, bias, slots, ids, weights, combined, shared_out)
+        rc = lib().moe_decode_run_noalloc(ctypes.byref(self.cfg), M, _ptr(x), _ptr(logits), _ptr(bias),
+                                          _ptr(slots), _ptr(ids), _ptr(weights), _ptr(combined),
+                                          _ptr(shared_out), _stream(stream))
+        if rc != OK:
+            raise MoeDecodeError(rc, "moe_decode_run_noalloc")
 
     def outputs(self, M: int):
         dev, H, k = self.device, self.hidden, self.top_k

@@ -3,9 +3,11 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -319,61 +321,9 @@ int validate_config(const moe_decode_config* c) {
   return MOE_DECODE_OK;
 }
 
-// Shared-expert scales as FP32: the caller's own, or converted once from the
-// packed UE8M0 form into buffers the handle owns. Synchronises the device.
-int prepare_shared_scales(moe_decode_handle* h) {
-  const moe_decode_config& c = h->cfg;
-  if (c.shared_scale_format == MOE_SCALES_F32) {
-    h->s13 = static_cast<const float*>(c.sw13_scale);
-    h->s2 = static_cast<const float*>(c.sw2_scale);
-    return MOE_DECODE_OK;
-  }
-  const int H = c.hidden, Is = c.shared_inter;
-  const size_t n13 = (size_t)(2 * Is / kTile) * (H / kTile), n2 = (size_t)(H / kTile) * (Is / kTile);
-  if (hipMalloc(&h->s13_owned, n13 * sizeof(float)) != hipSuccess ||
-      hipMalloc(&h->s2_owned, n2 * sizeof(float)) != hipSuccess) {
-    (void)hipGetLastError();
-    return MOE_DECODE_ERR_OUT_OF_MEMORY;
-  }
-  int32_t* bad = reinterpret_cast<int32_t*>(h->ws + h->reg[kCtrl].off) + kBadFlagWord;
-  int32_t flag = 0;
-  if (launch_unpack_ue8m0(static_cast<const int32_t*>(c.sw13_scale), 2 * Is, H, h->s13_owned, bad, nullptr) !=
-          hipSuccess ||
-      launch_unpack_ue8m0(static_cast<const int32_t*>(c.sw2_scale), H, Is, h->s2_owned, bad, nullptr) !=
-          hipSuccess ||
-      hipMemcpy(&flag, bad, sizeof(flag), hipMemcpyDeviceToHost) != hipSuccess ||
-      hipMemset(bad, 0, sizeof(int32_t)) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
-    return MOE_DECODE_ERR_HIP;
-  if (flag) return MOE_DECODE_ERR_INVALID_ARG;  // a 128-row block mixes exponent bytes
-  h->s13 = h->s13_owned;
-  h->s2 = h->s2_owned;
-  return MOE_DECODE_OK;
-}
-
-}  // namespace
-
-extern "C" {
-
-const char* moe_decode_error_string(int code) {
-  switch (code) {
-    case MOE_DECODE_OK: return "ok";
-    case MOE_DECODE_ERR_INVALID_ARG: return "invalid argument";
-    case MOE_DECODE_ERR_UNSUPPORTED: return "unsupported shape or option";
-    case MOE_DECODE_ERR_TOO_MANY_TOKENS: return "more tokens than the handle's max_tokens";
-    case MOE_DECODE_ERR_HIP: return "HIP runtime error";
-    case MOE_DECODE_ERR_OUT_OF_MEMORY: return "out of device memory";
-    default: return "unknown error";
-  }
-}
-
-int moe_decode_create(const moe_decode_config* cfg, moe_decode_t* out) {
-  if (!out) return MOE_DECODE_ERR_INVALID_ARG;
-  *out = nullptr;
-  const int v = validate_config(cfg);
-  if (v != MOE_DECODE_OK) return v;
-  const moe_decode_config& c = *cfg;
-
-  // Workspace sized for every M up to max_tokens.
+// The workspace regions for every M up to c.max_tokens, each 256-byte
+// aligned; returns the total bytes.
+size_t layout_workspace(const moe_decode_config& c, Region reg[kRegions], bool* shared_own_quant) {
   const size_t Rcap = (size_t)c.max_tokens * c.top_k;
   const size_t Ucap = std::min<size_t>(local_count(c), Rcap);
   const bool fp4 = c.weight_format == MOE_WEIGHTS_NVFP4;
@@ -411,154 +361,113 @@ int moe_decode_create(const moe_decode_config* cfg, moe_decode_t* out) {
       fp4 ? 0 : T * (H / 16) * sizeof(int32_t),  // arrival counts (at least 16 rows per workgroup)
       fp4 ? 0 : Rcap * (I / kTile) * sizeof(int32_t),  // arrival counts per (route, hidden block)
   };
-  moe_decode_handle* h = new (std::nothrow) moe_decode_handle();
-  if (!h) return MOE_DECODE_ERR_OUT_OF_MEMORY;
-  h->cfg = c;
   size_t off = 0;
   for (int i = 0; i < kRegions; ++i) {
-    h->reg[i] = Region{off, sizes[i]};
+    reg[i] = Region{off, sizes[i]};
     off += (sizes[i] + 255) & ~size_t(255);
   }
-  h->ws_bytes = off;
-  h->words = (c.max_tokens + 63) / 64;
-  h->shared_own_quant = own_quant;
-  if (hipGetDevice(&h->device) != hipSuccess) {
-    delete h;
-    return MOE_DECODE_ERR_HIP;
+  *shared_own_quant = own_quant;
+  return off;
+}
+
+// Shared-expert scales as FP32: the caller's own, or converted once from the
+// packed UE8M0 form into buffers the handle owns. Synchronises the device.
+int prepare_shared_scales(moe_decode_handle* h) {
+  const moe_decode_config& c = h->cfg;
+  if (c.shared_scale_format == MOE_SCALES_F32) {
+    h->s13 = static_cast<const float*>(c.sw13_scale);
+    h->s2 = static_cast<const float*>(c.sw2_scale);
+    return MOE_DECODE_OK;
   }
-  if (hipMalloc(&h->ws, h->ws_bytes) != hipSuccess) {
+  const int H = c.hidden, Is = c.shared_inter;
+  const size_t n13 = (size_t)(2 * Is / kTile) * (H / kTile), n2 = (size_t)(H / kTile) * (Is / kTile);
+  if (hipMalloc(&h->s13_owned, n13 * sizeof(float)) != hipSuccess ||
+      hipMalloc(&h->s2_owned, n2 * sizeof(float)) != hipSuccess) {
     (void)hipGetLastError();
-    delete h;
     return MOE_DECODE_ERR_OUT_OF_MEMORY;
   }
-  if (hipMemset(h->ws, 0, h->ws_bytes) != hipSuccess) {
-    (void)hipFree(h->ws);
-    delete h;
+  int32_t* bad = reinterpret_cast<int32_t*>(h->ws + h->reg[kCtrl].off) + kBadFlagWord;
+  int32_t flag = 0;
+  if (launch_unpack_ue8m0(static_cast<const int32_t*>(c.sw13_scale), 2 * Is, H, h->s13_owned, bad, nullptr) !=
+          hipSuccess ||
+      launch_unpack_ue8m0(static_cast<const int32_t*>(c.sw2_scale), H, Is, h->s2_owned, bad, nullptr) !=
+          hipSuccess ||
+      hipMemcpy(&flag, bad, sizeof(flag), hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemset(bad, 0, sizeof(int32_t)) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
     return MOE_DECODE_ERR_HIP;
-  }
-  for (int i = 0; i < kEvents; ++i) {
-    if (hipEventCreate(&h->ev[i]) != hipSuccess) {
-      for (int j = 0; j < i; ++j) (void)hipEventDestroy(h->ev[j]);
-      (void)hipFree(h->ws);
-      delete h;
-      return MOE_DECODE_ERR_HIP;
-    }
-  }
-  if (!fp4) {  // 0 (one workgroup per unit) if the query fails
-    h->wgp_wgs1 = gemm_wgp_resident_wgs(c.hidden / kTile);
-    h->wgp_wgs2 = gemm_wgp_resident_wgs(c.inter / kTile);
-  }
-  if (fp4) {
-    h->fp4_wgs1 = gemm_fp4_resident_wgs(c.hidden);
-    h->fp4_wgs2 = gemm_fp4_resident_wgs(c.inter);
-    if (h->fp4_wgs1 <= 0 || h->fp4_wgs2 <= 0) {
-      moe_decode_destroy(h);
-      return MOE_DECODE_ERR_HIP;
-    }
-    // the weight scales, read once here into the kernel's layout
-    const size_t El = local_count(c), rows13 = El * 2 * I, rows2 = El * H;
-    if (hipMalloc(&h->fp4_s13, rows13 * (H / 16)) != hipSuccess ||
-        hipMalloc(&h->fp4_s2, rows2 * (I / 16)) != hipSuccess) {
+  if (flag) return MOE_DECODE_ERR_INVALID_ARG;  // a 128-row block mixes exponent bytes
+  h->s13 = h->s13_owned;
+  h->s2 = h->s2_owned;
+  return MOE_DECODE_OK;
+}
+
+// ---- The workspace of moe_decode_run_noalloc ------------------------------
+// A file-scope device array: each GPU holds its own copy, at its own
+// address, from the library's load on that GPU until the process ends. In
+// host code `scratch` names a host-side stand-in, not device memory: device
+// addresses come only from the per-device lookup below.
+constexpr size_t kScratchBytes = MOE_DECODE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+constexpr int kMaxCachedBlocks = 1024;  // K / 128 values whose resident-workgroup counts are cached
+
+struct DeviceScratch {
+  std::once_flag once;
+  unsigned char* ptr = nullptr;  // this device's copy of `scratch`
+  // resident workgroups of the persistent FP8 GEMM for K / 128 = i, plus one
+  // (0: not yet asked)
+  std::atomic<int> wgp[kMaxCachedBlocks + 1] = {};
+};
+DeviceScratch g_dev[kMaxDevices];
+
+// The device copy of `scratch` on device dev (the current device), looked
+// up once per device; nullptr if the lookup failed.
+unsigned char* device_scratch(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  DeviceScratch& d = g_dev[dev];
+  std::call_once(d.once, [&] {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess)
+      d.ptr = static_cast<unsigned char*>(p);
+    else
       (void)hipGetLastError();
-      moe_decode_destroy(h);
-      return MOE_DECODE_ERR_OUT_OF_MEMORY;
-    }
-    if (launch_reorder_fp4_scales(static_cast<const uint8_t*>(c.w13_scale), h->fp4_s13, rows13, (int)H,
-                                  nullptr) != hipSuccess ||
-        launch_reorder_fp4_scales(static_cast<const uint8_t*>(c.w2_scale), h->fp4_s2, rows2, (int)I, nullptr) !=
-            hipSuccess ||
-        hipDeviceSynchronize() != hipSuccess) {
-      moe_decode_destroy(h);
-      return MOE_DECODE_ERR_HIP;
-    }
-  }
-  if (Is > 0) {
-    const int r = prepare_shared_scales(h);
-    if (r != MOE_DECODE_OK) {
-      moe_decode_destroy(h);
-      return r;
-    }
-  }
-  if (std::getenv("MOE_DECODE_DEBUG")) {
-    const Plan p = make_plan(c, c.max_tokens, h->fp4_wgs1, h->fp4_wgs2, h->wgp_wgs1, h->wgp_wgs2);
-    std::fprintf(stderr,
-                 "moe_decode: H=%d I=%d E=%d k=%d max_tokens=%d workspace=%zu B; at M=%d: "
-                 "path=%d splits1=%d (ks %d) splits2=%d (ks %d) grid1=%d grid2=%d\n",
-                 c.hidden, c.inter, c.experts, c.top_k, c.max_tokens, h->ws_bytes, c.max_tokens,
-                 p.path, p.s1, p.ks1, p.s2, p.ks2, p.grid1, p.grid2);
-  }
-  *out = h;
-  return MOE_DECODE_OK;
+  });
+  return d.ptr;
 }
 
-void moe_decode_destroy(moe_decode_t h) {
-  if (!h) return;
-  int prev = 0;
-  (void)hipGetDevice(&prev);
-  (void)hipSetDevice(h->device);
-  (void)hipDeviceSynchronize();
-  for (int i = 0; i < kEvents; ++i) (void)hipEventDestroy(h->ev[i]);
-  (void)hipFree(h->ws);
-  if (h->s13_owned) (void)hipFree(h->s13_owned);
-  if (h->s2_owned) (void)hipFree(h->s2_owned);
-  if (h->fp4_s13) (void)hipFree(h->fp4_s13);
-  if (h->fp4_s2) (void)hipFree(h->fp4_s2);
-  (void)hipSetDevice(prev);
-  delete h;
+int cached_wgp_wgs(int dev, int nkb) {
+  if (nkb > kMaxCachedBlocks) return gemm_wgp_resident_wgs(nkb);
+  std::atomic<int>& slot = g_dev[dev].wgp[nkb];
+  int v = slot.load(std::memory_order_relaxed);
+  if (v == 0) {
+    v = gemm_wgp_resident_wgs(nkb) + 1;
+    slot.store(v, std::memory_order_relaxed);
+  }
+  return v - 1;
 }
 
-int moe_decode_plan(moe_decode_t h, int32_t M, int32_t* out, int32_t n) {
-  if (!h || !out || n < 9 || M < 1) return MOE_DECODE_ERR_INVALID_ARG;
-  if (M > h->cfg.max_tokens) return MOE_DECODE_ERR_TOO_MANY_TOKENS;
-  const Plan p = make_plan(h->cfg, M, h->fp4_wgs1, h->fp4_wgs2, h->wgp_wgs1, h->wgp_wgs2);
-  out[0] = p.path;
-  out[1] = p.s1;
-  out[2] = p.s2;
-  const int blk = p.path == MOE_GEMM_FP4 ? 2 : 1;  // the FP4 plan counts 256-value steps
-  out[3] = p.ks1 * blk;
-  out[4] = p.ks2 * blk;
-  out[5] = p.grid1;
-  out[6] = p.grid2;
-  out[7] = p.tpw1;
-  out[8] = p.tpw2;
-  if (n >= 15) {
-    out[9] = p.ss1;
-    out[10] = p.ss2;
-    out[11] = p.sks1;
-    out[12] = p.sks2;
-    out[13] = p.sunits1;
-    out[14] = p.sunits2;
-  }
-  if (n >= 17) {
-    out[15] = p.path == MOE_GEMM_MFMA ? p.kp1 : 1;
-    out[16] = p.path == MOE_GEMM_MFMA ? p.kp2 : 1;
-  }
-  if (n >= 18) out[17] = 5 - (p.fuse_combine ? 1 : 0) - (p.fuse_swiglu ? 1 : 0);
-  if (n >= 20) {
-    out[18] = p.persist1;
-    out[19] = p.persist2;
-  }
-  return MOE_DECODE_OK;
-}
-
-int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits, const float* bias,
-                   void* slots, int32_t* ids, float* weights, void* combined, void* shared_out,
-                   void* stream) {
-  if (!h) return MOE_DECODE_ERR_INVALID_ARG;
-  if (M < 0) return MOE_DECODE_ERR_INVALID_ARG;
-  if (M > h->cfg.max_tokens) return MOE_DECODE_ERR_TOO_MANY_TOKENS;
-  if (M == 0) return MOE_DECODE_OK;
+// Pointer checks of a run (M >= 1): INVALID_ARG for a NULL or misaligned
+// buffer, or a shared_out without a shared expert.
+int check_run_pointers(const moe_decode_config& c, const void* x, const void* logits, const float* bias,
+                       const void* slots, const int32_t* ids, const float* weights, const void* combined,
+                       const void* shared_out) {
   if (!x || !logits || !bias || !slots || !ids || !weights || !combined)
     return MOE_DECODE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(slots) || !aligned16(combined) || !aligned16(logits) ||
       ((uintptr_t)ids & 3u) || ((uintptr_t)weights & 3u) || ((uintptr_t)bias & 3u))
     return MOE_DECODE_ERR_INVALID_ARG;
-  if (shared_out && (h->cfg.shared_inter == 0 || !aligned16(shared_out)))
-    return MOE_DECODE_ERR_INVALID_ARG;
+  if (shared_out && (c.shared_inter == 0 || !aligned16(shared_out))) return MOE_DECODE_ERR_INVALID_ARG;
+  return MOE_DECODE_OK;
+}
+
+// The five launches of one step on the handle's workspace (h->ws, h->reg);
+// the arguments are checked.
+int run_layer(moe_decode_handle* h, int32_t M, const void* x, const void* logits, const float* bias,
+              void* slots, int32_t* ids, float* weights, void* combined, void* shared_out, hipStream_t s) {
   const bool shared = shared_out != nullptr;
 
   const moe_decode_config& c = h->cfg;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const Plan p = make_plan(c, M, h->fp4_wgs1, h->fp4_wgs2, h->wgp_wgs1, h->wgp_wgs2);
   const int R = M * c.top_k;
   const bool fp4 = c.weight_format == MOE_WEIGHTS_NVFP4;
@@ -769,6 +678,212 @@ int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
   h->timed_run = h->timing;
   h->ev_count = evn;
   return e == hipSuccess ? MOE_DECODE_OK : MOE_DECODE_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_decode_error_string(int code) {
+  switch (code) {
+    case MOE_DECODE_OK: return "ok";
+    case MOE_DECODE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_DECODE_ERR_UNSUPPORTED: return "unsupported shape or option";
+    case MOE_DECODE_ERR_TOO_MANY_TOKENS: return "more tokens than the handle's max_tokens";
+    case MOE_DECODE_ERR_HIP: return "HIP runtime error";
+    case MOE_DECODE_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case MOE_DECODE_ERR_SCRATCH_TOO_SMALL:
+      return "the step needs more workspace than the no-allocation buffer holds";
+    default: return "unknown error";
+  }
+}
+
+int moe_decode_create(const moe_decode_config* cfg, moe_decode_t* out) {
+  if (!out) return MOE_DECODE_ERR_INVALID_ARG;
+  *out = nullptr;
+  const int v = validate_config(cfg);
+  if (v != MOE_DECODE_OK) return v;
+  const moe_decode_config& c = *cfg;
+
+  const bool fp4 = c.weight_format == MOE_WEIGHTS_NVFP4;
+  const size_t H = c.hidden, I = c.inter, Is = c.shared_inter;
+  moe_decode_handle* h = new (std::nothrow) moe_decode_handle();
+  if (!h) return MOE_DECODE_ERR_OUT_OF_MEMORY;
+  h->cfg = c;
+  h->ws_bytes = layout_workspace(c, h->reg, &h->shared_own_quant);
+  h->words = (c.max_tokens + 63) / 64;
+  if (hipGetDevice(&h->device) != hipSuccess) {
+    delete h;
+    return MOE_DECODE_ERR_HIP;
+  }
+  if (hipMalloc(&h->ws, h->ws_bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    delete h;
+    return MOE_DECODE_ERR_OUT_OF_MEMORY;
+  }
+  if (hipMemset(h->ws, 0, h->ws_bytes) != hipSuccess) {
+    (void)hipFree(h->ws);
+    delete h;
+    return MOE_DECODE_ERR_HIP;
+  }
+  for (int i = 0; i < kEvents; ++i) {
+    if (hipEventCreate(&h->ev[i]) != hipSuccess) {
+      for (int j = 0; j < i; ++j) (void)hipEventDestroy(h->ev[j]);
+      (void)hipFree(h->ws);
+      delete h;
+      return MOE_DECODE_ERR_HIP;
+    }
+  }
+  if (!fp4) {  // 0 (one workgroup per unit) if the query fails
+    h->wgp_wgs1 = gemm_wgp_resident_wgs(c.hidden / kTile);
+    h->wgp_wgs2 = gemm_wgp_resident_wgs(c.inter / kTile);
+  }
+  if (fp4) {
+    h->fp4_wgs1 = gemm_fp4_resident_wgs(c.hidden);
+    h->fp4_wgs2 = gemm_fp4_resident_wgs(c.inter);
+    if (h->fp4_wgs1 <= 0 || h->fp4_wgs2 <= 0) {
+      moe_decode_destroy(h);
+      return MOE_DECODE_ERR_HIP;
+    }
+    // the weight scales, read once here into the kernel's layout
+    const size_t El = local_count(c), rows13 = El * 2 * I, rows2 = El * H;
+    if (hipMalloc(&h->fp4_s13, rows13 * (H / 16)) != hipSuccess ||
+        hipMalloc(&h->fp4_s2, rows2 * (I / 16)) != hipSuccess) {
+      (void)hipGetLastError();
+      moe_decode_destroy(h);
+      return MOE_DECODE_ERR_OUT_OF_MEMORY;
+    }
+    if (launch_reorder_fp4_scales(static_cast<const uint8_t*>(c.w13_scale), h->fp4_s13, rows13, (int)H,
+                                  nullptr) != hipSuccess ||
+        launch_reorder_fp4_scales(static_cast<const uint8_t*>(c.w2_scale), h->fp4_s2, rows2, (int)I, nullptr) !=
+            hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
+      moe_decode_destroy(h);
+      return MOE_DECODE_ERR_HIP;
+    }
+  }
+  if (Is > 0) {
+    const int r = prepare_shared_scales(h);
+    if (r != MOE_DECODE_OK) {
+      moe_decode_destroy(h);
+      return r;
+    }
+  }
+  if (std::getenv("MOE_DECODE_DEBUG")) {
+    const Plan p = make_plan(c, c.max_tokens, h->fp4_wgs1, h->fp4_wgs2, h->wgp_wgs1, h->wgp_wgs2);
+    std::fprintf(stderr,
+                 "moe_decode: H=%d I=%d E=%d k=%d max_tokens=%d workspace=%zu B; at M=%d: "
+                 "path=%d splits1=%d (ks %d) splits2=%d (ks %d) grid1=%d grid2=%d\n",
+                 c.hidden, c.inter, c.experts, c.top_k, c.max_tokens, h->ws_bytes, c.max_tokens,
+                 p.path, p.s1, p.ks1, p.s2, p.ks2, p.grid1, p.grid2);
+  }
+  *out = h;
+  return MOE_DECODE_OK;
+}
+
+void moe_decode_destroy(moe_decode_t h) {
+  if (!h) return;
+  int prev = 0;
+  (void)hipGetDevice(&prev);
+  (void)hipSetDevice(h->device);
+  (void)hipDeviceSynchronize();
+  for (int i = 0; i < kEvents; ++i) (void)hipEventDestroy(h->ev[i]);
+  (void)hipFree(h->ws);
+  if (h->s13_owned) (void)hipFree(h->s13_owned);
+  if (h->s2_owned) (void)hipFree(h->s2_owned);
+  if (h->fp4_s13) (void)hipFree(h->fp4_s13);
+  if (h->fp4_s2) (void)hipFree(h->fp4_s2);
+  (void)hipSetDevice(prev);
+  delete h;
+}
+
+int moe_decode_plan(moe_decode_t h, int32_t M, int32_t* out, int32_t n) {
+  if (!h || !out || n < 9 || M < 1) return MOE_DECODE_ERR_INVALID_ARG;
+  if (M > h->cfg.max_tokens) return MOE_DECODE_ERR_TOO_MANY_TOKENS;
+  const Plan p = make_plan(h->cfg, M, h->fp4_wgs1, h->fp4_wgs2, h->wgp_wgs1, h->wgp_wgs2);
+  out[0] = p.path;
+  out[1] = p.s1;
+  out[2] = p.s2;
+  const int blk = p.path == MOE_GEMM_FP4 ? 2 : 1;  // the FP4 plan counts 256-value steps
+  out[3] = p.ks1 * blk;
+  out[4] = p.ks2 * blk;
+  out[5] = p.grid1;
+  out[6] = p.grid2;
+  out[7] = p.tpw1;
+  out[8] = p.tpw2;
+  if (n >= 15) {
+    out[9] = p.ss1;
+    out[10] = p.ss2;
+    out[11] = p.sks1;
+    out[12] = p.sks2;
+    out[13] = p.sunits1;
+    out[14] = p.sunits2;
+  }
+  if (n >= 17) {
+    out[15] = p.path == MOE_GEMM_MFMA ? p.kp1 : 1;
+    out[16] = p.path == MOE_GEMM_MFMA ? p.kp2 : 1;
+  }
+  if (n >= 18) out[17] = 5 - (p.fuse_combine ? 1 : 0) - (p.fuse_swiglu ? 1 : 0);
+  if (n >= 20) {
+    out[18] = p.persist1;
+    out[19] = p.persist2;
+  }
+  return MOE_DECODE_OK;
+}
+
+int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits, const float* bias,
+                   void* slots, int32_t* ids, float* weights, void* combined, void* shared_out,
+                   void* stream) {
+  if (!h) return MOE_DECODE_ERR_INVALID_ARG;
+  if (M < 0) return MOE_DECODE_ERR_INVALID_ARG;
+  if (M > h->cfg.max_tokens) return MOE_DECODE_ERR_TOO_MANY_TOKENS;
+  if (M == 0) return MOE_DECODE_OK;
+  const int r = check_run_pointers(h->cfg, x, logits, bias, slots, ids, weights, combined, shared_out);
+  if (r != MOE_DECODE_OK) return r;
+  return run_layer(h, M, x, logits, bias, slots, ids, weights, combined, shared_out,
+                   static_cast<hipStream_t>(stream));
+}
+
+int moe_decode_run_noalloc(const moe_decode_config* cfg, int32_t M, const void* x, const void* logits,
+                           const float* bias, void* slots, int32_t* ids, float* weights, void* combined,
+                           void* shared_out, void* stream) {
+  if (!cfg || M < 0) return MOE_DECODE_ERR_INVALID_ARG;
+  if (M > MOE_DECODE_MAX_TOKENS) return MOE_DECODE_ERR_TOO_MANY_TOKENS;
+  moe_decode_handle h{};  // on the stack; its workspace is this device's scratch
+  h.cfg = *cfg;
+  moe_decode_config& c = h.cfg;
+  c.max_tokens = std::max(M, 1);
+  const int v = validate_config(&c);
+  if (v != MOE_DECODE_OK) return v;
+  // no handle-owned copies: FP4 scales are reordered, and packed shared
+  // scales converted, into memory a handle owns
+  if (c.weight_format != MOE_WEIGHTS_FP8 || (c.shared_inter > 0 && c.shared_scale_format != MOE_SCALES_F32))
+    return MOE_DECODE_ERR_UNSUPPORTED;
+  if (M == 0) return MOE_DECODE_OK;
+  const int r = check_run_pointers(c, x, logits, bias, slots, ids, weights, combined, shared_out);
+  if (r != MOE_DECODE_OK) return r;
+  h.ws_bytes = layout_workspace(c, h.reg, &h.shared_own_quant);
+  if (h.ws_bytes > kScratchBytes) return MOE_DECODE_ERR_SCRATCH_TOO_SMALL;
+  if (hipGetDevice(&h.device) != hipSuccess) return MOE_DECODE_ERR_HIP;
+  h.ws = device_scratch(h.device);
+  if (!h.ws) return MOE_DECODE_ERR_HIP;
+  h.words = (M + 63) / 64;
+  h.s13 = static_cast<const float*>(c.sw13_scale);
+  h.s2 = static_cast<const float*>(c.sw2_scale);
+  h.wgp_wgs1 = cached_wgp_wgs(h.device, c.hidden / kTile);
+  h.wgp_wgs2 = cached_wgp_wgs(h.device, c.inter / kTile);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // The buffer holds the previous call's data, in that call's layout: clear
+  // the arrival counters this step's kernels expect at zero.
+  const Plan p = make_plan(c, M, 0, 0, h.wgp_wgs1, h.wgp_wgs2);
+  auto words_of = [&](int i) { return reinterpret_cast<int32_t*>(h.ws + h.reg[i].off); };
+  hipError_t e = launch_zero_words(words_of(kCtrl), h.reg[kCtrl].bytes / sizeof(int32_t), s);
+  if (e == hipSuccess && p.fuse_combine)
+    e = launch_zero_words(words_of(kCount), h.reg[kCount].bytes / sizeof(int32_t), s);
+  if (e == hipSuccess && p.fuse_swiglu)
+    e = launch_zero_words(words_of(kSwCount), h.reg[kSwCount].bytes / sizeof(int32_t), s);
+  if (e != hipSuccess) return MOE_DECODE_ERR_HIP;
+  return run_layer(&h, M, x, logits, bias, slots, ids, weights, combined, shared_out, s);
 }
 
 int moe_decode_debug_stage(moe_decode_t h, int32_t stage, void* dst, size_t bytes, void* stream) {

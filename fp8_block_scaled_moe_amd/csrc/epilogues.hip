@@ -1,6 +1,8 @@
 // The SwiGLU/requant and slot/combine steps, each one launch that also covers
 // the shared expert when there is one; the arithmetic lives in
 // epilogue_device.h. Also the one-time conversion of packed UE8M0 scales.
+#include <algorithm>
+
 #include "epilogue_device.h"
 
 namespace moe {
@@ -57,6 +59,11 @@ __global__ void unpack_ue8m0_kernel(const int32_t* packed, int n, int k, float* 
   if (row == lead) out[(size_t)(row / kTile) * groups + g] = __uint_as_float(e << 23);
 }
 
+__global__ void zero_words_kernel(int32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
 // One workgroup per (token, 64 hidden columns).
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   __shared__ float lds[kMaxTopK * 64];
@@ -70,6 +77,13 @@ hipError_t launch_swiglu_requant(const SwigluArgs& a, hipStream_t s) {
   const int waves = a.R * (a.I / kTile) + (a.spart ? a.M * (a.Is / kTile) : 0);
   const int wpg = kThreads / kWave;
   hipLaunchKernelGGL(swiglu_requant_kernel, dim3((waves + wpg - 1) / wpg), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_words(int32_t* p, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(zero_words_kernel, dim3(blocks), dim3(256), 0, s, p, n);
   return hipGetLastError();
 }
 

@@ -217,6 +217,8 @@ int gemm_wgp_resident_wgs(int nkb);
 hipError_t launch_unpack_ue8m0(const int32_t* packed, int n, int k, float* out, int32_t* bad,
                                hipStream_t s);
 hipError_t launch_swiglu_requant(const SwigluArgs& a, hipStream_t s);
+// Zeroes n int32 words at p with a kernel (no memset node under graph capture).
+hipError_t launch_zero_words(int32_t* p, size_t n, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_codec_check(const float* in, uint8_t* q, float* dq, int n, hipStream_t s);
 

@@ -59,6 +59,8 @@ extern "C" {
 #define MOE_DECODE_ERR_TOO_MANY_TOKENS (-3) /* M > max_tokens of the handle */
 #define MOE_DECODE_ERR_HIP (-4)             /* a HIP call or kernel launch failed */
 #define MOE_DECODE_ERR_OUT_OF_MEMORY (-5)   /* workspace allocation failed */
+#define MOE_DECODE_ERR_SCRATCH_TOO_SMALL (-6) /* moe_decode_run_noalloc: the step needs more
+                                                 than MOE_DECODE_NOALLOC_SCRATCH_BYTES */
 
 #define MOE_DTYPE_F32 0
 #define MOE_DTYPE_BF16 1
@@ -224,6 +226,35 @@ int moe_decode_create(const moe_decode_config* cfg, moe_decode_t* out);
 int moe_decode_run(moe_decode_t h, int32_t M, const void* x, const void* logits,
                    const float* bias, void* slots, int32_t* ids, float* weights,
                    void* combined, void* shared_out, void* stream);
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, serving loops and harnesses that forbid allocation.
+ *
+ * moe_decode_run without a handle: the same launches and results as
+ * moe_decode_run on a handle created from *cfg (bit-identical outputs), with
+ * the workspace in a fixed device buffer of MOE_DECODE_NOALLOC_SCRATCH_BYTES
+ * that the library holds on each GPU it runs on until the process ends.
+ * Nothing is allocated: no hipMalloc, no hipFree, no allocating library call.
+ * The buffer's address is looked up once per device, on the first call made
+ * with that device current. The call runs on the current device.
+ *  - cfg as for moe_decode_create, except that max_tokens is not used (M
+ *    sizes the workspace) and only what needs no handle-owned copy is taken:
+ *    MOE_WEIGHTS_FP8 routed weights, and a shared expert only with
+ *    MOE_SCALES_F32 scales (UNSUPPORTED otherwise).
+ *  - Other arguments and errors as moe_decode_run; 0 <= M <= 256. A step
+ *    whose workspace exceeds the buffer returns SCRATCH_TOO_SMALL and
+ *    enqueues nothing (at DeepSeek-V3 shapes, H = 7168, I = 2048, top-8, up
+ *    to 64 tokens fit).
+ *  - Every call on one GPU shares that GPU's buffer, and the buffer keeps
+ *    the last call's contents (the call clears the counters it needs at
+ *    zero, with a kernel, before its other launches). Calls that overlap on
+ *    one GPU (on different streams, or from different threads without
+ *    ordering) race on the buffer and give undefined results. Handles
+ *    created with moe_decode_create do not use it. */
+#define MOE_DECODE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int moe_decode_run_noalloc(const moe_decode_config* cfg, int32_t M, const void* x, const void* logits,
+                           const float* bias, void* slots, int32_t* ids, float* weights, void* combined,
+                           void* shared_out, void* stream);
 
 /* Passage: the ownership rule of moe_decode_create (the pages' layer objects
  * release what they allocated when they go away; borrowed weights are left
