@@ -358,8 +358,11 @@ size_t layout_workspace(const moe_decode_config& c, Region reg[kRegions], bool* 
       sp2 * sizeof(float),            // shared down partials
       Rcap * sizeof(int32_t) * 4,     // job table (at most one job per route)
       Rcap * sizeof(int32_t),         // job of each route
-      fp4 ? 0 : T * (H / 16) * sizeof(int32_t),  // arrival counts (at least 16 rows per workgroup)
-      fp4 ? 0 : Rcap * (I / kTile) * sizeof(int32_t),  // arrival counts per (route, hidden block)
+      // arrival counts (at least 16 rows per workgroup); FP4 form: GEMM1's
+      // partial slots per (job, 64-row tile), jobs never outnumbering routes
+      fp4 ? Rcap * (2 * I / 64) * sizeof(int32_t) : T * (H / 16) * sizeof(int32_t),
+      // arrival counts per (route, hidden block); FP4 form: GEMM2's slots per (job, tile)
+      fp4 ? Rcap * (H / 64) * sizeof(int32_t) : Rcap * (I / kTile) * sizeof(int32_t),
   };
   size_t off = 0;
   for (int i = 0; i < kRegions; ++i) {
@@ -550,7 +553,8 @@ int run_layer(moe_decode_handle* h, int32_t M, const void* x, const void* logits
   sa.shs = atf(kSHs);
   sa.fp4 = fp4;
   sa.hs4 = at(kHs);
-  sa.stream = StreamDesc{b.ctrl, b.rjob, 2 * c.inter / kRowsPerWg, c.hidden / (2 * kTile), h->fp4_wgs1};
+  sa.stream = StreamDesc{reinterpret_cast<const int32_t*>(at(kCount)), b.rjob, R, 2 * c.inter / kRowsPerWg,
+                         c.hidden / (2 * kTile)};
   sa.ids = ids;
   sa.lb = lb;
   sa.lc = lc;
@@ -571,7 +575,8 @@ int run_layer(moe_decode_handle* h, int32_t M, const void* x, const void* logits
   ca.lb = lb;
   ca.lc = lc;
   ca.fp4 = fp4;
-  ca.stream = StreamDesc{b.ctrl, b.rjob, c.hidden / kRowsPerWg, c.inter / (2 * kTile), h->fp4_wgs2};
+  ca.stream = StreamDesc{reinterpret_cast<const int32_t*>(at(kSwCount)), b.rjob, R, c.hidden / kRowsPerWg,
+                         c.inter / (2 * kTile)};
 
   // problem descriptor of N x K weights and their activations
   auto problem = [](const void* w, const void* ws, const uint8_t* aq, const float* as, float* part, int N,
@@ -613,6 +618,7 @@ int run_layer(moe_decode_handle* h, int32_t M, const void* x, const void* logits
   if (fp4) g1.p[1].ws8 = h->fp4_s13;
   g1.pass_routes = p.pass_routes;
   g1.stream_wgs = h->fp4_wgs1;
+  g1.stream_counts = reinterpret_cast<int32_t*>(at(kCount));
   if (shared) {
     g1.p[0] = problem(c.sw13, h->s13, sxq, sxs, atf(kSP1), 2 * c.shared_inter, c.hidden, p.ss1, p.sks1, M, 1,
                       p.stpw1);
@@ -645,6 +651,7 @@ int run_layer(moe_decode_handle* h, int32_t M, const void* x, const void* logits
   if (fp4) g2.p[1].ws8 = h->fp4_s2;
   g2.pass_routes = p.pass_routes;
   g2.stream_wgs = h->fp4_wgs2;
+  g2.stream_counts = reinterpret_cast<int32_t*>(at(kSwCount));
   if (shared) {
     g2.p[0] = problem(c.sw2, h->s2, at(kSHq), atf(kSHs), atf(kSP2), c.hidden, c.shared_inter, p.ss2, p.sks2,
                       M, 1, p.stpw2);

@@ -3,51 +3,55 @@
 // scale per 16 values along K, against activations staged to E2M1 with their
 // own per-16 UE4M3 scales,
 //   out[r, n] = sum_g dec(Sw[e, n, g]) * dec(Sa[row(r), g]) * sum_{i in g} W[e, n, i] * A[row(r), i].
-// gfx950's FP4 matrix instructions take power-of-two scales per 32 values, not
-// UE4M3 per 16, so the codes are widened in software, exactly, to F16 pairs:
-// v_dot2 multiplies them exactly and adds in FP32, and a 16-value group's sum
-// of E2M1 products (a multiple of 1/4 below 600) is exact. Times the
-// activation scale it is still exact (at most 16 significant bits); the
-// weight scale then joins in one fused multiply-add into the FP32 total.
+//
+// On the matrix cores. gfx950's FP4 matrix instructions take power-of-two
+// scales per 32 values, not UE4M3 per 16, so the codes are widened to F16
+// with each value multiplied by its group's scale: an E2M1 value (two
+// significant bits) times a UE4M3 scale (four) is exact in F16, between
+// 2^-10 and 2688, on both operands. v_mfma_f32_4x4x4_16b_f16 then multiplies
+// exactly and adds in FP32. Its sixteen 4 x 4 x 4 blocks are laid along K:
+// for a wave's 16 rows and one 256-value item, instruction (row group g, k
+// step c) gives block b rows 4g .. 4g + 3 and the four values 16b + 4c ..
+// 16b + 4c + 3, so block b covers exactly scale group b of the item and a
+// lane's activation operand (block b, route x) is the same for all four row
+// groups: the activations are widened once per item for the 16 rows. The
+// blocks' partial sums are added across lanes when a tile ends. A job is up
+// to kFp4JobRoutes (four) routes of one expert, a block's four columns, so
+// an expert's weights are read once for up to four of its routes (decode
+// batches rarely give one GPU's expert more; more take further passes).
 //
 // Work split: the stream of (job, 64-row tile, 256-value step) items is cut
 // evenly over the workgroups (stream_device.h), so every workgroup reads the
-// same weight bytes however few experts are touched. A job is up to
-// kFp4JobRoutes (two) routes of one expert (the routing kernel builds the
-// job table), so an expert's weights are read once per two of its routes:
-// the inner product costs VALU work per route, and one GPU's share of
-// experts sees one or two routes per touched expert at decode batch sizes
-// (more routes per expert are the matrix-core path's case). Each of the four
-// waves owns 16 rows of the current tile; the jobs' activations (packed codes
-// and scale bytes, a ninth of the weight bytes per route and K value) are
-// staged in LDS once per job over the whole K. When a tile ends, or the
-// workgroup's range does, each wave writes its rows' sums for the job's
-// routes to the tile's partial slot.
+// same weight bytes however few experts are touched. Each of the four waves
+// owns 16 rows of the current tile.
 //
-// Per item a wave reads 16 rows x 128 bytes (eight lanes per row; rows rg and
-// rg + 8 per lane) plus the rows' 16 scale bytes each, kDepth items ahead of
-// use, straight across tile and job boundaries. The weight scales are read
-// from a copy reordered once at create (reorder_fp4_scales below): there one
-// item's scales of a wave's 16 rows are 256 contiguous bytes in lane order,
-// four per lane, so each item costs one coalesced load and every scale line
-// is fetched once (read in place, 16 bytes of each row's 128-byte line per
-// item, the lines are fetched again for most items).
+// Per item a wave reads 16 rows x 128 bytes with full-line loads (eight lanes
+// per row) and passes them through a private LDS tile to lane 4b + x as rows
+// x, 4 + x, 8 + x, 12 + x, bytes 8b .. 8b + 7; the rows' scales come from a
+// copy reordered once at create (reorder_fp4_scales below) as one coalesced
+// 4-byte load per lane; each lane's activation bytes (8) and scale byte come
+// from L2 straight into registers. The job count, the first job descriptors
+// and the first route entries are read under one wait at the start, so the
+// first weight request follows one memory round trip.
 #include <algorithm>
 
 #include "fp4_device.h"
+#include "gemm_device.h"
 #include "stream_device.h"
 
 namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kDepth = 2;                              // items in flight per wave
-constexpr int kStepValues = 256;                       // K values per item
-constexpr int kStepBytes = kStepValues / 2;            // packed bytes of a row's item
-constexpr int kStepScales = kStepValues / kFp4Group;   // scale bytes of a row's item
-constexpr int kJobBufs = 2;                            // jobs staged at once
-constexpr int kInfoInts = 2 + kFp4JobRoutes;           // a staged job's route count, expert, routes
-constexpr int kStageBatch = 4;                         // 16-byte staging loads in flight per thread
+constexpr int kDepth = 2;                             // items in flight per wave
+constexpr int kStepValues = 256;                      // K values per item
+constexpr int kStepBytes = kStepValues / 2;           // packed bytes of a row's item
+constexpr int kStepScales = kStepValues / kFp4Group;  // scale bytes of a row's item
+constexpr int kFp4TileStride = kStepBytes + 16;       // LDS row stride (conflict-free)
+constexpr int kFp4TileBytes = 16 * kFp4TileStride;
+constexpr int kSpec = kThreads;  // job descriptors and route entries read at the start
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 
 struct Cursor {
   int j, tile, s;  // job, 64-row tile, K step
@@ -63,207 +67,175 @@ __device__ __forceinline__ void advance(Cursor& c, int tiles, int steps) {
   }
 }
 
-// Route i of a job from its routes held in registers (selects, no indexing).
-__device__ __forceinline__ int pick_route(const int (&rt)[kFp4JobRoutes], int i) {
-  int v = rt[0];
-#pragma unroll
-  for (int k = 1; k < kFp4JobRoutes; ++k) v = i == k ? rt[k] : v;
-  return v;
+// The (s, s) F16 pair of byte i of w (a UE4M3 scale), exact.
+template <int kByte>
+__device__ __forceinline__ half2_t scale_pair(uint32_t w) {
+  constexpr uint32_t sel = kByte * 0x00000101u;  // bytes i, i in the low half
+  return e4m3x2_to_f16x2<false>(__builtin_amdgcn_perm(w, w, sel));
 }
 
-// A job's descriptor {expert, first route entry, count} and routes.
-__device__ __forceinline__ void load_job(const GemmProblem& a, int j, int4& jd, int (&rt)[kFp4JobRoutes]) {
-  jd = a.b.jobs[j];
-#pragma unroll
-  for (int i = 0; i < kFp4JobRoutes; ++i) rt[i] = i < jd.z ? a.b.routes[jd.y + i] : 0;
-}
-
-// A job's activations over the whole K into an LDS buffer
-// ([kFp4JobRoutes][S][128] packed codes, then [kFp4JobRoutes][S][16] scale
-// bytes) and its route count, expert and
-// routes into `info`. The whole workgroup calls it; a barrier must follow
-// before the buffer is read.
-__device__ void stage_job(const GemmProblem& a, const int4& jd, const int (&rt)[kFp4JobRoutes], int S,
-                          unsigned char* codes, int* info) {
-  const int nr = jd.z;
-  const int tid = threadIdx.x;
-  if (tid == 0) {
-    info[0] = nr;
-    info[1] = jd.x;
-  }
-  if (tid < nr) info[2 + tid] = pick_route(rt, tid);
-  unsigned char* scales = codes + (size_t)kFp4JobRoutes * S * kStepBytes;
-  const int per_route = S * (kStepBytes / 16 + kStepScales / 16);  // 16-byte chunks
-  const int total = nr * per_route;
-  const size_t row_bytes = (size_t)a.K / 2, row_scales = (size_t)a.K / kFp4Group;
-  for (int base = 0; base < total; base += kStageBatch * kThreads) {
-    u32x4_t v[kStageBatch];
-    unsigned char* dst[kStageBatch];
-#pragma unroll
-    for (int q = 0; q < kStageBatch; ++q) {
-      const int c = base + q * kThreads + tid;
-      dst[q] = nullptr;
-      if (c < total) {
-        const int r = c / per_route, cc = c - r * per_route;
-        const size_t row = (size_t)(pick_route(rt, r) / a.act_div);
-        const uint8_t* src;
-        if (cc < S * (kStepBytes / 16)) {
-          src = a.aq + row * row_bytes + (size_t)cc * 16;
-          dst[q] = codes + ((size_t)r * S * kStepBytes + (size_t)cc * 16);
-        } else {
-          const int sc = cc - S * (kStepBytes / 16);
-          src = a.as8 + row * row_scales + (size_t)sc * 16;
-          dst[q] = scales + ((size_t)r * S * kStepScales + (size_t)sc * 16);
-        }
-        v[q] = *reinterpret_cast<const u32x4_t*>(src);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < kStageBatch; ++q)
-      if (dst[q]) *reinterpret_cast<u32x4_t*>(dst[q]) = v[q];
-  }
+// Four E2M1 values (bytes kB and kB + 1 of w, low nibbles first) times s.
+template <int kB>
+__device__ __forceinline__ half4_t widen4(uint32_t w, half2_t s) {
+  const half2_t lo = e2m1x2_to_f16x2<kB>(w) * s, hi = e2m1x2_to_f16x2<kB + 1>(w) * s;
+  return half4_t{lo.x, lo.y, hi.x, hi.y};
 }
 
 template <int kRole>
 __global__ __launch_bounds__(kThreads) void gemm_fp4_kernel(GemmArgs args) {
-  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ __align__(16) unsigned char tiles_lds[4 * kFp4TileBytes];
+  __shared__ int4 spec_jobs[kSpec];
+  __shared__ int spec_routes[kSpec];
   const GemmProblem& a = args.p[1];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: addresses stay scalar
+
+  // One round trip: the job count beside the first job descriptors and route
+  // entries (jobs never outnumber routes, so both reads stay in their tables).
+  const int nspec = min(a.R, kSpec);
+  int4 jd_t = make_int4(0, 0, 0, 0);
+  int rt_t = 0;
+  if (tid < nspec) {
+    jd_t = a.b.jobs[tid];
+    rt_t = a.b.routes[tid];
+  }
+  const int J = a.b.ctrl[2];
+  if (tid < nspec) {
+    spec_jobs[tid] = jd_t;
+    spec_routes[tid] = rt_t;
+  }
+  __syncthreads();
+
   const int S = a.K / kStepValues, tiles = a.N / kRowsPerWg;
   const int per_job = tiles * S;  // > kDepth for every accepted shape
-  const StreamMap m = stream_map(a.b.ctrl[2], tiles, S, args.stream_wgs);
+  const StreamMap m = stream_map(J, tiles, S, args.stream_wgs);
   if ((int)blockIdx.x >= m.Wa) return;
-  const int64_t lo = stream_begin(blockIdx.x, m), hi = stream_begin(blockIdx.x + 1, m);
+  const uint32_t lo = stream_begin(blockIdx.x, m), hi = stream_begin(blockIdx.x + 1, m);
   if (lo >= hi) return;  // no items at all
   const int n = (int)(hi - lo);
 
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int rg = lane >> 3, ch = lane & 7;
-  const size_t row_bytes = (size_t)a.K / 2;
-  const size_t buf_bytes = (size_t)kFp4JobRoutes * S * (kStepBytes + kStepScales);
-  int* info = reinterpret_cast<int*>(smem + kJobBufs * buf_bytes);  // [kJobBufs][kInfoInts]
+  const int rg = lane >> 3, ch = lane & 7;  // load layout: rows rg and rg + 8, bytes 16ch..
+  const int x = lane & 3, blk = lane >> 2;  // MFMA layout: column / row x of block blk
+  const uint32_t row_bytes = (uint32_t)a.K / 2, row_scales = (uint32_t)a.K / kFp4Group;
+  uint8_t* tile = tiles_lds + wave * kFp4TileBytes;
 
-  const int j0 = (int)(lo / per_job), jlast = (int)((hi - 1) / per_job);
+  const int j0 = (int)(lo / (uint32_t)per_job), jlast = (int)((hi - 1) / (uint32_t)per_job);
   if (jlast > j0 + 1) return;  // cannot happen: a range holds at most one job's items
-  Cursor c{j0, (int)((lo % per_job) / S), (int)(lo % S)};  // the item being summed
-  Cursor pc = c;                                              // the next item to request
+  Cursor c{j0, (int)((lo % (uint32_t)per_job) / S), (int)(lo % (uint32_t)S)};  // the item being summed
+  Cursor pc = c;                                                               // the next item to request
   int pleft = n;
 
-  // The range's (at most two) jobs, read before any weight is requested so
-  // that no wait for them queues behind the weight stream; job j sits in
-  // buffer j - j0.
-  int4 jd0, jd1 = make_int4(0, 0, 0, 0);
-  int rt0[kFp4JobRoutes], rt1[kFp4JobRoutes] = {};
-  load_job(a, j0, jd0, rt0);
-  if (jlast > j0) load_job(a, j0 + 1, jd1, rt1);
-  // experts of the two jobs, uniform across the workgroup
+  // The range's (at most two) jobs: expert and route count (uniform), the
+  // route of this lane's column x (the job's first route for columns past
+  // the count, whose sums are not written), its activation offsets.
+  auto job_of = [&](int j) { return j < nspec ? spec_jobs[j] : a.b.jobs[j]; };
+  auto route_at = [&](int i) { return i < nspec ? spec_routes[i] : a.b.routes[i]; };
+  const int4 jd0 = job_of(j0), jd1 = jlast > j0 ? job_of(j0 + 1) : jd0;
   const int e0 = __builtin_amdgcn_readfirstlane(jd0.x), e1 = __builtin_amdgcn_readfirstlane(jd1.x);
+  const int nr0 = __builtin_amdgcn_readfirstlane(jd0.z), nr1 = __builtin_amdgcn_readfirstlane(jd1.z);
+  const int rt0 = route_at(jd0.y + (x < nr0 ? x : 0)), rt1 = route_at(jd1.y + (x < nr1 ? x : 0));
+  // 32-bit offsets of this lane's activation bytes and scale byte in step 0
+  const uint32_t xo0 = (uint32_t)(rt0 / a.act_div) * row_bytes + blk * 8;
+  const uint32_t xo1 = (uint32_t)(rt1 / a.act_div) * row_bytes + blk * 8;
+  const uint32_t so0 = (uint32_t)(rt0 / a.act_div) * row_scales + blk;
+  const uint32_t so1 = (uint32_t)(rt1 / a.act_div) * row_scales + blk;
   int pe = e0;
+  uint32_t pxo = xo0, pso = so0;
 
   u32x4_t wa[kDepth], wb[kDepth];
-  uint32_t sw[kDepth];
-  // this lane's offsets within its wave's 16-row group: rows rg (and rg + 8),
-  // bytes 16ch.. of an item; four scale bytes per lane in the reordered scales
-  const size_t lane_w = (size_t)rg * row_bytes + ch * 16;
-  const size_t lane_s = (size_t)lane * 4;
-  // Requests the item under the requesting cursor into buffer q; past the
-  // range's end the cursor stays on its last item (a repeat read, from L2).
-  auto request = [&](int q) {
+  uint32_t sw[kDepth], sx[kDepth];
+  uint2 xv[kDepth];
+  const uint32_t lane_w = (uint32_t)rg * row_bytes + ch * 16, lane_s = (uint32_t)lane * 4;
+  // Requests the item under the requesting cursor into buffer q: the weights
+  // and their scales (request_w), then the activations (request_x, which then
+  // moves the cursor on). Addresses are a uniform base plus this lane's
+  // 32-bit offset. Past the range's end the cursor stays on its last item (a
+  // repeat read, from L2).
+  auto request_w = [&](int q) {
     const size_t group = (size_t)pe * (a.N / 16) + pc.tile * (kRowsPerWg / 16) + wave;  // 16-row group
-    const uint8_t* p = a.w + (group * 16 * row_bytes + (size_t)pc.s * kStepBytes) + lane_w;
-    wa[q] = load_stream16(p);
-    wb[q] = load_stream16(p + 8 * row_bytes);
-    sw[q] = __builtin_nontemporal_load(
-        reinterpret_cast<const uint32_t*>(a.ws8 + ((group * S + pc.s) * kWave * 4) + lane_s));
+    const uint8_t* w = a.w + group * 16 * row_bytes + (size_t)pc.s * kStepBytes;
+    const uint8_t* ws = a.ws8 + (group * S + pc.s) * (kWave * 4);
+    wa[q] = load_stream16(w + lane_w);
+    wb[q] = load_stream16(w + (lane_w + 8 * row_bytes));
+    sw[q] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(ws + lane_s));
+  };
+  auto request_x = [&](int q) {
+    const uint8_t* xs = a.aq + (size_t)pc.s * kStepBytes;
+    const uint8_t* ss = a.as8 + (size_t)pc.s * kStepScales;
+    xv[q] = *reinterpret_cast<const uint2*>(xs + pxo);
+    sx[q] = ss[pso];
     if (--pleft > 0) {
       const int pj = pc.j;
       advance(pc, tiles, S);
-      if (pc.j != pj) pe = e1;
-    }
-  };
-#pragma unroll
-  for (int q = 0; q < kDepth; ++q) request(q);
-
-  stage_job(a, jd0, rt0, S, smem, info);
-  if (jlast > j0) stage_job(a, jd1, rt1, S, smem + buf_bytes, info + kInfoInts);
-  __syncthreads();
-
-  float acc_a[kFp4JobRoutes], acc_b[kFp4JobRoutes];
-#pragma unroll
-  for (int i = 0; i < kFp4JobRoutes; ++i) acc_a[i] = acc_b[i] = 0.f;
-
-  // One item from buffer q; `refill` requests the item kDepth further on.
-  auto process = [&](int q, bool refill) {
-    const int buf = c.j - j0;
-    const int nr = info[buf * kInfoInts];
-    const unsigned char* xc = smem + buf * buf_bytes;
-    const unsigned char* xs = xc + (size_t)kFp4JobRoutes * S * kStepBytes;
-
-    half2_t w0[16], w1[16];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      w0[4 * d] = e2m1x2_to_f16x2<0>(wa[q][d]);
-      w0[4 * d + 1] = e2m1x2_to_f16x2<1>(wa[q][d]);
-      w0[4 * d + 2] = e2m1x2_to_f16x2<2>(wa[q][d]);
-      w0[4 * d + 3] = e2m1x2_to_f16x2<3>(wa[q][d]);
-      w1[4 * d] = e2m1x2_to_f16x2<0>(wb[q][d]);
-      w1[4 * d + 1] = e2m1x2_to_f16x2<1>(wb[q][d]);
-      w1[4 * d + 2] = e2m1x2_to_f16x2<2>(wb[q][d]);
-      w1[4 * d + 3] = e2m1x2_to_f16x2<3>(wb[q][d]);
-    }
-    // weight scales of groups 2ch and 2ch + 1 of rows rg (bytes 0, 1) and rg + 8 (bytes 2, 3)
-    const float s0a = e4m3_value(sw[q]), s1a = e4m3_value(sw[q] >> 8);
-    const float s0b = e4m3_value(sw[q] >> 16), s1b = e4m3_value(sw[q] >> 24);
-    if (refill) request(q);
-
-#pragma unroll
-    for (int i = 0; i < kFp4JobRoutes; ++i) {
-      if (i < nr) {
-        const size_t rs = (size_t)i * S + c.s;
-        const u32x4_t xw = *reinterpret_cast<const u32x4_t*>(xc + rs * kStepBytes + ch * 16);
-        const uint32_t xsv = *reinterpret_cast<const uint16_t*>(xs + rs * kStepScales + ch * 2);
-        float pa0 = 0.f, pb0 = 0.f, pa1 = 0.f, pb1 = 0.f;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const half2_t x0 = e2m1x2_to_f16x2<0>(xw[d]), x1 = e2m1x2_to_f16x2<1>(xw[d]);
-          const half2_t x2 = e2m1x2_to_f16x2<2>(xw[d]), x3 = e2m1x2_to_f16x2<3>(xw[d]);
-          float& pa = d < 2 ? pa0 : pa1;
-          float& pb = d < 2 ? pb0 : pb1;
-          pa = __builtin_amdgcn_fdot2(w0[4 * d], x0, pa, false);
-          pb = __builtin_amdgcn_fdot2(w1[4 * d], x0, pb, false);
-          pa = __builtin_amdgcn_fdot2(w0[4 * d + 1], x1, pa, false);
-          pb = __builtin_amdgcn_fdot2(w1[4 * d + 1], x1, pb, false);
-          pa = __builtin_amdgcn_fdot2(w0[4 * d + 2], x2, pa, false);
-          pb = __builtin_amdgcn_fdot2(w1[4 * d + 2], x2, pb, false);
-          pa = __builtin_amdgcn_fdot2(w0[4 * d + 3], x3, pa, false);
-          pb = __builtin_amdgcn_fdot2(w1[4 * d + 3], x3, pb, false);
-        }
-        const float sx0 = e4m3_value(xsv), sx1 = e4m3_value(xsv >> 8);
-        acc_a[i] = fmaf(pa1 * sx1, s1a, fmaf(pa0 * sx0, s0a, acc_a[i]));
-        acc_b[i] = fmaf(pb1 * sx1, s1b, fmaf(pb0 * sx0, s0b, acc_b[i]));
+      if (pc.j != pj) {
+        pe = e1;
+        pxo = xo1;
+        pso = so1;
       }
     }
-    return nr;
+  };
+#pragma unroll
+  for (int q = 0; q < kDepth; ++q) {
+    request_w(q);
+    request_x(q);
+  }
+
+  float4_t acc[4] = {};  // row groups 0..3 (rows 4r .. 4r + 3): block blk's sum for route x
+
+  // One item from buffer q; `refill` requests the item kDepth further on.
+  // Each register set is refilled once its data is consumed: the weights
+  // after they pass through the tile, the activations after the MFMAs.
+  auto process = [&](int q, bool refill) {
+    *reinterpret_cast<u32x4_t*>(tile + rg * kFp4TileStride + ch * 16) = wa[q];
+    *reinterpret_cast<u32x4_t*>(tile + (rg + 8) * kFp4TileStride + ch * 16) = wb[q];
+    const half2_t ps[4] = {scale_pair<0>(sw[q]), scale_pair<1>(sw[q]), scale_pair<2>(sw[q]), scale_pair<3>(sw[q])};
+    if (refill) request_w(q);
+    wave_lds_fence();
+    uint2 wr[4];  // rows 4r + x, bytes 8blk .. 8blk + 7
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      wr[r] = *reinterpret_cast<const uint2*>(tile + (4 * r + x) * kFp4TileStride + blk * 8);
+    wave_lds_fence();
+    const half2_t pa = scale_pair<0>(sx[q]);
+    const half4_t b0 = widen4<0>(xv[q].x, pa), b1 = widen4<2>(xv[q].x, pa);
+    const half4_t b2 = widen4<0>(xv[q].y, pa), b3 = widen4<2>(xv[q].y, pa);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      acc[r] = __builtin_amdgcn_mfma_f32_4x4x4f16(widen4<0>(wr[r].x, ps[r]), b0, acc[r], 0, 0, 0);
+      acc[r] = __builtin_amdgcn_mfma_f32_4x4x4f16(widen4<2>(wr[r].x, ps[r]), b1, acc[r], 0, 0, 0);
+      acc[r] = __builtin_amdgcn_mfma_f32_4x4x4f16(widen4<0>(wr[r].y, ps[r]), b2, acc[r], 0, 0, 0);
+      acc[r] = __builtin_amdgcn_mfma_f32_4x4x4f16(widen4<2>(wr[r].y, ps[r]), b3, acc[r], 0, 0, 0);
+    }
+    if (refill) request_x(q);
   };
   // After item `done` (0-based in the range): at a tile's last step, or the
-  // range's last item, the rows' sums go to the tile's partial slot (rows rg
-  // and rg + 8; the eight lanes of a row hold consecutive 32-value pieces).
-  auto finish = [&](int done, int nr) {
+  // range's last item, the blocks' partials are added across lanes (a fixed
+  // butterfly over blocks 0 .. 15) and the live routes' sums go to the
+  // tile's partial slot: lane x (block 0) writes rows 4r .. 4r + 3 of the
+  // wave's 16 for route x.
+  auto finish = [&](int done) {
     if (c.s == S - 1 || done == n - 1) {
-      const int64_t tile_item = ((int64_t)c.j * tiles + c.tile) * S;
+      const uint32_t tile_item = ((uint32_t)c.j * tiles + c.tile) * S;
       const int slot = (int)blockIdx.x - stream_owner(tile_item, m);
-      const int row0 = c.tile * kRowsPerWg + wave * 16;
-      const int* rts = info + (c.j - j0) * kInfoInts + 2;
+      const bool first = c.j == j0;
+      // the workgroup summing the tile's last step records its slot count
+      if (c.s == S - 1 && tid == 0) args.stream_counts[(size_t)c.j * tiles + c.tile] = slot + 1;
 #pragma unroll
-      for (int i = 0; i < kFp4JobRoutes; ++i) {
-        if (i < nr) {
-          const float ta = group_sum<8>(acc_a[i]), tb = group_sum<8>(acc_b[i]);
-          if (ch == 0) {
-            float* dst = a.part + ((size_t)slot * a.R + rts[i]) * a.N + row0;
-            dst[rg] = ta;
-            dst[rg + 8] = tb;
-          }
+      for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = acc[r][i];
+          v += __shfl_xor(v, 4, kWave);
+          v += __shfl_xor(v, 8, kWave);
+          v += __shfl_xor(v, 16, kWave);
+          v += __shfl_xor(v, 32, kWave);
+          acc[r][i] = v;
         }
-        acc_a[i] = acc_b[i] = 0.f;
+        if (blk == 0 && x < (first ? nr0 : nr1)) {
+          float* dst = a.part + ((size_t)slot * a.R + (first ? rt0 : rt1)) * a.N + c.tile * kRowsPerWg + wave * 16 + 4 * r;
+          *reinterpret_cast<float4_t*>(dst) = acc[r];
+        }
+        acc[r] = float4_t{0.f, 0.f, 0.f, 0.f};
       }
     }
     advance(c, tiles, S);
@@ -272,28 +244,34 @@ __global__ __launch_bounds__(kThreads) void gemm_fp4_kernel(GemmArgs args) {
   int it = 0;
   for (; it + kDepth <= n; it += kDepth) {
 #pragma unroll
-    for (int q = 0; q < kDepth; ++q) finish(it + q, process(q, true));
+    for (int q = 0; q < kDepth; ++q) {
+      process(q, true);
+      finish(it + q);
+    }
   }
 #pragma unroll
   for (int q = 0; q < kDepth - 1; ++q)
-    if (it + q < n) finish(it + q, process(q, false));
+    if (it + q < n) {
+      process(q, false);
+      finish(it + q);
+    }
 }
 
 // The weight scales [rows, K/16] (rows = E * N, a multiple of 16) into the
 // kernel's layout: for 16-row group g, item s (256 values) and lane l =
-// 8 rg + ch, bytes ((g * S + s) * 64 + l) * 4 + {0, 1, 2, 3} = scales of
-// groups 2ch and 2ch + 1 (16 values each) of item s in rows 16g + rg, then
-// 16g + rg + 8. One thread per output word.
+// 4b + x, byte r of word (g * S + s) * 64 + l is the scale of group b of
+// item s in row 16g + 4r + x (the scales of the lane's MFMA operands). One
+// thread per output word.
 __global__ void reorder_fp4_scales_kernel(const uint8_t* src, uint32_t* dst, size_t words, int S) {
   const size_t w = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (w >= words) return;
-  const int l = (int)(w % kWave), rg = l >> 3, ch = l & 7;
+  const int l = (int)(w % kWave), x = l & 3, b = l >> 2;
   const size_t gs = w / kWave, g = gs / S;
   const int s = (int)(gs - g * S);
   const size_t row_scales = (size_t)S * kStepScales;
-  const uint8_t* a = src + (g * 16 + rg) * row_scales + (size_t)s * kStepScales + 2 * ch;
-  const uint8_t* b = a + 8 * row_scales;
-  dst[w] = (uint32_t)a[0] | ((uint32_t)a[1] << 8) | ((uint32_t)b[0] << 16) | ((uint32_t)b[1] << 24);
+  const uint8_t* p = src + (g * 16 + x) * row_scales + (size_t)s * kStepScales + b;
+  dst[w] = (uint32_t)p[0] | ((uint32_t)p[4 * row_scales] << 8) | ((uint32_t)p[8 * row_scales] << 16) |
+           ((uint32_t)p[12 * row_scales] << 24);
 }
 
 __global__ void codec_check_fp4_kernel(const float* in, uint8_t* q, float* dq, int n) {
@@ -315,17 +293,14 @@ __global__ void codec_check_fp4_kernel(const float* in, uint8_t* q, float* dq, i
 
 }  // namespace
 
-size_t gemm_fp4_lds_bytes(int K) {
-  const size_t S = (size_t)K / kStepValues;
-  return kJobBufs * kFp4JobRoutes * S * (kStepBytes + kStepScales) + kJobBufs * kInfoInts * sizeof(int);
-}
+size_t gemm_fp4_lds_bytes(int) { return 4 * (size_t)kFp4TileBytes + kSpec * (sizeof(int4) + sizeof(int)); }
 
-int gemm_fp4_resident_wgs(int K) {
+int gemm_fp4_resident_wgs(int) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(gemm_fp4_kernel<1>),
-                                                   kThreads, gemm_fp4_lds_bytes(K)) != hipSuccess) {
+                                                   kThreads, 0) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
@@ -333,11 +308,10 @@ int gemm_fp4_resident_wgs(int K) {
 }
 
 hipError_t launch_gemm_fp4(const GemmArgs& a, int role, int grid, hipStream_t s) {
-  const size_t lds = gemm_fp4_lds_bytes(a.p[1].K);
   if (role == 1)
-    hipLaunchKernelGGL(gemm_fp4_kernel<1>, dim3(grid), dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL(gemm_fp4_kernel<1>, dim3(grid), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(gemm_fp4_kernel<2>, dim3(grid), dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL(gemm_fp4_kernel<2>, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -24,15 +24,14 @@ struct Buckets {
   int32_t* rjob;     // [M*k] job of each local route
 };
 
-// How the FP4 GEMM's stream of work items (job, 64-row tile, 256-value step;
-// the step fastest) is split over its workgroups, and where the epilogues
-// find a tile's partial sums.
+// Where the epilogues find the FP4 GEMM's partial sums of a tile: the GEMM
+// records the partial slots of every (job, 64-row tile) (stream_device.h).
 struct StreamDesc {
-  const int32_t* ctrl;  // ctrl[2] = J
-  const int32_t* rjob;  // job of each route
-  int tiles;            // N / 64
-  int steps;            // K / 256
-  int wgs;              // resident workgroups of the GEMM launch
+  const int32_t* counts;  // [J, tiles] partial slots, written by the GEMM
+  const int32_t* rjob;    // job of each route
+  int R;                  // routes (jobs never outnumber them)
+  int tiles;              // N / 64
+  int steps;              // K / 256
 };
 
 struct RouteQuantArgs {
@@ -164,13 +163,14 @@ struct GemmArgs {
   int units0;           // work units of p[0]; 0 when there is none
   int pass_routes;      // MFMA path: routes staged per pass (<= 16)
   int stream_wgs;       // FP4 kernel: resident workgroups (stream_map)
+  int32_t* stream_counts;  // FP4 kernel: [J, tiles] partial slots of each tile, written here
   CombineFuse cf;       // K-in-workgroup GEMM2 only
   SwigluFuse sf;        // persistent GEMM1 only
 };
 
 // FP4 GEMM: a stream of (job, tile, step) items split evenly over the
 // workgroups; partial sums per tile go to part[slot] (stream_device.h).
-constexpr int kFp4JobRoutes = 2;  // routes of a job (one pass over an expert's weights)
+constexpr int kFp4JobRoutes = 4;  // routes of a job (one pass over an expert's weights): an MFMA block's columns
 size_t gemm_fp4_lds_bytes(int K);
 // workgroups that are resident at once on the current device (0 on error)
 int gemm_fp4_resident_wgs(int K);

@@ -322,7 +322,7 @@ int moe_decode_plan(moe_decode_t h, int32_t M, int32_t* out, int32_t n);
  * moe_decode_plan), and after a run slot 0 of stage 7 holds GEMM1's FP32
  * sums for the local routes; control word 2 is the job count J;
  * 17 job table int32[J][4] {local expert, first index into stage 4, route
- *    count (at most 2), 0}         18 job of each local route int32[M*k]
+ *    count (at most 4), 0}         18 job of each local route int32[M*k]
  * The size copied is min(bytes, size of the stage for the handle's maximum). */
 int moe_decode_debug_stage(moe_decode_t h, int32_t stage, void* dst, size_t bytes,
                            void* stream);

@@ -72,6 +72,10 @@ class MoeShape:
     weight_format: str = "fp8"
     local_begin: int = 0
     local_count: int = 0
+    # FP4 weight scale bytes: "mid" draws UE4M3 codes 0x30..0x3F (0.5 ..
+    # 1.875), "full" every finite code 0x00..0x7E (zero, the subnormals
+    # 2^-9 .. 7 * 2^-9 and the normals up to 448)
+    scale_codes: str = "mid"
 
     def with_(self, **kw) -> "MoeShape":
         return dataclasses.replace(self, **kw)
@@ -208,8 +212,9 @@ def _x_values_fp4(rng: np.random.Generator, shape: MoeShape) -> np.ndarray:
 def _make_inputs_fp4(shape: MoeShape, seed: int, device) -> MoeInputs:
     """FP4 workload: packed weights are uniform random bytes (each nibble an
     E2M1 code, low nibble first), scale bytes uniform over the UE4M3 codes
-    0x30..0x3F (0.5 .. 1.875), or over {0x30, 0x38, 0x40} (0.5, 1, 2) with
-    `pow2_scales`; local expert e draws from
+    0x30..0x3F (0.5 .. 1.875), over 0x00..0x7E with scale_codes="full", or
+    over {0x30, 0x38, 0x40} (0.5, 1, 2) with `pow2_scales`; local expert e
+    draws from
     torch.Generator(device).manual_seed(seed * 1000 + e)."""
     rng = np.random.default_rng(seed)
     M, H, I, E = shape.M, shape.hidden, shape.inter, shape.experts
@@ -231,7 +236,8 @@ def _make_inputs_fp4(shape: MoeShape, seed: int, device) -> MoeInputs:
     def scales(gen, shape_):
         if shape.pow2_scales:
             return pow2[torch.randint(0, 3, shape_, generator=gen, device=dev)]
-        return torch.randint(0x30, 0x40, shape_, generator=gen, device=dev).to(torch.uint8)
+        lo, hi = (0x00, 0x7F) if shape.scale_codes == "full" else (0x30, 0x40)
+        return torch.randint(lo, hi, shape_, generator=gen, device=dev).to(torch.uint8)
 
     for e in range(El):
         gen = torch.Generator(device=dev)

@@ -110,6 +110,31 @@ def check_fp4_layer(moe, inp, stages=True):
     return ref, (slots, ids, weights, combined)
 
 
+TINY_X_FACTORS = [1.0, 0.1, 0.03, 0.01, 0.004, 0.001]
+
+
+def test_fp4_full_scale_code_range():
+    """Weight scale bytes over every finite UE4M3 code (zero, subnormals
+    0x01..0x07, normals up to 0x7E = 448), and tokens whose activations are
+    small enough that their staged scales are subnormal or zero: the staging
+    bit-exact, GEMM1 within the FP32 bound, the rows within the bar
+    (nvfp4-megamoe-kernel README, "Data Formats": the scale is an e4m3 byte
+    read as its value)."""
+    shape = TINY.with_(M=6, hidden=768, inter=512, scale_codes="full")
+    inp = synth.make_inputs(shape, seed=37, device=DEV)
+    w = inp.w13_scale.cpu().numpy()
+    assert w.min() == 0 and w.max() == 0x7E and np.isin(np.arange(1, 8), w).all()
+    # tokens scaled down: their staged scales block_max / 6 fall from normal
+    # codes into the subnormal ones (below 2^-6) and, in the smallest, to zero
+    f = torch.tensor(TINY_X_FACTORS, device=DEV)[:, None]
+    inp.x = (inp.x.float() * f).to(torch.bfloat16)
+    moe = make_fp4(inp)
+    ref, _ = check_fp4_layer(moe, inp)
+    xs = ref["x_s"]
+    assert ((xs >= 1) & (xs <= 7)).any(), "no subnormal activation scales staged"
+    assert (xs >= 8).any() and (xs == 0).any()
+
+
 def test_fp4_tiny():
     inp = synth.make_inputs(TINY, seed=31, device=DEV)
     moe = make_fp4(inp)
@@ -117,12 +142,12 @@ def test_fp4_tiny():
     check_fp4_layer(moe, inp)
 
 
-JOB_ROUTES = 2  # routes of one job: one pass over an expert's weights
+JOB_ROUTES = 4  # routes of one job: one pass over an expert's weights (an MFMA block's columns)
 
 
 def check_jobs(moe, shape, ids):
     """The job table against the buckets and the routing ids: each touched
-    local expert's routes (ascending) cut into jobs of at most four, experts
+    local expert's routes (ascending) cut into jobs of at most JOB_ROUTES, experts
     ascending; every local route mapped to the job holding it."""
     M, k = shape.M, shape.top_k
     R = M * k
@@ -153,9 +178,9 @@ def check_jobs(moe, shape, ids):
 def test_fp4_jobs_one_wave():
     """At most 64 routes, so one wave groups them (ballot ranking): several
     jobs per expert, and routes outside the local range left out."""
-    shape = TINY.with_(M=12, hidden=512, inter=256, experts=10, top_k=4, local_begin=3, local_count=5)
+    shape = TINY.with_(M=32, hidden=512, inter=256, experts=10, top_k=2, local_begin=3, local_count=5)
     inp = synth.make_inputs(shape, seed=35, device=DEV)
-    inp.bias[[3, 5]] += 10.0  # experts 3 and 5 take every token: 12 routes, 6 jobs each
+    inp.bias[[3, 5]] += 10.0  # experts 3 and 5 take every token: 32 routes, 8 jobs each
     moe = make_fp4(inp)
     ref, _ = check_fp4_layer(moe, inp)
     check_jobs(moe, shape, ref["ids"])
@@ -181,10 +206,12 @@ def test_fp4_jobs_and_slots():
     check_jobs(moe, shape, ref["ids"])
 
 
-def test_fp4_more_jobs_than_workgroups():
-    """More jobs than resident workgroups (about 2200 against at most 1536):
-    every workgroup then takes at most one job's items."""
-    shape = TINY.with_(M=256, hidden=512, inter=256, experts=512, top_k=16, local_begin=0, local_count=512)
+def test_fp4_many_jobs():
+    """Many jobs (256 tokens, top-32 of 512 experts: about 2,100 jobs of up
+    to four routes, more than the resident workgroups), so every workgroup
+    takes at most one job's items; the grid holds at least one workgroup per
+    job."""
+    shape = TINY.with_(M=256, hidden=512, inter=256, experts=512, top_k=32, local_begin=0, local_count=512)
     inp = synth.make_inputs(shape, seed=36, device=DEV)
     moe = make_fp4(inp)
     plan = moe.plan(shape.M)
