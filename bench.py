@@ -43,7 +43,7 @@ GEMM1_TRAFFIC = [
                  "fp8_block_scaled_moe_amd/csrc/device_common.h",
                  "fp8_block_scaled_moe_amd/csrc/kernels.h",
                  "fp8_block_scaled_moe_amd/csrc/capi.hip"],  # the plan (K parts, grids)
-     "sources_sha256_16": "bd1d9f7c13c283d1",
+     "sources_sha256_16": "8f2f78da751a7466",
      "workload": "dsv3", "M": 4, "seed": 0, "unique_experts": 27,
      # medians per dispatch (KiB) and the copy kernel's reading of 256 MiB
      "fetch_kib": 387997.0, "write_kib": 512.0, "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0},
@@ -53,9 +53,9 @@ GEMM1_TRAFFIC = [
                  "fp8_block_scaled_moe_amd/csrc/device_common.h",
                  "fp8_block_scaled_moe_amd/csrc/kernels.h",
                  "fp8_block_scaled_moe_amd/csrc/capi.hip"],
-     "sources_sha256_16": "255f6392716bb5dc",
+     "sources_sha256_16": "4abf19cc6808adb0",
      "workload": "fp4_share", "M": 16, "seed": 0, "unique_experts": 4,
-     "fetch_kib": 56899.88, "write_kib": 560.0, "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0},
+     "fetch_kib": 50274.72, "write_kib": 604.38, "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0},
 ]
 
 
@@ -228,7 +228,8 @@ def run_one(args, shape, inp, moe, flush, per_kernel=True):
     wall = time.perf_counter() - t0
     layer_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
 
-    # pass 2: per-kernel times from events the library records between launches
+    # pass 2: per-kernel times; the library launches each kernel with HIP
+    # events that take its dispatch's own start and end (hipExtLaunchKernel)
     per = np.zeros((1, len(KERNELS)))
     if per_kernel:
         moe.set_timing(True)

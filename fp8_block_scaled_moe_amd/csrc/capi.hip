@@ -19,9 +19,9 @@ using namespace moe;
 
 namespace {
 
-constexpr int kEvents = 8;
 constexpr int kRegions = 21;
 constexpr int kStages = 5;  // timing slots: route, GEMM1, SwiGLU, GEMM2, combine
+constexpr int kEvents = 2 * kStages;  // start and stop of each timing slot
 constexpr int kTargetUnits = 4096;  // work units per GEMM launch to aim for (16 per CU)
 constexpr int kDenseTargetUnits = 256;  // units of the shared expert per GEMM launch
 constexpr int kWgTargetUnits = 4096;    // K-in-workgroup path: units to aim for (16 per CU)
@@ -95,9 +95,8 @@ struct moe_decode_handle {
   uint8_t* fp4_s2;
   bool timing;
   bool timed_run;
-  hipEvent_t ev[kEvents];
-  int ev_stage[kEvents];  // timing slot of the interval that ends at event i
-  int ev_count;           // events recorded by the last timed run
+  hipEvent_t ev[kEvents];  // slot i: ev[2i] and ev[2i + 1], filled by the slot's kernel
+  int ev_slots;            // bit i: slot i's kernel ran in the last timed run
 };
 
 namespace {
@@ -496,15 +495,16 @@ int run_layer(moe_decode_handle* h, int32_t M, const void* x, const void* logits
   uint8_t* sxq = h->shared_own_quant ? at(kSXq) : xq;
   float* sxs = h->shared_own_quant ? atf(kSXs) : xs;
 
-  int evn = 0;
-  // records an event closing timing slot `stage` (the first call opens)
-  auto mark = [&](int stage) -> hipError_t {
-    if (!h->timing) return hipSuccess;
-    h->ev_stage[evn] = stage;
-    return hipEventRecord(h->ev[evn++], s);
+  // timed runs: the kernel of timing slot `stage` fills that slot's events
+  // with its own start and end
+  int slots_run = 0;
+  auto events = [&](int stage) -> KernelEvents {
+    if (!h->timing) return {};
+    slots_run |= 1 << stage;
+    return KernelEvents{h->ev[2 * stage], h->ev[2 * stage + 1]};
   };
 
-  hipError_t e = mark(-1);
+  hipError_t e = hipSuccess;
 
   RouteQuantArgs ra;
   ra.logits = logits;
@@ -532,8 +532,7 @@ int run_layer(moe_decode_handle* h, int32_t M, const void* x, const void* logits
   ra.lb = lb;
   ra.lc = lc;
   ra.b = b;
-  if (e == hipSuccess) e = launch_route_quant(ra, s);
-  if (e == hipSuccess) e = mark(0);
+  if (e == hipSuccess) e = launch_route_quant(ra, s, events(0));
 
   SwigluArgs sa;
   sa.part = p1;
@@ -601,12 +600,13 @@ int run_layer(moe_decode_handle* h, int32_t M, const void* x, const void* logits
   };
   auto launch_gemm = [&](const GemmArgs& g, int role, int grid) {
     const int persist = role == 1 ? p.persist1 : p.persist2;
+    const KernelEvents ev = events(role == 1 ? 1 : 3);
     switch (p.path) {
-      case MOE_GEMM_FP4: return launch_gemm_fp4(g, role, grid, s);
+      case MOE_GEMM_FP4: return launch_gemm_fp4(g, role, grid, s, ev);
       case MOE_GEMM_MFMA:
-        return persist ? launch_gemm_wgp(g, role, persist, s) : launch_gemm_wg(g, role, grid, s);
-      case MOE_GEMM_MFMA_SPLITK: return launch_gemm_mfma(g, role, grid, s);
-      default: return launch_gemm_valu(g, role, grid, s);
+        return persist ? launch_gemm_wgp(g, role, persist, s, ev) : launch_gemm_wg(g, role, grid, s, ev);
+      case MOE_GEMM_MFMA_SPLITK: return launch_gemm_mfma(g, role, grid, s, ev);
+      default: return launch_gemm_valu(g, role, grid, s, ev);
     }
   };
 
@@ -636,12 +636,8 @@ int run_layer(moe_decode_handle* h, int32_t M, const void* x, const void* logits
     f.hs = hs;
   }
   if (e == hipSuccess) e = launch_gemm(g1, 1, p.grid1 - (shared ? 0 : p.sunits1));
-  if (e == hipSuccess) e = mark(1);
 
-  if (!p.fuse_swiglu) {
-    if (e == hipSuccess) e = launch_swiglu_requant(sa, s);
-    if (e == hipSuccess) e = mark(2);
-  }
+  if (!p.fuse_swiglu && e == hipSuccess) e = launch_swiglu_requant(sa, s, events(2));
 
   GemmArgs g2{};
   g2.p[1] = problem(c.w2, c.w2_scale, hq, hs, p2, c.hidden, c.inter, p.s2, p.ks2, R, 1, p.tpw2);
@@ -675,15 +671,11 @@ int run_layer(moe_decode_handle* h, int32_t M, const void* x, const void* logits
     f.all_local = lb == 0 && lc == c.experts;
   }
   if (e == hipSuccess) e = launch_gemm(g2, 2, p.grid2 - (shared ? 0 : p.sunits2));
-  if (e == hipSuccess) e = mark(3);
 
-  if (!p.fuse_combine) {
-    if (e == hipSuccess) e = launch_combine(ca, s);
-    if (e == hipSuccess) e = mark(4);
-  }
+  if (!p.fuse_combine && e == hipSuccess) e = launch_combine(ca, s, events(4));
 
   h->timed_run = h->timing;
-  h->ev_count = evn;
+  h->ev_slots = slots_run;
   return e == hipSuccess ? MOE_DECODE_OK : MOE_DECODE_ERR_HIP;
 }
 
@@ -926,13 +918,11 @@ int moe_decode_set_timing(moe_decode_t h, int32_t enable) {
 int moe_decode_last_timing(moe_decode_t h, float* ms, int32_t n) {
   if (!h || !ms || n < kStages) return MOE_DECODE_ERR_INVALID_ARG;
   for (int i = 0; i < kStages; ++i) ms[i] = 0.f;
-  if (!h->timed_run || h->ev_count < 2) return MOE_DECODE_ERR_INVALID_ARG;
-  const int last = h->ev_count - 1;
-  if (hipEventSynchronize(h->ev[last]) != hipSuccess) return MOE_DECODE_ERR_HIP;
-  for (int i = 1; i <= last; ++i) {
-    float t = 0.f;
-    if (hipEventElapsedTime(&t, h->ev[i - 1], h->ev[i]) != hipSuccess) return MOE_DECODE_ERR_HIP;
-    ms[h->ev_stage[i]] += t;
+  if (!h->timed_run || h->ev_slots == 0) return MOE_DECODE_ERR_INVALID_ARG;
+  for (int i = 0; i < kStages; ++i) {
+    if (!(h->ev_slots & (1 << i))) continue;
+    if (hipEventSynchronize(h->ev[2 * i + 1]) != hipSuccess) return MOE_DECODE_ERR_HIP;
+    if (hipEventElapsedTime(&ms[i], h->ev[2 * i], h->ev[2 * i + 1]) != hipSuccess) return MOE_DECODE_ERR_HIP;
   }
   return MOE_DECODE_OK;
 }

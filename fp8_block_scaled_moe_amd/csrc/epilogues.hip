@@ -73,10 +73,11 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
 
 }  // namespace
 
-hipError_t launch_swiglu_requant(const SwigluArgs& a, hipStream_t s) {
+hipError_t launch_swiglu_requant(const SwigluArgs& a, hipStream_t s, KernelEvents ev) {
   const int waves = a.R * (a.I / kTile) + (a.spart ? a.M * (a.Is / kTile) : 0);
   const int wpg = kThreads / kWave;
-  hipLaunchKernelGGL(swiglu_requant_kernel, dim3((waves + wpg - 1) / wpg), dim3(kThreads), 0, s, a);
+  hipExtLaunchKernelGGL(swiglu_requant_kernel, dim3((waves + wpg - 1) / wpg), dim3(kThreads), 0, s,
+                        ev.start, ev.stop, 0, a);
   return hipGetLastError();
 }
 
@@ -87,8 +88,9 @@ hipError_t launch_zero_words(int32_t* p, size_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel, dim3(a.M * (a.H / 64)), dim3(kThreads), 0, s, a);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s, KernelEvents ev) {
+  hipExtLaunchKernelGGL(combine_kernel, dim3(a.M * (a.H / 64)), dim3(kThreads), 0, s,
+                        ev.start, ev.stop, 0, a);
   return hipGetLastError();
 }
 

@@ -379,21 +379,21 @@ size_t gemm_mfma_lds_bytes(int pass_routes, int ks) {
          (size_t)(kMfmaRoutes + kMaxTpw) * kMaxKs * 4 + kMfmaRoutes * 4;
 }
 
-hipError_t launch_gemm_valu(const GemmArgs& a, int role, int grid, hipStream_t s) {
+hipError_t launch_gemm_valu(const GemmArgs& a, int role, int grid, hipStream_t s, KernelEvents ev) {
   if (role == 1)
-    hipLaunchKernelGGL(gemm_valu_kernel<1>, dim3(grid), dim3(kThreads), 0, s, a);
+    hipExtLaunchKernelGGL(gemm_valu_kernel<1>, dim3(grid), dim3(kThreads), 0, s, ev.start, ev.stop, 0, a);
   else
-    hipLaunchKernelGGL(gemm_valu_kernel<2>, dim3(grid), dim3(kThreads), 0, s, a);
+    hipExtLaunchKernelGGL(gemm_valu_kernel<2>, dim3(grid), dim3(kThreads), 0, s, ev.start, ev.stop, 0, a);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_mfma(const GemmArgs& a, int role, int grid, hipStream_t s) {
+hipError_t launch_gemm_mfma(const GemmArgs& a, int role, int grid, hipStream_t s, KernelEvents ev) {
   const int ks = a.units0 ? std::max(a.p[0].ks, a.p[1].ks) : a.p[1].ks;
   const size_t lds = gemm_mfma_lds_bytes(a.pass_routes, ks);
   if (role == 1)
-    hipLaunchKernelGGL(gemm_mfma_kernel<1>, dim3(grid), dim3(kThreads), lds, s, a);
+    hipExtLaunchKernelGGL(gemm_mfma_kernel<1>, dim3(grid), dim3(kThreads), lds, s, ev.start, ev.stop, 0, a);
   else
-    hipLaunchKernelGGL(gemm_mfma_kernel<2>, dim3(grid), dim3(kThreads), lds, s, a);
+    hipExtLaunchKernelGGL(gemm_mfma_kernel<2>, dim3(grid), dim3(kThreads), lds, s, ev.start, ev.stop, 0, a);
   return hipGetLastError();
 }
 

@@ -307,11 +307,11 @@ int gemm_fp4_resident_wgs(int) {
   return cus * per_cu;
 }
 
-hipError_t launch_gemm_fp4(const GemmArgs& a, int role, int grid, hipStream_t s) {
+hipError_t launch_gemm_fp4(const GemmArgs& a, int role, int grid, hipStream_t s, KernelEvents ev) {
   if (role == 1)
-    hipLaunchKernelGGL(gemm_fp4_kernel<1>, dim3(grid), dim3(kThreads), 0, s, a);
+    hipExtLaunchKernelGGL(gemm_fp4_kernel<1>, dim3(grid), dim3(kThreads), 0, s, ev.start, ev.stop, 0, a);
   else
-    hipLaunchKernelGGL(gemm_fp4_kernel<2>, dim3(grid), dim3(kThreads), 0, s, a);
+    hipExtLaunchKernelGGL(gemm_fp4_kernel<2>, dim3(grid), dim3(kThreads), 0, s, ev.start, ev.stop, 0, a);
   return hipGetLastError();
 }
 

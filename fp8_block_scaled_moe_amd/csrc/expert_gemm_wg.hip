@@ -585,7 +585,7 @@ int gemm_wgp_resident_wgs(int nkb) {
   return cus * per_cu;
 }
 
-hipError_t launch_gemm_wgp(const GemmArgs& a, int role, int grid, hipStream_t s) {
+hipError_t launch_gemm_wgp(const GemmArgs& a, int role, int grid, hipStream_t s, KernelEvents ev) {
   const GemmProblem& p = a.p[1];
   if (a.units0 || a.cf.on || grid < 1 || !gemm_wgp_fits(p.nkb, p.kparts))
     return hipErrorInvalidValue;
@@ -593,16 +593,19 @@ hipError_t launch_gemm_wgp(const GemmArgs& a, int role, int grid, hipStream_t s)
   if (a.sf.on) {
     // the unit's rows must lie in one 128-column block of up or of gate
     if (role != 1 || p.N != 2 * a.sf.I || kTile % (kRowsPerWg / p.kparts) != 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_wgp_kernel<1, true>), dim3(grid), dim3(kThreads), lds, s, a);
+    hipExtLaunchKernelGGL((gemm_wgp_kernel<1, true>), dim3(grid), dim3(kThreads), lds, s,
+                          ev.start, ev.stop, 0, a);
   } else if (role == 1) {
-    hipLaunchKernelGGL((gemm_wgp_kernel<1, false>), dim3(grid), dim3(kThreads), lds, s, a);
+    hipExtLaunchKernelGGL((gemm_wgp_kernel<1, false>), dim3(grid), dim3(kThreads), lds, s,
+                          ev.start, ev.stop, 0, a);
   } else {
-    hipLaunchKernelGGL((gemm_wgp_kernel<2, false>), dim3(grid), dim3(kThreads), lds, s, a);
+    hipExtLaunchKernelGGL((gemm_wgp_kernel<2, false>), dim3(grid), dim3(kThreads), lds, s,
+                          ev.start, ev.stop, 0, a);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_wg(const GemmArgs& a, int role, int grid, hipStream_t s) {
+hipError_t launch_gemm_wg(const GemmArgs& a, int role, int grid, hipStream_t s, KernelEvents ev) {
   const int nkb = a.units0 ? std::max(a.p[0].nkb, a.p[1].nkb) : a.p[1].nkb;
   const size_t lds = gemm_wg_lds_bytes(nkb);
   if (a.cf.on) {
@@ -610,11 +613,14 @@ hipError_t launch_gemm_wg(const GemmArgs& a, int role, int grid, hipStream_t s) 
     // and the reduction buffer; output rows are H wide
     if (role != 2 || a.cf.k > kMaxTopK || a.cf.M > kRedFloats || (a.units0 && a.p[0].N != a.p[1].N))
       return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_wg_kernel<2, true>), dim3(grid), dim3(kThreads), lds, s, a);
+    hipExtLaunchKernelGGL((gemm_wg_kernel<2, true>), dim3(grid), dim3(kThreads), lds, s,
+                          ev.start, ev.stop, 0, a);
   } else if (role == 1) {
-    hipLaunchKernelGGL((gemm_wg_kernel<1, false>), dim3(grid), dim3(kThreads), lds, s, a);
+    hipExtLaunchKernelGGL((gemm_wg_kernel<1, false>), dim3(grid), dim3(kThreads), lds, s,
+                          ev.start, ev.stop, 0, a);
   } else {
-    hipLaunchKernelGGL((gemm_wg_kernel<2, false>), dim3(grid), dim3(kThreads), lds, s, a);
+    hipExtLaunchKernelGGL((gemm_wg_kernel<2, false>), dim3(grid), dim3(kThreads), lds, s,
+                          ev.start, ev.stop, 0, a);
   }
   return hipGetLastError();
 }

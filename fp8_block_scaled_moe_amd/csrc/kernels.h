@@ -2,6 +2,7 @@
 // own translation unit and is launched through the function declared here.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -9,6 +10,14 @@ namespace moe {
 
 constexpr int kTile = 128;  // block size of every FP8 scale (K and N)
 constexpr int kMaxTopK = 32;
+
+// Events that a launch fills with its kernel's own start and end: the
+// timestamps of the kernel's dispatch (hipExtLaunchKernel), not of markers
+// queued beside it. Both null: an untimed launch.
+struct KernelEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
 
 // Distinct-expert buckets built by the routing kernel (device memory).
 struct Buckets {
@@ -174,7 +183,7 @@ constexpr int kFp4JobRoutes = 4;  // routes of a job (one pass over an expert's 
 size_t gemm_fp4_lds_bytes(int K);
 // workgroups that are resident at once on the current device (0 on error)
 int gemm_fp4_resident_wgs(int K);
-hipError_t launch_gemm_fp4(const GemmArgs& a, int role, int grid, hipStream_t s);
+hipError_t launch_gemm_fp4(const GemmArgs& a, int role, int grid, hipStream_t s, KernelEvents ev = {});
 // Weight scales [rows, K/16] UE4M3 (rows a multiple of 16) into the FP4
 // GEMM's layout: per 16-row group and 256-value step, 64 lanes x 4 bytes
 // (dst holds as many bytes as src).
@@ -195,20 +204,20 @@ constexpr size_t kMaxRouteLds = 64 * 1024;
 constexpr size_t kMaxWgLds = 64 * 1024;
 
 size_t route_quant_lds_bytes(int E, int words, int routes);
-hipError_t launch_route_quant(const RouteQuantArgs& a, hipStream_t s);
+hipError_t launch_route_quant(const RouteQuantArgs& a, hipStream_t s, KernelEvents ev = {});
 // role: 1 = GEMM1 (W13), 2 = GEMM2 (W2); it only selects the kernel symbol.
-hipError_t launch_gemm_valu(const GemmArgs& a, int role, int grid, hipStream_t s);
-hipError_t launch_gemm_mfma(const GemmArgs& a, int role, int grid, hipStream_t s);
+hipError_t launch_gemm_valu(const GemmArgs& a, int role, int grid, hipStream_t s, KernelEvents ev = {});
+hipError_t launch_gemm_mfma(const GemmArgs& a, int role, int grid, hipStream_t s, KernelEvents ev = {});
 size_t gemm_mfma_lds_bytes(int pass_routes, int ks);
 // The kernel with the whole K sum inside a workgroup (no split-K partials):
 // writes one FP32 value per (route, row) to part[0].
-hipError_t launch_gemm_wg(const GemmArgs& a, int role, int grid, hipStream_t s);
+hipError_t launch_gemm_wg(const GemmArgs& a, int role, int grid, hipStream_t s, KernelEvents ev = {});
 size_t gemm_wg_lds_bytes(int nkb);
 // Its persistent form (routed problem only; its units are the routing
 // kernel's jobs of at most kMfmaRoutes routes x rows): `grid` workgroups take
 // the units in turn. gemm_wgp_fits: nkb K blocks and kparts K parts are
 // within its conditions; resident_wgs is 0 on error.
-hipError_t launch_gemm_wgp(const GemmArgs& a, int role, int grid, hipStream_t s);
+hipError_t launch_gemm_wgp(const GemmArgs& a, int role, int grid, hipStream_t s, KernelEvents ev = {});
 size_t gemm_wgp_lds_bytes(int nkb);
 bool gemm_wgp_fits(int nkb, int kparts);
 int gemm_wgp_resident_wgs(int nkb);
@@ -216,10 +225,10 @@ int gemm_wgp_resident_wgs(int nkb);
 // *bad is set nonzero when the rows of a 128-row block disagree.
 hipError_t launch_unpack_ue8m0(const int32_t* packed, int n, int k, float* out, int32_t* bad,
                                hipStream_t s);
-hipError_t launch_swiglu_requant(const SwigluArgs& a, hipStream_t s);
+hipError_t launch_swiglu_requant(const SwigluArgs& a, hipStream_t s, KernelEvents ev = {});
 // Zeroes n int32 words at p with a kernel (no memset node under graph capture).
 hipError_t launch_zero_words(int32_t* p, size_t n, hipStream_t s);
-hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s, KernelEvents ev = {});
 hipError_t launch_codec_check(const float* in, uint8_t* q, float* dq, int n, hipStream_t s);
 
 }  // namespace moe

@@ -458,10 +458,10 @@ size_t route_quant_lds_bytes(int E, int words, int routes) {
   return (size_t)E * words * 8 + (size_t)routes * 4 + (size_t)E * 8 + 3 * kWaves * 4;
 }
 
-hipError_t launch_route_quant(const RouteQuantArgs& a, hipStream_t s) {
+hipError_t launch_route_quant(const RouteQuantArgs& a, hipStream_t s, KernelEvents ev) {
   const int grid = routing_wgs(a.M) + quant_wgs(a.M, a.H);
-  hipLaunchKernelGGL(route_quant_kernel, dim3(grid), dim3(kThreads),
-                     route_quant_lds_bytes(a.E, a.words, a.M * a.k), s, a);
+  hipExtLaunchKernelGGL(route_quant_kernel, dim3(grid), dim3(kThreads),
+                        route_quant_lds_bytes(a.E, a.words, a.M * a.k), s, ev.start, ev.stop, 0, a);
   return hipGetLastError();
 }
 

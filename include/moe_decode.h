@@ -328,13 +328,15 @@ int moe_decode_debug_stage(moe_decode_t h, int32_t stage, void* dst, size_t byte
                            void* stream);
 
 /* Benchmark support (no passage: it times this library's own launches).
- * Per-kernel timing of subsequent runs with HIP events recorded between the
- * launches (enable != 0; not for use under graph capture). After a run has
- * completed, moe_decode_last_timing writes the milliseconds of each launch in
- * order: route+quant, GEMM1, SwiGLU+requant, GEMM2, combine (the shared
- * expert, when run, is part of the last four; when the combine or the
- * SwiGLU runs inside a GEMM launch, its time is that GEMM's and its own
- * entry is 0). n is the capacity of ms (>= 5). */
+ * Per-kernel timing of subsequent runs (enable != 0; not for use under graph
+ * capture): each kernel of the layer is launched with a pair of HIP events
+ * that take its dispatch's own start and end timestamps (hipExtLaunchKernel),
+ * so the time excludes the gaps between launches. After a run has completed,
+ * moe_decode_last_timing writes the milliseconds of each kernel in order:
+ * route+quant, GEMM1, SwiGLU+requant, GEMM2, combine (the shared expert, when
+ * run, is part of the last four; when the combine or the SwiGLU runs inside a
+ * GEMM launch, its time is that GEMM's and its own entry is 0). n is the
+ * capacity of ms (>= 5). */
 int moe_decode_set_timing(moe_decode_t h, int32_t enable);
 int moe_decode_last_timing(moe_decode_t h, float* ms, int32_t n);
 

@@ -80,3 +80,49 @@ def test_handles_on_separate_streams(cases):
     torch.cuda.synchronize()
     for n, got in enumerate(outs):
         check(got, cases[n % len(cases)][2])
+
+
+def test_timed_runs_change_nothing_and_time_each_kernel(cases):
+    """Per-kernel timing (moe_decode_set_timing): outputs stay bit-identical,
+    every launched kernel has a positive time, a slot whose work ran inside a
+    GEMM launch reads 0, and the kernels' times add up to less than the
+    layer's (the events take each dispatch's own timestamps)."""
+    for inp, moe, ref in cases:
+        layer = []
+        for mode_timing in (False, True):
+            moe.set_timing(mode_timing)
+            for _ in range(3):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                got = moe(inp.x, inp.logits, inp.bias)
+                b.record()
+                torch.cuda.synchronize()
+                check(got, ref)
+                if mode_timing:
+                    ms = moe.last_timing()
+                    assert all(t > 0 for t in (ms[0], ms[1], ms[3])), ms
+                    assert all(t >= 0 for t in ms), ms
+                    layer.append((sum(ms), a.elapsed_time(b)))
+        moe.set_timing(False)
+        # the events around the call add their own markers, so the layer's
+        # span bounds the kernels' sum
+        assert all(s < span for s, span in layer), layer
+
+
+def test_timing_of_fused_launches():
+    """With the SwiGLU inside GEMM1 and the combine inside GEMM2, their slots
+    read 0 and the GEMM slots carry the time."""
+    inp = synth.make_inputs(SHAPES[0], seed=77, device=DEV)
+    for mode, zero in (("swiglu_in_gemm1", 2), ("combine_in_gemm2", 4)):
+        s = inp.shape
+        moe = MoeDecode(inp.w13, inp.w13_scale, inp.w2, inp.w2_scale, top_k=s.top_k, limit=s.limit,
+                        routed_scale=s.routed_scale, max_tokens=s.M, logits_dtype=inp.logits.dtype,
+                        ue8m0_act=s.ue8m0_act, launch_mode=mode)
+        ref = [t.clone() for t in moe(inp.x, inp.logits, inp.bias)]
+        moe.set_timing(True)
+        got = moe(inp.x, inp.logits, inp.bias)
+        torch.cuda.synchronize()
+        ms = moe.last_timing()
+        check(got, ref)
+        assert ms[zero] == 0 and ms[1] > 0 and ms[3] > 0, (mode, ms)
+        moe.close()
