@@ -43,7 +43,7 @@ GEMM1_TRAFFIC = [
                  "fp8_block_scaled_moe_amd/csrc/device_common.h",
                  "fp8_block_scaled_moe_amd/csrc/kernels.h",
                  "fp8_block_scaled_moe_amd/csrc/capi.hip"],  # the plan (K parts, grids)
-     "sources_sha256_16": "8f2f78da751a7466",
+     "sources_sha256_16": "66f48116f1eac6a0",
      "workload": "dsv3", "M": 4, "seed": 0, "unique_experts": 27,
      # medians per dispatch (KiB) and the copy kernel's reading of 256 MiB
      "fetch_kib": 387997.0, "write_kib": 512.0, "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0},
@@ -53,9 +53,9 @@ GEMM1_TRAFFIC = [
                  "fp8_block_scaled_moe_amd/csrc/device_common.h",
                  "fp8_block_scaled_moe_amd/csrc/kernels.h",
                  "fp8_block_scaled_moe_amd/csrc/capi.hip"],
-     "sources_sha256_16": "4abf19cc6808adb0",
+     "sources_sha256_16": "fcb1822eb6ecc4c7",
      "workload": "fp4_share", "M": 16, "seed": 0, "unique_experts": 4,
-     "fetch_kib": 50274.72, "write_kib": 604.38, "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0},
+     "fetch_kib": 50334.72, "write_kib": 604.42, "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0},
 ]
 
 
@@ -96,7 +96,7 @@ def parse():
     p.add_argument("--splits1", type=int, default=0)
     p.add_argument("--splits2", type=int, default=0)
     p.add_argument("--launch-mode", default="auto",
-                   choices=["auto", "separate", "combine_in_gemm2", "swiglu_in_gemm1"])
+                   choices=["auto", "separate", "combine_in_gemm2", "swiglu_in_gemm1", "route_in_gemm1"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--sweep", default="", help="comma-separated M values: one JSON line each")
     p.add_argument("--no-sweep", action="store_true",

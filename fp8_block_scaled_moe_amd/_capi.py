@@ -32,7 +32,7 @@ SCALES_F32 = 0
 SCALES_UE8M0_PACKED = 1
 WEIGHT_FORMATS = {"fp8": 0, "nvfp4": 1}
 GEMM_PATHS = {"auto": 0, "valu_splitk": 1, "mfma_splitk": 2, "mfma": 3, "fp4": 4}
-LAUNCH_MODES = {"auto": 0, "separate": 1, "combine_in_gemm2": 2, "swiglu_in_gemm1": 3}
+LAUNCH_MODES = {"auto": 0, "separate": 1, "combine_in_gemm2": 2, "swiglu_in_gemm1": 3, "route_in_gemm1": 4}
 
 STAGES = {
     "ctrl": 0, "uexp": 1, "uoff": 2, "ucnt": 3, "routes": 4, "x_q": 5, "x_s": 6,

@@ -35,6 +35,7 @@ constexpr int kStageSharedScale13 = 19, kStageSharedScale2 = 20;
 // 311.3, M=16 441.2 -> 446.4 (units no longer divide evenly over the
 // resident workgroups, and a static share cannot even them out).
 constexpr int kPersistMaxTokens = 8;
+constexpr int kMfmaRouteFuseRoutes = 64;  // routes one wave groups in the GEMM1 routing prologue
 // Beyond that, a GEMM whose K is at most this many 128-blocks still runs
 // persistent: its units are short next to the per-unit staging. Measured on
 // the latent shape (H=3584, I=1024, E=896, top-16, M=64), GEMM2 (8 blocks)
@@ -67,6 +68,7 @@ struct Plan {
   // K-in-workgroup path: resident workgroups of the persistent GEMM1 / GEMM2
   // launches (0: one workgroup per unit)
   int persist1, persist2;
+  bool route1;  // routing and the x quantisation run inside the persistent GEMM1 launch
 };
 
 struct Region {
@@ -90,6 +92,7 @@ struct moe_decode_handle {
   const float* s2;
   int fp4_wgs1, fp4_wgs2;  // FP4 form: resident workgroups of each GEMM launch
   int wgp_wgs1, wgp_wgs2;  // FP8 form: resident workgroups of the persistent GEMM kernels
+  int wgp_route_wgs1;      // and of the persistent GEMM1 with routing inside
   // FP4 form: the weight scales reordered for the GEMM kernel (owned)
   uint8_t* fp4_s13;
   uint8_t* fp4_s2;
@@ -163,7 +166,7 @@ int local_count(const moe_decode_config& c) { return c.local_experts ? c.local_e
 // fp4_wgs1/2: the FP4 GEMM launches' resident workgroups, wgp_wgs1/2 those of
 // the persistent FP8 GEMMs (0 while only sizing the workspace).
 Plan make_plan(const moe_decode_config& c, int M, int fp4_wgs1 = 0, int fp4_wgs2 = 0, int wgp_wgs1 = 0,
-               int wgp_wgs2 = 0) {
+               int wgp_wgs2 = 0, int wgp_route_wgs1 = 0) {
   Plan p{};
   const int R = M * c.top_k;
   p.umax = std::min(local_count(c), R);
@@ -231,6 +234,19 @@ Plan make_plan(const moe_decode_config& c, int M, int fp4_wgs1 = 0, int fp4_wgs2
         }
         p.persist1 = std::min(p.grid1, wgp_wgs1);
         p.fuse_swiglu = c.launch_mode == MOE_LAUNCH_SWIGLU_IN_GEMM1;
+        // Routing inside the GEMM1 launch: every workgroup routes the few
+        // tokens itself (the "mega_moe" page's per-warp routing, here per
+        // workgroup) and one wave groups the routes. The workgroups' first
+        // weight request waits for that prologue (5.3 us at one token, 9.0
+        // at two, against about 0.5 us after a routing launch); measured on
+        // MI355X at DeepSeek-V3 shapes, the layer took 73.3 against 78.0 us
+        // at one token and 128.2 against 129.0 at two, so MOE_LAUNCH_AUTO
+        // takes it at one token.
+        const bool want_route = c.launch_mode == MOE_LAUNCH_ROUTE_IN_GEMM1 ||
+                                (c.launch_mode == MOE_LAUNCH_AUTO && M == 1);
+        p.route1 = want_route && M <= kRouteFuseMaxTokens && M * c.top_k <= kMfmaRouteFuseRoutes &&
+                   wgp_route_wgs1 > 0 && gemm_wgp_route_fits(nkb1, c.experts);
+        if (p.route1) p.persist1 = std::min(p.grid1, wgp_route_wgs1);
       }
       if (wgp_wgs2 > 0 && !p.fuse_combine && (few || nkb2 <= kPersistShortBlocks) && gemm_wgp_fits(nkb2, p.kp2))
         p.persist2 = std::min(p.grid2, wgp_wgs2);
@@ -299,7 +315,7 @@ int validate_config(const moe_decode_config* c) {
   if (gemm_wg_lds_bytes(std::max(c->hidden, std::max(c->inter, c->shared_inter)) / kTile) > kMaxWgLds)
     return MOE_DECODE_ERR_UNSUPPORTED;
   if (c->splits1 < 0 || c->splits2 < 0) return MOE_DECODE_ERR_INVALID_ARG;
-  if (c->launch_mode < MOE_LAUNCH_AUTO || c->launch_mode > MOE_LAUNCH_SWIGLU_IN_GEMM1)
+  if (c->launch_mode < MOE_LAUNCH_AUTO || c->launch_mode > MOE_LAUNCH_ROUTE_IN_GEMM1)
     return MOE_DECODE_ERR_UNSUPPORTED;
   {
     const int words = (c->max_tokens + 63) / 64;
@@ -420,6 +436,8 @@ struct DeviceScratch {
   // resident workgroups of the persistent FP8 GEMM for K / 128 = i, plus one
   // (0: not yet asked)
   std::atomic<int> wgp[kMaxCachedBlocks + 1] = {};
+  // the same for the persistent GEMM1 with routing inside, [E > 256][K / 128]
+  std::atomic<int> wgp_route[2][kMaxCachedBlocks + 1] = {};
 };
 DeviceScratch g_dev[kMaxDevices];
 
@@ -449,6 +467,17 @@ int cached_wgp_wgs(int dev, int nkb) {
   return v - 1;
 }
 
+int cached_wgp_route_wgs(int dev, int nkb, int E) {
+  if (nkb > kMaxCachedBlocks) return gemm_wgp_route_resident_wgs(nkb, E);
+  std::atomic<int>& slot = g_dev[dev].wgp_route[E > 256][nkb];  // the kernel for E <= 256 or for more
+  int v = slot.load(std::memory_order_relaxed);
+  if (v == 0) {
+    v = gemm_wgp_route_resident_wgs(nkb, E) + 1;
+    slot.store(v, std::memory_order_relaxed);
+  }
+  return v - 1;
+}
+
 // Pointer checks of a run (M >= 1): INVALID_ARG for a NULL or misaligned
 // buffer, or a shared_out without a shared expert.
 int check_run_pointers(const moe_decode_config& c, const void* x, const void* logits, const float* bias,
@@ -470,7 +499,7 @@ int run_layer(moe_decode_handle* h, int32_t M, const void* x, const void* logits
   const bool shared = shared_out != nullptr;
 
   const moe_decode_config& c = h->cfg;
-  const Plan p = make_plan(c, M, h->fp4_wgs1, h->fp4_wgs2, h->wgp_wgs1, h->wgp_wgs2);
+  const Plan p = make_plan(c, M, h->fp4_wgs1, h->fp4_wgs2, h->wgp_wgs1, h->wgp_wgs2, h->wgp_route_wgs1);
   const int R = M * c.top_k;
   const bool fp4 = c.weight_format == MOE_WEIGHTS_NVFP4;
   const int lb = c.local_begin, lc = local_count(c);
@@ -532,7 +561,7 @@ int run_layer(moe_decode_handle* h, int32_t M, const void* x, const void* logits
   ra.lb = lb;
   ra.lc = lc;
   ra.b = b;
-  if (e == hipSuccess) e = launch_route_quant(ra, s, events(0));
+  if (!p.route1 && e == hipSuccess) e = launch_route_quant(ra, s, events(0));
 
   SwigluArgs sa;
   sa.part = p1;
@@ -625,6 +654,25 @@ int run_layer(moe_decode_handle* h, int32_t M, const void* x, const void* logits
     g1.p[0].dense = M;
     g1.p[0].kparts = p.skp1;
     g1.units0 = p.sunits1;
+  }
+  if (p.route1) {
+    RouteFuse& f = g1.rf;
+    f.on = 1;
+    f.logits = logits;
+    f.logits_bf16 = ra.logits_bf16;
+    f.bias = bias;
+    f.x = ra.x;
+    f.M = M;
+    f.E = c.experts;
+    f.k = c.top_k;
+    f.routed_scale = c.routed_scale;
+    f.ue8m0 = c.ue8m0_act;
+    f.lb = lb;
+    f.lc = lc;
+    f.ids = ids;
+    f.weights = weights;
+    f.xq = xq;
+    f.xs = xs;
   }
   if (p.fuse_swiglu) {
     SwigluFuse& f = g1.sf;
@@ -736,6 +784,8 @@ int moe_decode_create(const moe_decode_config* cfg, moe_decode_t* out) {
   if (!fp4) {  // 0 (one workgroup per unit) if the query fails
     h->wgp_wgs1 = gemm_wgp_resident_wgs(c.hidden / kTile);
     h->wgp_wgs2 = gemm_wgp_resident_wgs(c.inter / kTile);
+    if (gemm_wgp_route_fits(c.hidden / kTile, c.experts))
+      h->wgp_route_wgs1 = gemm_wgp_route_resident_wgs(c.hidden / kTile, c.experts);
   }
   if (fp4) {
     h->fp4_wgs1 = gemm_fp4_resident_wgs(c.hidden);
@@ -769,7 +819,8 @@ int moe_decode_create(const moe_decode_config* cfg, moe_decode_t* out) {
     }
   }
   if (std::getenv("MOE_DECODE_DEBUG")) {
-    const Plan p = make_plan(c, c.max_tokens, h->fp4_wgs1, h->fp4_wgs2, h->wgp_wgs1, h->wgp_wgs2);
+    const Plan p = make_plan(c, c.max_tokens, h->fp4_wgs1, h->fp4_wgs2, h->wgp_wgs1, h->wgp_wgs2,
+                             h->wgp_route_wgs1);
     std::fprintf(stderr,
                  "moe_decode: H=%d I=%d E=%d k=%d max_tokens=%d workspace=%zu B; at M=%d: "
                  "path=%d splits1=%d (ks %d) splits2=%d (ks %d) grid1=%d grid2=%d\n",
@@ -799,7 +850,7 @@ void moe_decode_destroy(moe_decode_t h) {
 int moe_decode_plan(moe_decode_t h, int32_t M, int32_t* out, int32_t n) {
   if (!h || !out || n < 9 || M < 1) return MOE_DECODE_ERR_INVALID_ARG;
   if (M > h->cfg.max_tokens) return MOE_DECODE_ERR_TOO_MANY_TOKENS;
-  const Plan p = make_plan(h->cfg, M, h->fp4_wgs1, h->fp4_wgs2, h->wgp_wgs1, h->wgp_wgs2);
+  const Plan p = make_plan(h->cfg, M, h->fp4_wgs1, h->fp4_wgs2, h->wgp_wgs1, h->wgp_wgs2, h->wgp_route_wgs1);
   out[0] = p.path;
   out[1] = p.s1;
   out[2] = p.s2;
@@ -822,7 +873,7 @@ int moe_decode_plan(moe_decode_t h, int32_t M, int32_t* out, int32_t n) {
     out[15] = p.path == MOE_GEMM_MFMA ? p.kp1 : 1;
     out[16] = p.path == MOE_GEMM_MFMA ? p.kp2 : 1;
   }
-  if (n >= 18) out[17] = 5 - (p.fuse_combine ? 1 : 0) - (p.fuse_swiglu ? 1 : 0);
+  if (n >= 18) out[17] = 5 - (p.fuse_combine ? 1 : 0) - (p.fuse_swiglu ? 1 : 0) - (p.route1 ? 1 : 0);
   if (n >= 20) {
     out[18] = p.persist1;
     out[19] = p.persist2;
@@ -871,10 +922,12 @@ int moe_decode_run_noalloc(const moe_decode_config* cfg, int32_t M, const void* 
   h.s2 = static_cast<const float*>(c.sw2_scale);
   h.wgp_wgs1 = cached_wgp_wgs(h.device, c.hidden / kTile);
   h.wgp_wgs2 = cached_wgp_wgs(h.device, c.inter / kTile);
+  if (gemm_wgp_route_fits(c.hidden / kTile, c.experts))
+    h.wgp_route_wgs1 = cached_wgp_route_wgs(h.device, c.hidden / kTile, c.experts);
   hipStream_t s = static_cast<hipStream_t>(stream);
   // The buffer holds the previous call's data, in that call's layout: clear
   // the arrival counters this step's kernels expect at zero.
-  const Plan p = make_plan(c, M, 0, 0, h.wgp_wgs1, h.wgp_wgs2);
+  const Plan p = make_plan(c, M, 0, 0, h.wgp_wgs1, h.wgp_wgs2, h.wgp_route_wgs1);
   auto words_of = [&](int i) { return reinterpret_cast<int32_t*>(h.ws + h.reg[i].off); };
   hipError_t e = launch_zero_words(words_of(kCtrl), h.reg[kCtrl].bytes / sizeof(int32_t), s);
   if (e == hipSuccess && p.fuse_combine)

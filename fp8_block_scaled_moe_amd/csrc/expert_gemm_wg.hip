@@ -33,6 +33,7 @@
 
 #include "epilogue_device.h"
 #include "gemm_device.h"
+#include "route_device.h"
 
 namespace moe {
 namespace {
@@ -325,7 +326,7 @@ struct UnitRef {
 // activation and FP8 codes (the arithmetic of the separate kernel, its split
 // sum of one slice included). Contains barriers.
 __device__ void finish_swiglu_blocks(const SwigluFuse& f, const GemmProblem& a, const UnitRef& u, int rows_wg,
-                                     int* claimed, int& nclaim) {
+                                     int* claimed, int& nclaim, const int32_t* routes) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   // These stores are at the device coherence point once they complete (the
   // next unit's first requests, issued before them, complete too).
@@ -337,7 +338,7 @@ __device__ void finish_swiglu_blocks(const SwigluFuse& f, const GemmProblem& a, 
   const int c = (row0 < f.I ? row0 : row0 - f.I) / kTile;  // the unit's rows lie in one 128-row block
   const int nblk = f.I / kTile, target = 2 * (kTile / rows_wg);
   if (tid < u.cnt) {
-    const int r = a.b.routes[u.off + tid];
+    const int r = routes[u.off + tid];
     int32_t* ctr = f.counters + (size_t)r * nblk + c;
     if (__hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == target - 1) {
       __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
@@ -358,26 +359,224 @@ __device__ void finish_swiglu_blocks(const SwigluFuse& f, const GemmProblem& a, 
   }
 }
 
-template <int kRole, bool kSwiglu>
+__host__ __device__ inline size_t wgp_lds_bytes(int nkb) {
+  return 4 * (size_t)kTileBytes + kRedFloats * 4 + (size_t)2 * (4 * nkb + nkb * kRoutesPerPass) * 4;
+}
+
+// LDS of the routing prologue, after the kernel's own: the jobs, x's FP8
+// codes and scales, the picks and the buckets (at most 64 routes).
+struct RouteLds {
+  uint8_t* xq;  // [M][K]
+  float* xs;    // [M][K / 128]
+  int* ids;     // [M * k]
+  Buckets b;    // routes, uexp, uoff, ucnt, rjob [64], ctrl [4], jobs [64]
+};
+
+__host__ __device__ inline size_t route_lds_bytes(int nkb) {
+  return (size_t)kWave * 16 + (size_t)kRouteFuseMaxTokens * nkb * (kTile + 4) + (size_t)6 * kWave * 4 + 16;
+}
+
+__device__ __forceinline__ RouteLds carve_route(unsigned char* p, int nkb) {
+  RouteLds l;
+  l.b.jobs = reinterpret_cast<int4*>(p);
+  p += kWave * 16;
+  l.xq = p;
+  p += (size_t)kRouteFuseMaxTokens * nkb * kTile;
+  l.xs = reinterpret_cast<float*>(p);
+  int* q = reinterpret_cast<int*>(l.xs + kRouteFuseMaxTokens * nkb);
+  l.ids = q;
+  l.b.routes = q + kWave;
+  l.b.uexp = q + 2 * kWave;
+  l.b.uoff = q + 3 * kWave;
+  l.b.ucnt = q + 4 * kWave;
+  l.b.rjob = q + 5 * kWave;
+  l.b.ctrl = q + 6 * kWave;
+  return l;
+}
+
+// Whole workgroup, before its first unit: routing of the M tokens, their
+// local routes grouped into jobs of at most 16, and x staged as FP8 codes,
+// into this workgroup's LDS, by the routing kernel's own functions. The
+// sigmoids of all (token, expert) pairs are shared out over the workgroup
+// through `keys_lds` (the kernel's weight tiles, not yet in use); then wave
+// t < M takes token t's picks, a chain of dependent wave-wide steps, while
+// the other waves quantise x's 128-blocks (eight lanes per block); with
+// one token the picking wave lists the jobs right away, with two wave 0
+// groups the routes after a barrier. Workgroup 0 also writes the picks,
+// weights, expert-ordered buckets, codes and scales to device memory. Expert e of a token sits in
+// lane e % 64, slot e / 64 (E <= 64 kPer, M * E * 8 bytes within the weight
+// tiles' space, M * k <= 64: checked by the host). Contains barriers.
+template <int kPer>
+__device__ void route_prologue(const RouteFuse& f, const GemmProblem& a, unsigned char* keys_lds, const RouteLds& l) {
+  constexpr int kWaves = kThreads / kWave;
+  // blocks per group of eight lanes when the waves past the M picking ones quantise
+  constexpr int kMinGroups = (kWaves - kRouteFuseMaxTokens) * (kWave / 8);
+  constexpr int kQ = (kRouteFuseMaxTokens * kMaxPersistBlocks + kMinGroups - 1) / kMinGroups;
+  constexpr int kS = kRouteFuseMaxTokens * kWave * kPer / kThreads;  // sigmoids per thread
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int M = f.M, E = f.E, K = a.K, nkb = a.nkb;
+  const bool out = blockIdx.x == 0;
+  uint32_t* keys = reinterpret_cast<uint32_t*>(keys_lds);  // [M][E]
+  float* scores = reinterpret_cast<float*>(keys + M * E);  // [M][E]
+
+  // every load first: the logits and bias of this thread's pairs, and (waves
+  // past the picking ones) the BF16 values of the thread's group's blocks
+  float z[kS], bias[kS];
+#pragma unroll
+  for (int q = 0; q < kS; ++q) {
+    const int i = tid + q * kThreads;
+    z[q] = 0.f;
+    bias[q] = 0.f;
+    if (i < M * E) {
+      z[q] = router_logit(f.logits, f.logits_bf16, E, i / E, i % E);
+      bias[q] = f.bias[i % E];
+    }
+  }
+  // quantising waves only: group grp in [0, groups) takes blocks grp,
+  // grp + groups, ... of the M * nkb
+  const bool quant = wave >= M;
+  const int groups = (kWaves - M) * (kWave / 8), sub = lane % 8;
+  const int grp = quant ? (wave - M) * (kWave / 8) + lane / 8 : 0;
+  const int items = M * nkb;
+  u32x4_t lo[kQ], hi[kQ];
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    const int item = grp + q * groups;
+    if (quant && item < items) {
+      const size_t at = (size_t)(item / nkb) * K + (size_t)(item % nkb) * kTile + sub * 16;
+      lo[q] = *reinterpret_cast<const u32x4_t*>(f.x + at);
+      hi[q] = *reinterpret_cast<const u32x4_t*>(f.x + at + 8);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < kS; ++q) {
+    const int i = tid + q * kThreads;
+    if (i < M * E) {
+      const float sc = sigmoid_f32(z[q]);
+      scores[i] = sc;
+      keys[i] = ordered_key(sc + bias[q]);
+    }
+  }
+  __syncthreads();
+
+  if (wave < M) {  // token `wave`'s picks
+    const int t = wave;
+    uint32_t key[kPer];
+    float score[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int e = lane + kWave * j;
+      key[j] = 0;
+      score[j] = 0.f;
+      if (e < E) {
+        key[j] = keys[t * E + e];
+        score[j] = scores[t * E + e];
+      }
+    }
+    int id;
+    float s, total;
+    pick_top_k<kPer>(key, score, E, f.k, lane, id, s, total);
+    if (lane < f.k) {
+      l.ids[t * f.k + lane] = id;
+      if (out) {
+        f.ids[(size_t)t * f.k + lane] = id;
+        f.weights[(size_t)t * f.k + lane] = pick_weight(s, total, f.routed_scale);
+      }
+    }
+    if (M == 1) {
+      // One route per expert: this workgroup's jobs are the local picks in
+      // pick order, one route each (a GEMM1 sum depends only on its route,
+      // not on the job that carries it). The kernels that follow get the
+      // expert-ordered buckets from workgroup 0.
+      const int e_loc = id - f.lb;
+      const uint64_t local = __ballot(lane < f.k && e_loc >= 0 && e_loc < f.lc);
+      const int pos = __popcll(local & ((1ull << lane) - 1ull));
+      if ((local >> lane) & 1ull) {
+        l.b.jobs[pos] = make_int4(e_loc, pos, 1, 0);
+        l.b.routes[pos] = lane;
+      }
+      if (lane == 0) l.b.ctrl[2] = __popcll(local);
+      if (out) {
+        wave_lds_fence();
+        bucket_routes_wave(a.b, l.ids, f.k, f.lb, f.lc, kRoutesPerPass, lane);
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    const int item = grp + q * groups;
+    if (quant && item < items) {  // the same for the eight lanes of a group
+      float v[16];
+      bf16x16_values(lo[q], hi[q], v);
+      float sc;
+      const u32x4_t c = fp8_block_codes(v, block_amax8(v), f.ue8m0, sc);
+      const int t = item / nkb, blk = item % nkb;
+      const size_t at = (size_t)t * K + (size_t)blk * kTile + sub * 16;
+      *reinterpret_cast<u32x4_t*>(l.xq + at) = c;
+      if (sub == 0) l.xs[t * nkb + blk] = sc;
+      if (out) {
+        *reinterpret_cast<u32x4_t*>(f.xq + at) = c;
+        if (sub == 0) f.xs[(size_t)t * nkb + blk] = sc;
+      }
+    }
+  }
+  __syncthreads();
+  if (M > 1) {
+    if (wave == 0) {
+      bucket_routes_wave(l.b, l.ids, M * f.k, f.lb, f.lc, kRoutesPerPass, lane);
+      if (out) bucket_routes_wave(a.b, l.ids, M * f.k, f.lb, f.lc, kRoutesPerPass, lane);
+    }
+    __syncthreads();
+  }
+}
+
+// kRoutePer > 0: the routing prologue runs first (RouteFuse; experts per
+// lane), and the jobs, routes and activations come from this workgroup's LDS.
+template <int kRole, bool kSwiglu, int kRoutePer>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void gemm_wgp_kernel(GemmArgs args) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int claimed[kRoutesPerPass];
   __shared__ int nclaim;
+  constexpr bool kRoute = kRoutePer > 0;
   const GemmProblem& a = args.p[1];
-  // The argument lines the first unit needs are read under one wait, and
-  // the first unit's job beside the job count: read at first use, each
-  // would add a memory round trip before the first weight request. The job
-  // index is clamped to the routes (jobs never outnumber them), so the early
-  // read stays inside the table; past the count it is not used.
-  int kparts = a.kparts;  // passed through the read below, so nothing computes ahead of it
-  asm volatile("" : "+s"(kparts) : "s"(a.w), "s"(a.b.jobs), "s"(a.b.ctrl), "s"(a.R));
-  const int rows_wg = kRowsPerWg / kparts;
-  const int per_expert = a.N / rows_wg;
   int u = blockIdx.x;
+  int kparts, rows_wg, per_expert, total;
+  int4 job0;
+  const int4* jobs;
+  const int32_t* routes;
+  const uint8_t* aq;  // activation codes [rows, K] and scales [rows, K / 128]
+  const float* as;
+  if constexpr (kRoute) {
+    const RouteLds l = carve_route(smem + wgp_lds_bytes(a.nkb), a.nkb);
+    route_prologue<kRoutePer>(args.rf, a, smem, l);
+    kparts = a.kparts;
+    rows_wg = kRowsPerWg / kparts;
+    per_expert = a.N / rows_wg;
+    jobs = l.b.jobs;
+    routes = l.b.routes;
+    aq = l.xq;
+    as = l.xs;
+    job0 = jobs[min(u / per_expert, kWave - 1)];  // past the count: not used
+    total = l.b.ctrl[2] * per_expert;
+  } else {
+    // The argument lines the first unit needs are read under one wait, and
+    // the first unit's job beside the job count: read at first use, each
+    // would add a memory round trip before the first weight request. The job
+    // index is clamped to the routes (jobs never outnumber them), so the early
+    // read stays inside the table; past the count it is not used.
+    kparts = a.kparts;  // passed through the read below, so nothing computes ahead of it
+    asm volatile("" : "+s"(kparts) : "s"(a.w), "s"(a.b.jobs), "s"(a.b.ctrl), "s"(a.R));
+    rows_wg = kRowsPerWg / kparts;
+    per_expert = a.N / rows_wg;
+    jobs = a.b.jobs;
+    routes = a.b.routes;
+    aq = a.aq;
+    as = a.as;
+    job0 = jobs[min(u / per_expert, a.R - 1)];
+    total = a.b.ctrl[2] * per_expert;  // jobs x units per job
+    asm volatile("" ::"v"(job0.x), "v"(job0.y), "v"(job0.z));  // keeps the read above the exit
+  }
   const int j0 = u / per_expert;
-  const int4 job0 = a.b.jobs[min(j0, a.R - 1)];
-  const int total = a.b.ctrl[2] * per_expert;  // jobs x units per job
-  asm volatile("" ::"v"(job0.x), "v"(job0.y), "v"(job0.z));  // keeps the read above the exit
   const int G = gridDim.x;
   if (u >= total) return;  // more slots than units: the whole workgroup exits
 
@@ -399,7 +598,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     UnitRef x;
     const int j = v / per_expert;
     x.tile = v - j * per_expert;
-    const int4 job = a.b.jobs[j];  // {local expert, first index in routes, count <= 16, 0}
+    const int4 job = jobs[j];  // {local expert, first index in routes, count <= 16, 0}
     x.e = job.x;
     x.off = job.y;
     x.cnt = job.z;
@@ -416,7 +615,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   float sw = 0.f, sx[kSxPerThread];
   int rt_next = 0, xrow_next = 0;
   auto fetch_routes = [&](const UnitRef& x) {  // first level: the route of this lane's column
-    rt_next = a.b.routes[x.off + (col < x.cnt ? col : 0)];  // lanes past the routes repeat route 0
+    rt_next = routes[x.off + (col < x.cnt ? col : 0)];  // lanes past the routes repeat route 0
     xrow_next = rt_next / a.act_div;
     if (tid < nsw) {
       const int r = tid / nkb, b = tid - r * nkb;
@@ -427,7 +626,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
 #pragma unroll
     for (int j = 0; j < kSxPerThread; ++j) {
       const int b = tid / kRoutesPerPass + (kThreads / kRoutesPerPass) * j;
-      sx[j] = col < x.cnt && b < nkb ? a.as[(size_t)xrow_next * nkb + b] : 0.f;
+      sx[j] = col < x.cnt && b < nkb ? as[(size_t)xrow_next * nkb + b] : 0.f;
     }
   };
   auto commit = [&](float* st, const UnitRef& x) {
@@ -448,8 +647,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   auto x_of = [&](int xrow) { return (uint32_t)(xrow * a.K + kb0 * kTile + g * 16); };
   auto load_x = [&](uint32_t px, int q, int st) {
     const uint32_t o = px + (uint32_t)st * kTile;
-    xa[q] = *reinterpret_cast<const u32x4_t*>(a.aq + o);
-    xb[q] = *reinterpret_cast<const u32x4_t*>(a.aq + (o + 64));
+    xa[q] = *reinterpret_cast<const u32x4_t*>(aq + o);
+    xb[q] = *reinterpret_cast<const u32x4_t*>(aq + (o + 64));
   };
 
   // The first unit: requests, then staging, as the one-unit kernel does.
@@ -546,7 +745,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
         *reinterpret_cast<float4_t*>(dst) = acc;
       }
     }
-    if constexpr (kSwiglu) finish_swiglu_blocks(args.sf, a, cur, rows_wg, claimed, nclaim);
+    if constexpr (kSwiglu) finish_swiglu_blocks(args.sf, a, cur, rows_wg, claimed, nclaim, routes);
     if (!more) break;
     commit(stage + (buf ^ 1) * stage_floats, nx);
     __syncthreads();  // the next unit's scales are in place; this unit is done with red and its stage
@@ -565,8 +764,13 @@ size_t gemm_wg_lds_bytes(int nkb) {
          kRoutesPerPass * 4;
 }
 
-size_t gemm_wgp_lds_bytes(int nkb) {
-  return 4 * (size_t)kTileBytes + kRedFloats * 4 + (size_t)2 * (4 * nkb + nkb * kRoutesPerPass) * 4;
+size_t gemm_wgp_lds_bytes(int nkb) { return wgp_lds_bytes(nkb); }
+
+size_t gemm_wgp_route_lds_bytes(int nkb) { return wgp_lds_bytes(nkb) + route_lds_bytes(nkb); }
+
+bool gemm_wgp_route_fits(int nkb, int E) {
+  return E >= 1 && E <= 16 * kWave && (size_t)kRouteFuseMaxTokens * E * 8 <= wgp_lds_bytes(nkb) &&
+         nkb <= kMaxPersistBlocks;
 }
 
 bool gemm_wgp_fits(int nkb, int kparts) {
@@ -577,8 +781,22 @@ int gemm_wgp_resident_wgs(int nkb) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(gemm_wgp_kernel<1, false>),
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(gemm_wgp_kernel<1, false, 0>),
                                                    kThreads, gemm_wgp_lds_bytes(nkb)) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return cus * per_cu;
+}
+
+int gemm_wgp_route_resident_wgs(int nkb, int E) {
+  int dev = 0, cus = 0, per_cu = 0;
+  const void* k = E <= 4 * kWave ? reinterpret_cast<const void*>(gemm_wgp_kernel<1, false, 4>)
+                                 : reinterpret_cast<const void*>(gemm_wgp_kernel<1, false, 16>);
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, gemm_wgp_route_lds_bytes(nkb)) !=
+          hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
@@ -590,16 +808,29 @@ hipError_t launch_gemm_wgp(const GemmArgs& a, int role, int grid, hipStream_t s,
   if (a.units0 || a.cf.on || grid < 1 || !gemm_wgp_fits(p.nkb, p.kparts))
     return hipErrorInvalidValue;
   const size_t lds = gemm_wgp_lds_bytes(p.nkb);
-  if (a.sf.on) {
+  if (a.rf.on) {
+    // every workgroup routes: its LDS holds the jobs, x's codes and the picks
+    const RouteFuse& f = a.rf;
+    if (role != 1 || a.sf.on || f.M < 1 || f.M > kRouteFuseMaxTokens || f.M * f.k > kWave || f.k < 1 ||
+        p.K != p.nkb * kTile || p.act_div != f.k || !gemm_wgp_route_fits(p.nkb, f.E))
+      return hipErrorInvalidValue;
+    const size_t rlds = gemm_wgp_route_lds_bytes(p.nkb);
+    if (f.E <= 4 * kWave)
+      hipExtLaunchKernelGGL((gemm_wgp_kernel<1, false, 4>), dim3(grid), dim3(kThreads), rlds, s,
+                            ev.start, ev.stop, 0, a);
+    else
+      hipExtLaunchKernelGGL((gemm_wgp_kernel<1, false, 16>), dim3(grid), dim3(kThreads), rlds, s,
+                            ev.start, ev.stop, 0, a);
+  } else if (a.sf.on) {
     // the unit's rows must lie in one 128-column block of up or of gate
     if (role != 1 || p.N != 2 * a.sf.I || kTile % (kRowsPerWg / p.kparts) != 0) return hipErrorInvalidValue;
-    hipExtLaunchKernelGGL((gemm_wgp_kernel<1, true>), dim3(grid), dim3(kThreads), lds, s,
+    hipExtLaunchKernelGGL((gemm_wgp_kernel<1, true, 0>), dim3(grid), dim3(kThreads), lds, s,
                           ev.start, ev.stop, 0, a);
   } else if (role == 1) {
-    hipExtLaunchKernelGGL((gemm_wgp_kernel<1, false>), dim3(grid), dim3(kThreads), lds, s,
+    hipExtLaunchKernelGGL((gemm_wgp_kernel<1, false, 0>), dim3(grid), dim3(kThreads), lds, s,
                           ev.start, ev.stop, 0, a);
   } else {
-    hipExtLaunchKernelGGL((gemm_wgp_kernel<2, false>), dim3(grid), dim3(kThreads), lds, s,
+    hipExtLaunchKernelGGL((gemm_wgp_kernel<2, false, 0>), dim3(grid), dim3(kThreads), lds, s,
                           ev.start, ev.stop, 0, a);
   }
   return hipGetLastError();

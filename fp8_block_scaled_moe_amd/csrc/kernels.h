@@ -165,6 +165,30 @@ struct SwigluFuse {
   float* hs;            // [R, I/128]
 };
 
+// Routing and the activation quantisation inside the persistent GEMM1 launch
+// (at most kRouteFuseMaxTokens tokens and 64 routes): every workgroup routes
+// the M tokens, groups their local routes into jobs and stages x as FP8
+// codes in its own LDS before its first unit, with the functions the
+// routing kernel runs (route_device.h); workgroup 0 also writes the picks,
+// weights, buckets, codes and scales out for the kernels that follow.
+// Arrays as in RouteQuantArgs; the buckets are the routed problem's.
+constexpr int kRouteFuseMaxTokens = 2;
+struct RouteFuse {
+  int on;
+  const void* logits;   // [M, E] f32 or bf16
+  int logits_bf16;
+  const float* bias;    // [E]
+  const uint16_t* x;    // [M, K] bf16
+  int M, E, k;
+  float routed_scale;
+  int ue8m0;
+  int lb, lc;
+  int32_t* ids;         // [M, k]
+  float* weights;       // [M, k]
+  uint8_t* xq;          // [M, K] e4m3 (the routed problem's aq)
+  float* xs;            // [M, K/128] (its as)
+};
+
 // One GEMM launch: the dense problem's units (if any) come first in the grid,
 // then the routed problem's.
 struct GemmArgs {
@@ -175,6 +199,7 @@ struct GemmArgs {
   int32_t* stream_counts;  // FP4 kernel: [J, tiles] partial slots of each tile, written here
   CombineFuse cf;       // K-in-workgroup GEMM2 only
   SwigluFuse sf;        // persistent GEMM1 only
+  RouteFuse rf;         // persistent GEMM1 only
 };
 
 // FP4 GEMM: a stream of (job, tile, step) items split evenly over the
@@ -221,6 +246,12 @@ hipError_t launch_gemm_wgp(const GemmArgs& a, int role, int grid, hipStream_t s,
 size_t gemm_wgp_lds_bytes(int nkb);
 bool gemm_wgp_fits(int nkb, int kparts);
 int gemm_wgp_resident_wgs(int nkb);
+// The persistent GEMM1 with routing inside (RouteFuse): LDS per workgroup,
+// whether E experts fit its routing prologue for nkb K blocks, and its
+// resident workgroups (0 on error).
+size_t gemm_wgp_route_lds_bytes(int nkb);
+bool gemm_wgp_route_fits(int nkb, int E);
+int gemm_wgp_route_resident_wgs(int nkb, int E);
 // FP32 [n/128, k/128] scales from packed UE8M0 words int32 [n, ceil(k/512)];
 // *bad is set nonzero when the rows of a 128-row block disagree.
 hipError_t launch_unpack_ue8m0(const int32_t* packed, int n, int k, float* out, int32_t* bad,

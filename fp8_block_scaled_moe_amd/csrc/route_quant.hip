@@ -1,13 +1,6 @@
-// Routing, activation quantisation and expert bucketing.
-//
-// Routing follows the vLLM "mega_moe" page (top_k_pick, _ordered): FP32
-// sigmoid scores, FP32 keys score + bias compared through a monotone integer
-// image, top_k rounds of a wave-wide maximum with ties to the lower expert,
-// weights = picked score / (FP32 sum of picked scores in pick order) * scale.
-// The activation quantiser is the same page's epilogue: per 128 values,
-// scale = max(amax, 1e-10) / 448 (IEEE divide), optionally rounded up to a
-// power of two after flooring it at 1e-10, then v * (1 / scale) encoded to
-// e4m3.
+// Routing, activation quantisation and expert bucketing (the arithmetic is
+// in route_device.h, shared with the routing prologue of the persistent
+// GEMM1).
 //
 // Launch: one 1024-thread routing workgroup per 4 tokens (2 when there are
 // more than 4); its waves 0..3 (or 0..1, on their own SIMDs) each route one
@@ -19,9 +12,8 @@
 // arrive (atomic counter, reset by that workgroup) does it.
 #include <algorithm>
 
-#include "kernels.h"
-#include "device_common.h"
 #include "fp4_device.h"
+#include "route_device.h"
 
 namespace moe {
 namespace {
@@ -29,7 +21,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;  // 16
 // Tokens per workgroup, one routing wave each, one per SIMD: routing is
-// VALU-issue bound (FP64 sigmoid, 64-bit DPP maxima), so two routing waves
+// VALU-issue bound (FP64 sigmoid, DPP maxima), so two routing waves
 // on a SIMD take twice as long (measured on MI355X at M = 8: 11.6 us as two
 // workgroups against 13.0 us as one). Up to 4 tokens run in one workgroup
 // (no cross-workgroup handoff); more run 2 to a workgroup: on one GPU's FP4
@@ -51,101 +43,31 @@ inline int quant_wgs(int M, int H) {
   return items > have ? std::min((items - have + kThreads / 8 - 1) / (kThreads / 8), kMaxQuantWgs) : 0;
 }
 
-// Monotone image of an FP32 value in uint32: a > b as floats (with -0 < +0)
-// iff key(a) > key(b). Negatives flip every bit, the rest flip the sign bit.
-__device__ __forceinline__ uint32_t ordered_key(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ float sigmoid_f32(float z) {
-  // FP32 rounding of the sigmoid evaluated in FP64.
-  return (float)(1.0 / (1.0 + exp(-(double)z)));
-}
-
-template <int kCtrl>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)v, kCtrl, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), kCtrl, 0xF, 0xF, false);
-  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
-  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, lane);
-  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-// Wave-wide maximum: DPP permutations inside each row of 16 lanes (swap
-// neighbours, swap pairs, half-row mirror, row mirror), then the four row
-// results through readlane. Every lane returns the same value.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = max_u64(v, dpp_u64<0xB1>(v));   // quad_perm [1,0,3,2]
-  v = max_u64(v, dpp_u64<0x4E>(v));   // quad_perm [2,3,0,1]
-  v = max_u64(v, dpp_u64<0x141>(v));  // row_half_mirror
-  v = max_u64(v, dpp_u64<0x140>(v));  // row_mirror
-  return max_u64(max_u64(readlane_u64(v, 0), readlane_u64(v, 16)),
-                 max_u64(readlane_u64(v, 32), readlane_u64(v, 48)));
-}
-
 // One wave: the picks and weights of token t. Lane l holds experts
 // l + 64 j for j < kPer (kPer >= E / 64).
 template <int kPer>
 __device__ void route_token(const RouteQuantArgs& a, int t, int lane, int* ids_l) {
-  const int E = a.E;
   float score[kPer];
-  uint64_t key[kPer];
+  uint32_t key[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     score[j] = 0.f;
     key[j] = 0;
     const int e = lane + kWave * j;
-    if (e < E) {
-      const size_t at = (size_t)t * E + e;
-      const float z = a.logits_bf16 ? bf16_value(((const uint16_t*)a.logits)[at])
-                                    : ((const float*)a.logits)[at];
-      const float s = sigmoid_f32(z);
-      const float biased = s + a.bias[e];
-      score[j] = s;
-      // high word: the key; low word: ~e, so that equal keys favour lower e
-      key[j] = ((uint64_t)ordered_key(biased) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+    if (e < a.E) {
+      score[j] = sigmoid_f32(router_logit(a.logits, a.logits_bf16, a.E, t, e));
+      key[j] = ordered_key(score[j] + a.bias[e]);
     }
   }
-  float total = 0.f;
-  int my_id = 0;
-  float my_score = 0.f;
-  for (int r = 0; r < a.k; ++r) {
-    uint64_t best = key[0];
-#pragma unroll
-    for (int j = 1; j < kPer; ++j) best = max_u64(best, key[j]);
-    best = wave_max_u64(best);
-    const int winner = (int)(0xFFFFFFFFu - (uint32_t)best);
-    const int owner = winner & (kWave - 1);
-    const int slot = winner / kWave;
-    float s_slot = 0.f;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      if (j == slot) {
-        s_slot = score[j];
-        if (lane == owner) key[j] = 0;
-      }
-    }
-    const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_slot), owner));
-    total = total + s;
-    if (lane == r) {
-      my_id = winner;
-      my_score = s;
-    }
-  }
+  int my_id;
+  float my_score, total;
+  pick_top_k<kPer>(key, score, a.E, a.k, lane, my_id, my_score, total);
   if (lane < a.k) {
-    const float w = (my_score / total) * a.routed_scale;
     const size_t at = (size_t)t * a.k + lane;
     // written through to the device coherence point: another workgroup (on
     // another XCD, with its own L2) may read it in the cross-workgroup handoff
     __hip_atomic_store(a.ids + at, my_id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    a.weights[at] = w;
+    a.weights[at] = pick_weight(my_score, total, a.routed_scale);
     ids_l[at] = my_id;
   }
 }
@@ -183,13 +105,7 @@ __device__ void quant_blocks(const RouteQuantArgs& a, int group, int groups) {
       const int item = base + q * groups + group;
       if (item < items) {  // the same for all eight lanes of a group
         float v[16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[2 * i] = bf16_value(lo[q][i] & 0xFFFFu);
-          v[2 * i + 1] = bf16_value(lo[q][i] >> 16);
-          v[8 + 2 * i] = bf16_value(hi[q][i] & 0xFFFFu);
-          v[8 + 2 * i + 1] = bf16_value(hi[q][i] >> 16);
-        }
+        bf16x16_values(lo[q], hi[q], v);
         const int t = item / nblk, blk = item % nblk;
         const size_t at = (size_t)t * a.H + (size_t)blk * kTile + sub * 16;
         if (a.fp4) {  // this lane's 16 values are one FP4 group
@@ -199,30 +115,14 @@ __device__ void quant_blocks(const RouteQuantArgs& a, int group, int groups) {
           a.xs4[at / kFp4Group] = (uint8_t)sbyte;
           continue;
         }
-        float amax = kAmaxFloor;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
-        amax = group_max<8>(amax);
-        // scale = amax / 448, optionally rounded up to a power of two; codes
-        // = e4m3(v * (1 / scale))
-        auto emit = [&](int ue8m0, uint8_t* xq, float* xs) {
-          float s = amax / kFp8Max;
-          if (ue8m0) {
-            const uint32_t b = __float_as_uint(fmaxf(s, kAmaxFloor));
-            s = __uint_as_float(((b >> 23) + ((b & 0x7FFFFFu) != 0u)) << 23);
-          }
-          const float inv = 1.0f / s;
-          u32x4_t out;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            out[w] = e4m3x4_encode(v[4 * w] * inv, v[4 * w + 1] * inv, v[4 * w + 2] * inv,
-                                   v[4 * w + 3] * inv);
-          }
-          *reinterpret_cast<u32x4_t*>(xq + at) = out;
-          if (sub == 0) xs[(size_t)t * nblk + blk] = s;
-        };
-        emit(a.ue8m0, a.xq, a.xs);
-        if (a.xq2) emit(a.ue8m0_2, a.xq2, a.xs2);  // the shared expert's own scale rule
+        const float amax = block_amax8(v);
+        float sc;
+        *reinterpret_cast<u32x4_t*>(a.xq + at) = fp8_block_codes(v, amax, a.ue8m0, sc);
+        if (sub == 0) a.xs[(size_t)t * nblk + blk] = sc;
+        if (a.xq2) {  // the shared expert's own scale rule
+          *reinterpret_cast<u32x4_t*>(a.xq2 + at) = fp8_block_codes(v, amax, a.ue8m0_2, sc);
+          if (sub == 0) a.xs2[(size_t)t * nblk + blk] = sc;
+        }
       }
     }
   }
@@ -328,63 +228,9 @@ __device__ void bucket_routes(const RouteQuantArgs& a, const Lds& l) {
   }
 }
 
-// The same grouping by one wave when there are at most 64 routes, without
-// moving data between lanes. Lane r holds route r's local expert e. One
-// ballot per bit of e, from the top bit down, narrows two masks per lane:
-// the lanes whose expert equals e so far (eq) and those already known to be
-// smaller (lt). Then the route's place in (expert, route) order is
-// popc(lt) + popc(eq below the lane), the first lane of each expert's run
-// (none of eq below it) writes the bucket, and the bucket's index is the
-// number of smaller experts' first lanes. Non-local routes take no part.
-__device__ void bucket_routes_wave(const RouteQuantArgs& a, const int* ids, int lane) {
-  const int e = lane < a.M * a.k ? ids[lane] - a.lb : -1;
-  const bool mine = e >= 0 && e < a.lc;
-  const uint64_t below = (1ull << lane) - 1ull;
-  uint64_t eq = __ballot(mine), lt = 0;
-  const int bits = 32 - __builtin_clz((unsigned)max(a.lc - 1, 1));
-  for (int b = bits - 1; b >= 0; --b) {
-    const bool one = mine && ((e >> b) & 1);
-    const uint64_t ones = __ballot(one);
-    lt |= one ? eq & ~ones : 0ull;
-    eq &= one ? ones : ~ones;
-  }
-  const int pos = __popcll(eq & below);  // place in the expert's run
-  const int off = __popcll(lt);          // routes of smaller experts
-  const int cnt = __popcll(eq);
-  const bool first = mine && pos == 0;
-  const uint64_t starts = __ballot(first);
-  if (mine) a.b.routes[off + pos] = lane;
-  if (first) {
-    const int u = __popcll(starts & lt);
-    a.b.uexp[u] = e;
-    a.b.uoff[u] = off;
-    a.b.ucnt[u] = cnt;
-  }
-  if (lane == 0) a.b.ctrl[1] = __popcll(starts);
-  const int jr = a.job_routes;
-  if (jr > 0) {
-    // each run cut into jobs of jr routes; a run's first job is the sum of
-    // the smaller experts' job counts, taken one bit of the counts at a
-    // time (a count is at most 64)
-    const int nj = (cnt + jr - 1) / jr;
-    int jb = 0, total = 0;
-#pragma unroll
-    for (int b = 0; b < 7; ++b) {
-      const uint64_t has = __ballot(first && ((nj >> b) & 1));
-      jb += __popcll(has & lt) << b;
-      total += __popcll(has) << b;
-    }
-    if (mine) {
-      a.b.rjob[lane] = jb + pos / jr;
-      if (pos % jr == 0) a.b.jobs[jb + pos / jr] = make_int4(e, off + pos, min(jr, cnt - pos), 0);
-    }
-    if (lane == 0) a.b.ctrl[2] = total;
-  }
-}
-
 __device__ __forceinline__ void bucket_any(const RouteQuantArgs& a, const Lds& l) {
   if (a.M * a.k <= kWave) {
-    if (threadIdx.x < kWave) bucket_routes_wave(a, l.ids, threadIdx.x);
+    if (threadIdx.x < kWave) bucket_routes_wave(a.b, l.ids, a.M * a.k, a.lb, a.lc, a.job_routes, threadIdx.x);
   } else {
     bucket_routes(a, l);
   }

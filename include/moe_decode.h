@@ -87,7 +87,8 @@ extern "C" {
 #define MOE_GEMM_FP4 4          /* the MOE_WEIGHTS_NVFP4 kernel (reported by moe_decode_plan; gemm_path stays AUTO) */
 
 /* Launch shapes of run(). Every shape gives bit-identical results. */
-#define MOE_LAUNCH_AUTO 0             /* the shape measured fastest: MOE_LAUNCH_SEPARATE */
+#define MOE_LAUNCH_AUTO 0             /* the shape measured fastest: MOE_LAUNCH_ROUTE_IN_GEMM1 at
+                                         one token where it applies, else MOE_LAUNCH_SEPARATE */
 #define MOE_LAUNCH_SEPARATE 1         /* each step a launch of its own (five launches) */
 #define MOE_LAUNCH_COMBINE_IN_GEMM2 2 /* MOE_GEMM_MFMA only: the combine inside the GEMM2 launch
                                          (the workgroup that completes a token's column tile
@@ -96,6 +97,12 @@ extern "C" {
                                          requant inside the GEMM1 launch (the workgroup that
                                          completes a route's 128-column block finishes it);
                                          otherwise MOE_LAUNCH_SEPARATE */
+#define MOE_LAUNCH_ROUTE_IN_GEMM1 4   /* when GEMM1 runs on persistent workgroups, M <= 2 and
+                                         M * top_k <= 64: routing and the x quantisation inside
+                                         the GEMM1 launch (every workgroup routes the tokens
+                                         itself, the "mega_moe" page's per-warp routing, and
+                                         workgroup 0 writes ids and weights); otherwise
+                                         MOE_LAUNCH_SEPARATE */
 
 /* Limits of this implementation. */
 #define MOE_DECODE_MAX_EXPERTS 1024
@@ -283,7 +290,8 @@ const char* moe_decode_error_string(int code);
  * part, out[13] / out[14] = its work units in the GEMM1 / GEMM2 launches.
  * With n >= 17: out[15] / out[16] = K parts per workgroup in GEMM1 / GEMM2
  * (1 on the split-K paths). With n >= 18: out[17] = kernel launches of run()
- * (5, or 4 when the combine or the SwiGLU runs inside a GEMM launch). With n >= 20:
+ * (5, less one for each of routing, the SwiGLU and the combine that runs
+ * inside a GEMM launch). With n >= 20:
  * out[18] / out[19] = workgroups of the persistent GEMM1 / GEMM2 launch on
  * MOE_GEMM_MFMA (0: one workgroup per unit). On MOE_GEMM_FP4: out[1] / out[2] = the most
  * partial slots a 64-row tile can have, out[3] / out[4] = 128-K blocks of
@@ -334,9 +342,9 @@ int moe_decode_debug_stage(moe_decode_t h, int32_t stage, void* dst, size_t byte
  * so the time excludes the gaps between launches. After a run has completed,
  * moe_decode_last_timing writes the milliseconds of each kernel in order:
  * route+quant, GEMM1, SwiGLU+requant, GEMM2, combine (the shared expert, when
- * run, is part of the last four; when the combine or the SwiGLU runs inside a
- * GEMM launch, its time is that GEMM's and its own entry is 0). n is the
- * capacity of ms (>= 5). */
+ * run, is part of the last four; when routing, the combine or the SwiGLU
+ * runs inside a GEMM launch, its time is that GEMM's and its own entry is 0).
+ * n is the capacity of ms (>= 5). */
 int moe_decode_set_timing(moe_decode_t h, int32_t enable);
 int moe_decode_last_timing(moe_decode_t h, float* ms, int32_t n);
 

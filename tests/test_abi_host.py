@@ -78,7 +78,7 @@ _SHARED = dict(sw13=8192, sw13_scale=8192, sw2=8192, sw2_scale=8192, shared_limi
     (dict(w13=None), _capi.ERR_INVALID_ARG),
     (dict(w2_scale=4100), _capi.ERR_INVALID_ARG),   # misaligned
     (dict(gemm_path=5), _capi.ERR_UNSUPPORTED),
-    (dict(launch_mode=4), _capi.ERR_UNSUPPORTED),
+    (dict(launch_mode=5), _capi.ERR_UNSUPPORTED),
     (dict(launch_mode=-1), _capi.ERR_UNSUPPORTED),
     (dict(splits1=-1), _capi.ERR_INVALID_ARG),
     # shared expert

@@ -46,7 +46,8 @@ def assert_same(a, b):
 
 @pytest.mark.parametrize("path", ["auto", "mfma_splitk"])
 def test_noalloc_matches_handle_dsv3(path):
-    """DeepSeek-V3 shapes: 8 tokens, then 3 on the same buffer."""
+    """DeepSeek-V3 shapes: 8 tokens, then 3 on the same buffer, then 1 (with
+    the automatic launch shape, routing inside the GEMM1 launch)."""
     inp = synth.make_inputs(synth.CONFIGS["dsv3"].with_(M=8), seed=40, device=DEV)
     moe = make(inp, 8, gemm_path=path)
     for M in (8, 3):
@@ -59,6 +60,8 @@ def test_noalloc_matches_handle_dsv3(path):
     assert np.array_equal(b[1].cpu().numpy(), ref["ids"])
     np.testing.assert_allclose(host(b[2]), ref["weights"], rtol=WEIGHT_RTOL, atol=0)
     assert_rows_close(host(b[3]), ref["combined"], what="combined")
+    assert moe.plan(1)["launches"] == (4 if path == "auto" else 5)
+    assert_same(*both(moe, inp, 1))
 
 
 @pytest.mark.parametrize("mode", ["separate", "combine_in_gemm2", "swiglu_in_gemm1"])
