@@ -41,21 +41,24 @@ GEMM1_TRAFFIC = [
     {"sources": ["fp8_block_scaled_moe_amd/csrc/expert_gemm_wg.hip",
                  "fp8_block_scaled_moe_amd/csrc/gemm_device.h",
                  "fp8_block_scaled_moe_amd/csrc/device_common.h",
+                 "fp8_block_scaled_moe_amd/csrc/epilogue_device.h",
+                 "fp8_block_scaled_moe_amd/csrc/route_device.h",
                  "fp8_block_scaled_moe_amd/csrc/kernels.h",
                  "fp8_block_scaled_moe_amd/csrc/capi.hip"],  # the plan (K parts, grids)
-     "sources_sha256_16": "66f48116f1eac6a0",
+     "sources_sha256_16": "53f74abbcc88435e",
      "workload": "dsv3", "M": 4, "seed": 0, "unique_experts": 27,
      # medians per dispatch (KiB) and the copy kernel's reading of 256 MiB
-     "fetch_kib": 387997.0, "write_kib": 512.0, "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0},
+     "fetch_kib": 387990.5, "write_kib": 512.0, "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0},
     {"sources": ["fp8_block_scaled_moe_amd/csrc/expert_gemm_fp4.hip",
                  "fp8_block_scaled_moe_amd/csrc/fp4_device.h",
+                 "fp8_block_scaled_moe_amd/csrc/gemm_device.h",
                  "fp8_block_scaled_moe_amd/csrc/stream_device.h",
                  "fp8_block_scaled_moe_amd/csrc/device_common.h",
                  "fp8_block_scaled_moe_amd/csrc/kernels.h",
                  "fp8_block_scaled_moe_amd/csrc/capi.hip"],
-     "sources_sha256_16": "fcb1822eb6ecc4c7",
+     "sources_sha256_16": "dd531656c61de1e8",
      "workload": "fp4_share", "M": 16, "seed": 0, "unique_experts": 4,
-     "fetch_kib": 50334.72, "write_kib": 604.42, "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0},
+     "fetch_kib": 50262.41, "write_kib": 604.38, "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0},
 ]
 
 
