@@ -5,17 +5,21 @@
 //   out[r, n] = sum_g dec(Sw[e, n, g]) * dec(Sa[row(r), g]) * sum_{i in g} W[e, n, i] * A[row(r), i].
 //
 // On the matrix cores. gfx950's FP4 matrix instructions take power-of-two
-// scales per 32 values, not UE4M3 per 16, so the codes are widened to F16
-// with each value multiplied by its group's scale: an E2M1 value (two
-// significant bits) times a UE4M3 scale (four) is exact in F16, between
-// 2^-10 and 2688, on both operands. v_mfma_f32_4x4x4_16b_f16 then multiplies
-// exactly and adds in FP32. Its sixteen 4 x 4 x 4 blocks are laid along K:
-// for a wave's 16 rows and one 256-value item, instruction (row group g, k
-// step c) gives block b rows 4g .. 4g + 3 and the four values 16b + 4c ..
-// 16b + 4c + 3, so block b covers exactly scale group b of the item and a
-// lane's activation operand (block b, route x) is the same for all four row
-// groups: the activations are widened once per item for the 16 rows. The
-// blocks' partial sums are added across lanes when a tile ends. A job is up
+// scales per 32 values, not UE4M3 per 16, so the codes are widened to F16 in
+// software and the scales applied around v_mfma_f32_4x4x4_16b_f16. Its
+// sixteen 4 x 4 x 4 blocks are laid along K: for a wave's 16 rows and one
+// 256-value item, instruction (row group g, k step c) gives block b rows
+// 4g .. 4g + 3 and the four values 16b + 4c .. 16b + 4c + 3, so block b
+// covers exactly scale group b of the item, and a lane's activation operand
+// (block b, route x) is the same for all four row groups: the activations
+// are widened once per item for the 16 rows, each value times its group's
+// scale (an E2M1 value, two significant bits, times a UE4M3 scale, four, is
+// exact in F16, between 2^-10 and 2688). The weights are widened as they
+// are. A block's four chained instructions then sum the group exactly in
+// FP32 (every partial sum is an integer below 2^12 times Sa / 4), and one
+// FMA per output multiplies the group sum by the row's weight scale (exact,
+// 20 bits) and adds it to the FP32 accumulator: one rounding per group. The
+// accumulators' block partials are added across lanes when a tile ends. A job is up
 // to kFp4JobRoutes (four) routes of one expert, a block's four columns, so
 // an expert's weights are read once for up to four of its routes (decode
 // batches rarely give one GPU's expert more; more take further passes).
@@ -27,10 +31,11 @@
 //
 // Per item a wave reads 16 rows x 128 bytes with full-line loads (eight lanes
 // per row) and passes them through a private LDS tile to lane 4b + x as rows
-// x, 4 + x, 8 + x, 12 + x, bytes 8b .. 8b + 7; the rows' scales come from a
-// copy reordered once at create (reorder_fp4_scales below) as one coalesced
-// 4-byte load per lane; each lane's activation bytes (8) and scale byte come
-// from L2 straight into registers. The job count, the first job descriptors
+// x, 4 + x, 8 + x, 12 + x, bytes 8b .. 8b + 7; the 16 rows' scales of group b
+// come from a copy reordered once at create (reorder_fp4_scales below) as one
+// 16-byte load per lane (the four lanes of a block read the same bytes);
+// each lane's activation bytes (8) and scale byte come from L2 straight into
+// registers. The job count, the first job descriptors
 // and the first route entries are read under one wait at the start, so the
 // first weight request follows one memory round trip.
 #include <algorithm>
@@ -43,15 +48,25 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kDepth = 2;                             // items in flight per wave
+// Items in flight per wave: three for a long K (150 VGPRs, three waves per
+// SIMD), two otherwise (120, four). Measured on MI355X over one GPU's FP4
+// share (H = 7168, I = 3072, event timing): GEMM1 (K = 7168) took 13.3
+// against 14.8 us at M = 4, 20.6 against 22.1 at M = 16 (4 experts), 41.0
+// against 40.7 at M = 16 (9 experts) and 75.7 against 76.4 at M = 64 with
+// three rather than two; GEMM2 (K = 3072) 9.8 against 9.2 at M = 4 and 42.8
+// against 40.0 at M = 64.
+constexpr int kDeepK = 4096;
+__host__ __device__ constexpr int fp4_depth(int K) { return K >= kDeepK ? 3 : 2; }
 constexpr int kStepValues = 256;                      // K values per item
 constexpr int kStepBytes = kStepValues / 2;           // packed bytes of a row's item
 constexpr int kStepScales = kStepValues / kFp4Group;  // scale bytes of a row's item
 constexpr int kFp4TileStride = kStepBytes + 16;       // LDS row stride (conflict-free)
 constexpr int kFp4TileBytes = 16 * kFp4TileStride;
 constexpr int kSpec = kThreads;  // job descriptors and route entries read at the start
+constexpr int kFp4ScaleBytes = 16 * kStepScales;  // weight scale bytes of a 16-row group and item
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 
 struct Cursor {
   int j, tile, s;  // job, 64-row tile, K step
@@ -81,7 +96,20 @@ __device__ __forceinline__ half4_t widen4(uint32_t w, half2_t s) {
   return half4_t{lo.x, lo.y, hi.x, hi.y};
 }
 
-template <int kRole>
+// The same four values as they are.
+template <int kB>
+__device__ __forceinline__ half4_t widen4(uint32_t w) {
+  const half2_t lo = e2m1x2_to_f16x2<kB>(w), hi = e2m1x2_to_f16x2<kB + 1>(w);
+  return half4_t{lo.x, lo.y, hi.x, hi.y};
+}
+
+// Bytes 2h and 2h + 1 of w (UE4M3 scales) as FP32, exact.
+template <bool kHi>
+__device__ __forceinline__ float2_t scale_f32x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, kHi);
+}
+
+template <int kRole, int kDepth>
 __global__ __launch_bounds__(kThreads) void gemm_fp4_kernel(GemmArgs args) {
   __shared__ __align__(16) unsigned char tiles_lds[4 * kFp4TileBytes];
   __shared__ int4 spec_jobs[kSpec];
@@ -142,10 +170,10 @@ __global__ __launch_bounds__(kThreads) void gemm_fp4_kernel(GemmArgs args) {
   int pe = e0;
   uint32_t pxo = xo0, pso = so0;
 
-  u32x4_t wa[kDepth], wb[kDepth];
-  uint32_t sw[kDepth], sx[kDepth];
+  u32x4_t wa[kDepth], wb[kDepth], sw[kDepth];
+  uint32_t sx[kDepth];
   uint2 xv[kDepth];
-  const uint32_t lane_w = (uint32_t)rg * row_bytes + ch * 16, lane_s = (uint32_t)lane * 4;
+  const uint32_t lane_w = (uint32_t)rg * row_bytes + ch * 16, lane_s = (uint32_t)blk * 16;
   // Requests the item under the requesting cursor into buffer q: the weights
   // and their scales (request_w), then the activations (request_x, which then
   // moves the cursor on). Addresses are a uniform base plus this lane's
@@ -154,10 +182,10 @@ __global__ __launch_bounds__(kThreads) void gemm_fp4_kernel(GemmArgs args) {
   auto request_w = [&](int q) {
     const size_t group = (size_t)pe * (a.N / 16) + pc.tile * (kRowsPerWg / 16) + wave;  // 16-row group
     const uint8_t* w = a.w + group * 16 * row_bytes + (size_t)pc.s * kStepBytes;
-    const uint8_t* ws = a.ws8 + (group * S + pc.s) * (kWave * 4);
+    const uint8_t* ws = a.ws8 + (group * S + pc.s) * kFp4ScaleBytes;
     wa[q] = load_stream16(w + lane_w);
     wb[q] = load_stream16(w + (lane_w + 8 * row_bytes));
-    sw[q] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(ws + lane_s));
+    sw[q] = load_stream16(ws + lane_s);
   };
   auto request_x = [&](int q) {
     const uint8_t* xs = a.aq + (size_t)pc.s * kStepBytes;
@@ -188,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void gemm_fp4_kernel(GemmArgs args) {
   auto process = [&](int q, bool refill) {
     *reinterpret_cast<u32x4_t*>(tile + rg * kFp4TileStride + ch * 16) = wa[q];
     *reinterpret_cast<u32x4_t*>(tile + (rg + 8) * kFp4TileStride + ch * 16) = wb[q];
-    const half2_t ps[4] = {scale_pair<0>(sw[q]), scale_pair<1>(sw[q]), scale_pair<2>(sw[q]), scale_pair<3>(sw[q])};
+    const u32x4_t ws = sw[q];  // scales of rows 0 .. 15, group blk
     if (refill) request_w(q);
     wave_lds_fence();
     uint2 wr[4];  // rows 4r + x, bytes 8blk .. 8blk + 7
@@ -199,12 +227,19 @@ __global__ __launch_bounds__(kThreads) void gemm_fp4_kernel(GemmArgs args) {
     const half2_t pa = scale_pair<0>(sx[q]);
     const half4_t b0 = widen4<0>(xv[q].x, pa), b1 = widen4<2>(xv[q].x, pa);
     const half4_t b2 = widen4<0>(xv[q].y, pa), b3 = widen4<2>(xv[q].y, pa);
+    const float4_t zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      acc[r] = __builtin_amdgcn_mfma_f32_4x4x4f16(widen4<0>(wr[r].x, ps[r]), b0, acc[r], 0, 0, 0);
-      acc[r] = __builtin_amdgcn_mfma_f32_4x4x4f16(widen4<2>(wr[r].x, ps[r]), b1, acc[r], 0, 0, 0);
-      acc[r] = __builtin_amdgcn_mfma_f32_4x4x4f16(widen4<0>(wr[r].y, ps[r]), b2, acc[r], 0, 0, 0);
-      acc[r] = __builtin_amdgcn_mfma_f32_4x4x4f16(widen4<2>(wr[r].y, ps[r]), b3, acc[r], 0, 0, 0);
+      // group blk's exact sum for rows 4r .. 4r + 3 and route x
+      float4_t d = __builtin_amdgcn_mfma_f32_4x4x4f16(widen4<0>(wr[r].x), b0, zero, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_4x4x4f16(widen4<2>(wr[r].x), b1, d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_4x4x4f16(widen4<0>(wr[r].y), b2, d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_4x4x4f16(widen4<2>(wr[r].y), b3, d, 0, 0, 0);
+      const float2_t s01 = scale_f32x2<false>(ws[r]), s23 = scale_f32x2<true>(ws[r]);
+      acc[r][0] = fmaf(d[0], s01.x, acc[r][0]);
+      acc[r][1] = fmaf(d[1], s01.y, acc[r][1]);
+      acc[r][2] = fmaf(d[2], s23.x, acc[r][2]);
+      acc[r][3] = fmaf(d[3], s23.y, acc[r][3]);
     }
     if (refill) request_x(q);
   };
@@ -258,20 +293,21 @@ __global__ __launch_bounds__(kThreads) void gemm_fp4_kernel(GemmArgs args) {
 }
 
 // The weight scales [rows, K/16] (rows = E * N, a multiple of 16) into the
-// kernel's layout: for 16-row group g, item s (256 values) and lane l =
-// 4b + x, byte r of word (g * S + s) * 64 + l is the scale of group b of
-// item s in row 16g + 4r + x (the scales of the lane's MFMA operands). One
-// thread per output word.
+// kernel's layout: for 16-row group g and item s (256 values), 16 blocks of
+// 16 bytes, block b holding the scales of group b of item s in rows 16g ..
+// 16g + 15 (byte i: row 16g + i), which is what the lanes of MFMA block b
+// read. One thread per output word: word (g * S + s) * 64 + 4b + q holds
+// rows 16g + 4q .. 16g + 4q + 3.
 __global__ void reorder_fp4_scales_kernel(const uint8_t* src, uint32_t* dst, size_t words, int S) {
   const size_t w = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (w >= words) return;
-  const int l = (int)(w % kWave), x = l & 3, b = l >> 2;
+  const int l = (int)(w % kWave), b = l >> 2, q = l & 3;
   const size_t gs = w / kWave, g = gs / S;
   const int s = (int)(gs - g * S);
   const size_t row_scales = (size_t)S * kStepScales;
-  const uint8_t* p = src + (g * 16 + x) * row_scales + (size_t)s * kStepScales + b;
-  dst[w] = (uint32_t)p[0] | ((uint32_t)p[4 * row_scales] << 8) | ((uint32_t)p[8 * row_scales] << 16) |
-           ((uint32_t)p[12 * row_scales] << 24);
+  const uint8_t* p = src + (g * 16 + 4 * q) * row_scales + (size_t)s * kStepScales + b;
+  dst[w] = (uint32_t)p[0] | ((uint32_t)p[row_scales] << 8) | ((uint32_t)p[2 * row_scales] << 16) |
+           ((uint32_t)p[3 * row_scales] << 24);
 }
 
 __global__ void codec_check_fp4_kernel(const float* in, uint8_t* q, float* dq, int n) {
@@ -295,12 +331,13 @@ __global__ void codec_check_fp4_kernel(const float* in, uint8_t* q, float* dq, i
 
 size_t gemm_fp4_lds_bytes(int) { return 4 * (size_t)kFp4TileBytes + kSpec * (sizeof(int4) + sizeof(int)); }
 
-int gemm_fp4_resident_wgs(int) {
+int gemm_fp4_resident_wgs(int K) {
   int dev = 0, cus = 0, per_cu = 0;
+  const void* k = fp4_depth(K) == 3 ? reinterpret_cast<const void*>(gemm_fp4_kernel<1, 3>)
+                                    : reinterpret_cast<const void*>(gemm_fp4_kernel<1, 2>);
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(gemm_fp4_kernel<1>),
-                                                   kThreads, 0) != hipSuccess) {
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, 0) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
@@ -308,10 +345,15 @@ int gemm_fp4_resident_wgs(int) {
 }
 
 hipError_t launch_gemm_fp4(const GemmArgs& a, int role, int grid, hipStream_t s, KernelEvents ev) {
-  if (role == 1)
-    hipExtLaunchKernelGGL(gemm_fp4_kernel<1>, dim3(grid), dim3(kThreads), 0, s, ev.start, ev.stop, 0, a);
+  const bool deep = fp4_depth(a.p[1].K) == 3;
+  if (role == 1 && deep)
+    hipExtLaunchKernelGGL((gemm_fp4_kernel<1, 3>), dim3(grid), dim3(kThreads), 0, s, ev.start, ev.stop, 0, a);
+  else if (role == 1)
+    hipExtLaunchKernelGGL((gemm_fp4_kernel<1, 2>), dim3(grid), dim3(kThreads), 0, s, ev.start, ev.stop, 0, a);
+  else if (deep)
+    hipExtLaunchKernelGGL((gemm_fp4_kernel<2, 3>), dim3(grid), dim3(kThreads), 0, s, ev.start, ev.stop, 0, a);
   else
-    hipExtLaunchKernelGGL(gemm_fp4_kernel<2>, dim3(grid), dim3(kThreads), 0, s, ev.start, ev.stop, 0, a);
+    hipExtLaunchKernelGGL((gemm_fp4_kernel<2, 2>), dim3(grid), dim3(kThreads), 0, s, ev.start, ev.stop, 0, a);
   return hipGetLastError();
 }
 

@@ -210,8 +210,8 @@ size_t gemm_fp4_lds_bytes(int K);
 int gemm_fp4_resident_wgs(int K);
 hipError_t launch_gemm_fp4(const GemmArgs& a, int role, int grid, hipStream_t s, KernelEvents ev = {});
 // Weight scales [rows, K/16] UE4M3 (rows a multiple of 16) into the FP4
-// GEMM's layout: per 16-row group and 256-value step, 64 lanes x 4 bytes
-// (dst holds as many bytes as src).
+// GEMM's layout: per 16-row group and 256-value step, the step's 16 scale
+// groups x the 16 rows' bytes (dst holds as many bytes as src).
 hipError_t launch_reorder_fp4_scales(const uint8_t* src, uint8_t* dst, size_t rows, int K, hipStream_t s);
 hipError_t launch_codec_check_fp4(const float* in, uint8_t* q, float* dq, int n, hipStream_t s);
 

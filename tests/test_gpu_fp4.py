@@ -221,6 +221,34 @@ def test_fp4_many_jobs():
     assert J > 1536 and plan["grid1"] >= J and plan["grid2"] >= J
 
 
+def test_fp4_long_k_many_jobs():
+    """GEMM1 of K = 4096 (three items in flight, three waves per SIMD, 768
+    resident workgroups) with more jobs than resident workgroups: token t's
+    logits favour experts 16t .. 16t + 15 of 1,024 (bias zero, so the
+    sigmoid decides), so each expert takes one route and there are 1,024
+    jobs."""
+    shape = TINY.with_(M=64, hidden=4096, inter=256, experts=1024, top_k=16, local_begin=0,
+                       local_count=1024)
+    inp = synth.make_inputs(shape, seed=38, device=DEV)
+    favour = (torch.arange(shape.M, device=DEV)[:, None] * 16 + torch.arange(16, device=DEV)) % shape.experts
+    inp.logits.scatter_add_(1, favour, torch.full((shape.M, 16), 20.0, device=DEV, dtype=inp.logits.dtype))
+    inp.bias.zero_()
+    moe = make_fp4(inp)
+    plan = moe.plan(shape.M)
+    ref, _ = check_fp4_layer(moe, inp, stages=False)
+    check_jobs(moe, shape, ref["ids"])
+    J = int(stage(moe, "ctrl", 3, torch.int32).cpu().numpy()[2])
+    assert J == 1024 and plan["grid1"] >= J and plan["grid2"] >= J
+
+
+def test_fp4_long_k_gemm2():
+    """GEMM2 of K = 4096 (three items in flight) with its slot bookkeeping,
+    stages checked."""
+    shape = TINY.with_(M=3, hidden=512, inter=4096, experts=8, top_k=3, local_begin=0, local_count=8)
+    inp = synth.make_inputs(shape, seed=39, device=DEV)
+    check_fp4_layer(make_fp4(inp), inp)
+
+
 def test_fp4_exact_grid_case():
     """x on the E2M1 grid with a +-6 in every 16-block (every staged scale
     exactly 1) and power-of-two weight scales: every GEMM1 sum is exact in
