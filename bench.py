@@ -45,7 +45,7 @@ GEMM1_TRAFFIC = [
                  "fp8_block_scaled_moe_amd/csrc/route_device.h",
                  "fp8_block_scaled_moe_amd/csrc/kernels.h",
                  "fp8_block_scaled_moe_amd/csrc/capi.hip"],  # the plan (K parts, grids)
-     "sources_sha256_16": "53f74abbcc88435e",
+     "sources_sha256_16": "cad3e4c085a37aec",
      "workload": "dsv3", "M": 4, "seed": 0, "unique_experts": 27,
      # medians per dispatch (KiB) and the copy kernel's reading of 256 MiB
      "fetch_kib": 387990.5, "write_kib": 512.0, "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0},
@@ -56,9 +56,9 @@ GEMM1_TRAFFIC = [
                  "fp8_block_scaled_moe_amd/csrc/device_common.h",
                  "fp8_block_scaled_moe_amd/csrc/kernels.h",
                  "fp8_block_scaled_moe_amd/csrc/capi.hip"],
-     "sources_sha256_16": "dd531656c61de1e8",
+     "sources_sha256_16": "b87e965d14ef94d3",
      "workload": "fp4_share", "M": 16, "seed": 0, "unique_experts": 4,
-     "fetch_kib": 50262.41, "write_kib": 604.38, "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0},
+     "fetch_kib": 49131.38, "write_kib": 342.0, "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0},
 ]
 
 

@@ -36,6 +36,9 @@ CASES = {
     "dsv3_m16": (DSV3_32.with_(M=16), {}),
     "combine_in_gemm2": (DSV3_32, dict(launch_mode="combine_in_gemm2")),
     "swiglu_in_gemm1": (DSV3_32, dict(launch_mode="swiglu_in_gemm1")),
+    # routing inside the GEMM1 launch: the default at one token, asked for at two
+    "route_in_gemm1_m1": (DSV3_32.with_(M=1), {}),
+    "route_in_gemm1_m2": (DSV3_32.with_(M=2), dict(launch_mode="route_in_gemm1")),
     "shared_expert": (synth.CONFIGS["tiny"].with_(M=5, hidden=512, inter=256, experts=12, top_k=3,
                                                   shared_inter=384), {}),
     "fp4_share": (synth.CONFIGS["fp4_share"].with_(M=5, hidden=512, inter=256, experts=24, top_k=3,
