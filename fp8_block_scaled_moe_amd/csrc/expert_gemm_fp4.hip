@@ -267,7 +267,8 @@ __global__ __launch_bounds__(kThreads) void gemm_fp4_kernel(GemmArgs args) {
           acc[r][i] = v;
         }
         if (blk == 0 && x < (first ? nr0 : nr1)) {
-          float* dst = a.part + ((size_t)slot * a.R + (first ? rt0 : rt1)) * a.N + c.tile * kRowsPerWg + wave * 16 + 4 * r;
+          float* dst = a.part + ((size_t)slot * a.R + (first ? rt0 : rt1)) * a.N + c.tile * kRowsPerWg +
+                       wave * 16 + 4 * r;
           *reinterpret_cast<float4_t*>(dst) = acc[r];
         }
         acc[r] = float4_t{0.f, 0.f, 0.f, 0.f};

@@ -403,9 +403,10 @@ __device__ __forceinline__ RouteLds carve_route(unsigned char* p, int nkb) {
 // the other waves quantise x's 128-blocks (eight lanes per block); with
 // one token the picking wave lists the jobs right away, with two wave 0
 // groups the routes after a barrier. Workgroup 0 also writes the picks,
-// weights, expert-ordered buckets, codes and scales to device memory. Expert e of a token sits in
-// lane e % 64, slot e / 64 (E <= 64 kPer, M * E * 8 bytes within the weight
-// tiles' space, M * k <= 64: checked by the host). Contains barriers.
+// weights, expert-ordered buckets, codes and scales to device memory.
+// Expert e of a token sits in lane e % 64, slot e / 64 (E <= 64 kPer,
+// M * E * 8 bytes within the weight tiles' space, M * k <= 64: checked by
+// the host). Contains barriers.
 template <int kPer>
 __device__ void route_prologue(const RouteFuse& f, const GemmProblem& a, unsigned char* keys_lds, const RouteLds& l) {
   constexpr int kWaves = kThreads / kWave;
