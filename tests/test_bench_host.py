@@ -24,7 +24,7 @@ def test_more_than_one_gpu_exits_with_a_message():
 
 def test_traffic_follows_the_sources(monkeypatch, tmp_path):
     src = tmp_path / "kernel.hip"
-    src.write_text("// kernel\n")
+    src.write_text("// kernel\n__global__ void k(int* p) { p[0] = 1; }\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     entry = {"sources": ["kernel.hip"], "sources_sha256_16": bench.sources_hash(["kernel.hip"]),
              "workload": "w", "M": 4, "seed": 0, "unique_experts": 3,
@@ -34,5 +34,8 @@ def test_traffic_follows_the_sources(monkeypatch, tmp_path):
     assert bench.gemm1_traffic("w", 4, 0, 3) == (2000 + 10) * 1024
     assert bench.gemm1_traffic("w", 8, 0, 3) is None      # another token count
     assert bench.gemm1_traffic("w", 4, 0, 4) is None      # other experts touched
-    src.write_text("// kernel, changed\n")
-    assert bench.gemm1_traffic("w", 4, 0, 3) is None      # sources changed since the counters
+    # comments and layout do not count: the compiled kernel is the same
+    src.write_text("/* the kernel */\n__global__ void k(int* p)\n{\n  p[0] = 1;  // store\n}\n")
+    assert bench.gemm1_traffic("w", 4, 0, 3) == (2000 + 10) * 1024
+    src.write_text("// kernel\n__global__ void k(int* p) { p[0] = 2; }\n")
+    assert bench.gemm1_traffic("w", 4, 0, 3) is None      # code changed since the counters
