@@ -422,17 +422,15 @@ __device__ void route_prologue(const RouteFuse& f, const GemmProblem& a, unsigne
 
   // every load first: the logits and bias of this thread's pairs, and (waves
   // past the picking ones) the BF16 values of the thread's group's blocks
+  // (pairs past M * E load the last one and are not kept)
+  int at[kS];
   float z[kS], bias[kS];
 #pragma unroll
   for (int q = 0; q < kS; ++q) {
-    const int i = tid + q * kThreads;
-    z[q] = 0.f;
-    bias[q] = 0.f;
-    if (i < M * E) {
-      z[q] = router_logit(f.logits, f.logits_bf16, E, i / E, i % E);
-      bias[q] = f.bias[i % E];
-    }
+    at[q] = min(tid + q * kThreads, M * E - 1);
+    bias[q] = f.bias[at[q] % E];
   }
+  load_logits<kS>(f.logits, f.logits_bf16, at, z);
   // quantising waves only: group grp in [0, groups) takes blocks grp,
   // grp + groups, ... of the M * nkb
   const bool quant = wave >= M;

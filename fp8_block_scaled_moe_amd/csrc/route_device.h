@@ -4,7 +4,7 @@
 //
 // Routing follows the vLLM "mega_moe" page (top_k_pick, _ordered): FP32
 // sigmoid scores, FP32 keys score + bias compared through a monotone integer
-// image, top_k rounds of a wave-wide maximum with ties to the lower expert,
+// image, the top_k largest keys in order with ties to the lower expert,
 // weights = picked score / (FP32 sum of picked scores in pick order) * scale.
 // The activation quantiser is the same page's epilogue: per 128 values,
 // scale = max(amax, 1e-10) / 448 (IEEE divide), optionally rounded up to a
@@ -29,10 +29,21 @@ __device__ __forceinline__ float sigmoid_f32(float z) {
   return (float)(1.0 / (1.0 + exp(-(double)z)));
 }
 
-// Logit of expert e for token t ([M, E] f32 or bf16).
-__device__ __forceinline__ float router_logit(const void* logits, int bf16, int E, int t, int e) {
-  const size_t at = (size_t)t * E + e;
-  return bf16 ? bf16_value(((const uint16_t*)logits)[at]) : ((const float*)logits)[at];
+// Router logits ([M, E] f32 or bf16) at flat indices at[q] (each in
+// bounds), as FP32. Every load is issued before any value is widened, so a
+// thread waits for memory once, not once per logit.
+template <int kN>
+__device__ __forceinline__ void load_logits(const void* logits, int bf16, const int (&at)[kN], float (&z)[kN]) {
+  uint32_t raw[kN];
+  if (bf16) {
+#pragma unroll
+    for (int q = 0; q < kN; ++q) raw[q] = ((const uint16_t*)logits)[at[q]];
+  } else {
+#pragma unroll
+    for (int q = 0; q < kN; ++q) raw[q] = ((const uint32_t*)logits)[at[q]];
+  }
+#pragma unroll
+  for (int q = 0; q < kN; ++q) z[q] = __uint_as_float(bf16 ? raw[q] << 16 : raw[q]);
 }
 
 // Wave-wide maximum of a uint32: DPP permutations inside each row of 16
@@ -50,20 +61,17 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return max(max(a, b), max(c, d));
 }
 
-// One wave: the k picks of a token. Lane l holds experts l + 64 j (j < kPer,
-// e < E): key[j] (the ordered image of score + bias; 0 past E) and
-// score[j]. A round takes the largest remaining key and, among equal keys,
-// the lowest expert: a wave maximum of the keys, then the first lane, in
-// expert order, whose remaining key equals it (one compare-ballot per slot,
-// lowest slot winning: expert l + 64 j grows with j before l). A pick's key
-// becomes 0 and its lane leaves the slot's `open` mask, so the maximum needs
-// no mask (every key is >= 0) and a later round whose maximum is 0 still
-// skips it. The pick's score joins the FP32 total in pick order. Lane
-// r < k returns the r-th pick and its score; every lane returns the total.
-// key[] is consumed.
+// Selection by rounds (few experts per lane): a round takes the largest
+// remaining key and, among equal keys, the lowest expert: a wave maximum of
+// the keys, then the first lane, in expert order, whose remaining key equals
+// it (one compare-ballot per slot, lowest slot winning: expert l + 64 j
+// grows with j before l). A pick's key becomes 0 and its lane leaves the
+// slot's `open` mask, so the maximum needs no mask (every key is >= 0) and a
+// later round whose maximum is 0 still skips it. kv[] (0 past E) is
+// consumed.
 template <int kPer>
-__device__ __forceinline__ void pick_top_k(uint32_t (&key)[kPer], const float (&score)[kPer], int E, int k, int lane,
-                                           int& id, float& s_mine, float& total) {
+__device__ __forceinline__ void pick_by_rounds(uint32_t (&kv)[kPer], const float (&score)[kPer], int E, int k,
+                                               int lane, int& id, float& s_mine, float& total) {
   uint64_t open[kPer];  // lanes whose slot j holds an expert not yet picked
 #pragma unroll
   for (int j = 0; j < kPer; ++j) open[j] = __ballot(lane + kWave * j < E);
@@ -71,14 +79,14 @@ __device__ __forceinline__ void pick_top_k(uint32_t (&key)[kPer], const float (&
   id = 0;
   s_mine = 0.f;
   for (int r = 0; r < k; ++r) {
-    uint32_t m = key[0];
+    uint32_t m = kv[0];
 #pragma unroll
-    for (int j = 1; j < kPer; ++j) m = max(m, key[j]);
+    for (int j = 1; j < kPer; ++j) m = max(m, kv[j]);
     m = wave_max_u32(m);
     int winner = 0;
 #pragma unroll
     for (int j = kPer - 1; j >= 0; --j) {  // the lowest slot with a hit is kept
-      const uint64_t hit = __ballot(key[j] == m) & open[j];
+      const uint64_t hit = __ballot(kv[j] == m) & open[j];
       winner = hit ? kWave * j + (int)__builtin_ctzll(hit) : winner;
     }
     const int owner = winner & (kWave - 1), slot = winner / kWave;
@@ -88,7 +96,7 @@ __device__ __forceinline__ void pick_top_k(uint32_t (&key)[kPer], const float (&
       if (j == slot) {
         s_slot = score[j];
         open[j] &= ~(1ull << owner);
-        if (lane == owner) key[j] = 0;
+        if (lane == owner) kv[j] = 0;
       }
     }
     const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_slot), owner));
@@ -98,6 +106,109 @@ __device__ __forceinline__ void pick_top_k(uint32_t (&key)[kPer], const float (&
       s_mine = s;
     }
   }
+}
+
+// Selection by a threshold (many experts per lane), the same picks in the
+// same order:
+// 1. A threshold T, one bit at a time from the top: T | bit is kept while at
+//    least k keys reach it (a ballot and a popcount per slot). The search
+//    stops as soon as exactly k keys reach T: those are the picks. Slots past
+//    E hold key 0, which no candidate (>= 1) counts.
+// 2. If it ran through all bits with more than k keys at T, T is the k-th
+//    largest key: every key above T is a pick, and the lowest experts with
+//    key T make up the rest (experts ascend with the slot, then the lane).
+// 3. The picks go to lanes 0..k-1 in expert order (scalar bit scans of the
+//    slot ballots, lane reads and selects).
+// 4. Each lane counts the picks before its own, an earlier pick having the
+//    larger key or the same key and the lower expert; the ranks are a
+//    permutation, and one lane permute puts pick r in lane r.
+// Its cost grows with the bits searched (times kPer) rather than with k
+// rounds of dependent wave-wide steps. Measured on MI355X: faster than the
+// rounds at 16 experts per lane and 16 picks, slower at 4 per lane and 8
+// picks and at 8 per lane and 6 picks.
+template <int kPer>
+__device__ __forceinline__ void pick_by_threshold(const uint32_t (&kv)[kPer], const float (&score)[kPer], int E, int k,
+                                                  int lane, int& id, float& s_mine, float& total) {
+  uint32_t T = 0;
+  int n_ge = E;  // experts whose key reaches T
+  for (int b = 31; b >= 0 && n_ge != k; --b) {
+    const uint32_t c = T | (1u << b);
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) n += __popcll(__ballot(kv[j] >= c));
+    if (n >= k) {
+      T = c;
+      n_ge = n;
+    }
+  }
+
+  uint64_t sel[kPer];
+  if (n_ge == k) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) sel[j] = __ballot(lane + kWave * j < E && kv[j] >= T);
+  } else {
+    int need = k;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      sel[j] = __ballot(kv[j] > T);
+      need -= __popcll(sel[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      uint64_t tie = __ballot(lane + kWave * j < E && kv[j] == T);
+      for (; need > 0 && tie != 0; --need) {
+        const uint64_t low = tie & (~tie + 1ull);
+        sel[j] |= low;
+        tie ^= low;
+      }
+    }
+  }
+
+  int pk = 0, pe = 0, ps = 0;  // this lane's pick (lanes below k): key, expert, score bits
+  int pos = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    for (uint64_t m = sel[j]; m != 0; m &= m - 1ull, ++pos) {
+      const int l = (int)__builtin_ctzll(m);
+      const int kl = __builtin_amdgcn_readlane((int)kv[j], l);
+      const int sl = __builtin_amdgcn_readlane(__float_as_int(score[j]), l);
+      const bool here = lane == pos;
+      pk = here ? kl : pk;
+      ps = here ? sl : ps;
+      pe = here ? l + kWave * j : pe;
+    }
+  }
+
+  const uint64_t mine = ((uint64_t)(uint32_t)pk << 32) | (uint32_t)~pe;
+  int rank = 0;
+  for (int q = 0; q < k; ++q) {
+    const uint64_t other = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(pk, q) << 32) |
+                           (uint32_t)~__builtin_amdgcn_readlane(pe, q);
+    rank += other > mine ? 1 : 0;
+  }
+  const int to = (lane < k ? rank : lane) * 4;
+  id = __builtin_amdgcn_ds_permute(to, pe);
+  s_mine = __int_as_float(__builtin_amdgcn_ds_permute(to, ps));
+  total = 0.f;
+  for (int r = 0; r < k; ++r) total = total + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_mine), r));
+}
+
+// One wave: the k picks of a token (k <= E, k <= 64). Lane l holds experts
+// l + 64 j (j < kPer, e < E): key[j] (the ordered image of score + bias)
+// and score[j]. The picks are the k largest keys, equal keys ordered by
+// expert (lower first), and come out in that order. Lane r < k returns the
+// r-th pick and its score, the other lanes 0 and 0; every lane returns the
+// FP32 sum of the picked scores taken in pick order.
+template <int kPer>
+__device__ __forceinline__ void pick_top_k(const uint32_t (&key)[kPer], const float (&score)[kPer], int E, int k,
+                                           int lane, int& id, float& s_mine, float& total) {
+  uint32_t kv[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) kv[j] = lane + kWave * j < E ? key[j] : 0u;
+  if constexpr (kPer >= 16)
+    pick_by_threshold<kPer>(kv, score, E, k, lane, id, s_mine, total);
+  else
+    pick_by_rounds<kPer>(kv, score, E, k, lane, id, s_mine, total);
 }
 
 // Routing weight of a pick: its score over the picks' total, times the

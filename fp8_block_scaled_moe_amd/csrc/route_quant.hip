@@ -47,17 +47,21 @@ inline int quant_wgs(int M, int H) {
 // l + 64 j for j < kPer (kPer >= E / 64).
 template <int kPer>
 __device__ void route_token(const RouteQuantArgs& a, int t, int lane, int* ids_l) {
-  float score[kPer];
+  // slots past E load expert E - 1 and are never opened
+  int at[kPer];
+  float z[kPer], bias[kPer], score[kPer];
   uint32_t key[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    score[j] = 0.f;
-    key[j] = 0;
-    const int e = lane + kWave * j;
-    if (e < a.E) {
-      score[j] = sigmoid_f32(router_logit(a.logits, a.logits_bf16, a.E, t, e));
-      key[j] = ordered_key(score[j] + a.bias[e]);
-    }
+    const int e = min(lane + kWave * j, a.E - 1);
+    at[j] = t * a.E + e;
+    bias[j] = a.bias[e];
+  }
+  load_logits<kPer>(a.logits, a.logits_bf16, at, z);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    score[j] = sigmoid_f32(z[j]);
+    key[j] = ordered_key(score[j] + bias[j]);
   }
   int my_id;
   float my_score, total;
