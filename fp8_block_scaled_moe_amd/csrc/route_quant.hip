@@ -20,22 +20,25 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;  // 16
-// Tokens per workgroup, one routing wave each, one per SIMD: routing is
-// VALU-issue bound (FP64 sigmoid, DPP maxima), so two routing waves
-// on a SIMD take twice as long (measured on MI355X at M = 8: 11.6 us as two
-// workgroups against 13.0 us as one). Up to 4 tokens run in one workgroup
-// (no cross-workgroup handoff); more run 2 to a workgroup: on one GPU's FP4
-// share (M = 16, E = 384, top-6) the kernel took 17.0 us at 4 tokens per
-// workgroup and 13.6 us at 2, and the DeepSeek-V3 shapes at M = 8..64 were
-// even (measured on MI355X).
-constexpr int kTokensPerWg = 4;
+// Tokens per workgroup, one routing wave each. Up to 16 tokens are routed
+// in one workgroup, so no handoff between workgroups is needed (4 slots at
+// M <= 4, the other 12 waves quantising). A routing wave's selection is a
+// chain of dependent cross-lane steps, so waves sharing a SIMD overlap
+// well: on MI355X the kernel took 6.2 us at DeepSeek-V3 shapes with M = 8
+// in one workgroup against 9.0 us over four, and 10.1 against 12.1 us at
+// M = 16. Past 16 tokens they run 2 to a workgroup and the last workgroup
+// to arrive groups the routes.
+constexpr int kTokensPerWgFew = 4;
+constexpr int kTokensPerWgOne = 16;  // all waves of a workgroup
 constexpr int kTokensPerWgMany = 2;
-__host__ __device__ inline int tokens_per_wg(int M) { return M <= kTokensPerWg ? kTokensPerWg : kTokensPerWgMany; }
+__host__ __device__ inline int tokens_per_wg(int M) {
+  return M <= kTokensPerWgFew ? kTokensPerWgFew : M <= kTokensPerWgOne ? M : kTokensPerWgMany;
+}
 __host__ __device__ inline int routing_wgs(int M) { return (M + tokens_per_wg(M) - 1) / tokens_per_wg(M); }
 // Workgroups that only quantise, launched after the routing ones when the
 // routing workgroups' quantising waves would take more than one 128-block
-// per eight lanes (at most 4 tokens on one workgroup, 56 blocks each at
-// H = 7168, against 96 groups of eight lanes).
+// per eight lanes (4 tokens on one workgroup: 56 blocks each at H = 7168,
+// against 96 groups of eight lanes).
 constexpr int kMaxQuantWgs = 16;
 inline int quant_wgs(int M, int H) {
   const int have = routing_wgs(M) * (kThreads - tokens_per_wg(M) * kWave) / 8;
@@ -133,31 +136,61 @@ __device__ void quant_blocks(const RouteQuantArgs& a, int group, int groups) {
 }
 
 struct Lds {
+  int* totals;     // [2 * kWaves] per-wave scan totals
   uint64_t* mask;  // [E][W] token bitmask of every expert
   int* ids;        // [M*k] picks
   int* first;      // [E] first route slot of each expert
-  int* jbase;      // [E] first job of each expert (FP4 form)
-  int* scratch;    // [3 * kWaves] per-wave scan totals
+  int* jbase;      // [E] first job of each expert
 };
 
 __device__ __forceinline__ Lds carve(unsigned char* lds, int E, int W, int R) {
   Lds l;
-  l.mask = reinterpret_cast<uint64_t*>(lds);
-  l.ids = reinterpret_cast<int*>(lds + (size_t)E * W * 8);
+  l.totals = reinterpret_cast<int*>(lds);  // first: read as 16-byte words
+  l.mask = reinterpret_cast<uint64_t*>(lds + 2 * kWaves * 4);
+  l.ids = reinterpret_cast<int*>(lds + 2 * kWaves * 4 + (size_t)E * W * 8);
   l.first = l.ids + R;
   l.jbase = l.first + E;
-  l.scratch = l.jbase + E;
   return l;
 }
 
+// Inclusive prefix sum over the lanes of a wave: shifts by 1, 2, 4 and 8
+// lanes inside each row of 16 (lanes with no source add nothing), then each
+// row adds the totals of the rows before it.
+__device__ __forceinline__ int wave_prefix_sum(int v, int lane) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+            r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = lane / 16;
+  return v + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
+
+// Routes of local expert e (its token mask's popcount).
+__device__ __forceinline__ int expert_routes(const Lds& l, int e, int W) {
+  int c = 0;
+  for (int w = 0; w < W; ++w) c += __popcll(l.mask[(size_t)e * W + w]);
+  return c;
+}
+
+// Jobs of an expert with c routes, at most jr routes each (none when jr = 0).
+__device__ __forceinline__ int expert_jobs(int c, int jr) { return jr > 0 ? (c + jr - 1) / jr : 0; }
+
 // Routes of the local experts grouped by expert (local index e - lb),
 // experts ascending, each expert's routes in ascending token order (so
-// ascending route index).
+// ascending route index). l.ids holds the picks and l.mask is zero.
+// 1. Token masks per expert in LDS.
+// 2. Thread e owns expert e (E <= 1024): its route count, presence and job
+//    count go through a prefix sum over the wave (presence and routes
+//    packed in one word: at most 1024 and 8192), the waves' totals through
+//    LDS (none with at most 64 experts: wave 0 alone), giving each expert
+//    its rank, first route slot and first job.
+// 3. Every route finds its slot from its expert's mask.
+// Every index written is checked against the buffers' sizes.
 __device__ void bucket_routes(const RouteQuantArgs& a, const Lds& l) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int E = a.lc, W = a.words, R = a.M * a.k;
-  for (int i = tid; i < E * W; i += kThreads) l.mask[i] = 0;
-  __syncthreads();
+  const int E = a.lc, W = a.words, R = a.M * a.k, jr = a.job_routes, ucap = min(E, R);
   for (int r = tid; r < R; r += kThreads) {
     const int t = r / a.k;
     const int e = l.ids[r] - a.lb;
@@ -165,58 +198,57 @@ __device__ void bucket_routes(const RouteQuantArgs& a, const Lds& l) {
       atomicOr(reinterpret_cast<unsigned long long*>(&l.mask[(size_t)e * W + t / 64]), 1ull << (t % 64));
   }
   __syncthreads();
-  // thread e owns expert e (E <= kThreads); block-wide exclusive scan of
-  // (present, count, jobs) gives each present expert its rank, first slot
-  // and first job
-  const int jr = a.job_routes;
-  int cnt = 0;
-  if (tid < E)
-    for (int w = 0; w < W; ++w) cnt += __popcll(l.mask[(size_t)tid * W + w]);
-  const int present = cnt > 0;
-  const int nj = jr > 0 ? (cnt + jr - 1) / jr : 0;
-  int inc_p = present, inc_r = cnt, inc_j = nj;
+  const bool one_wave = E <= kWave;  // then wave 0 alone, with no totals to exchange
+  if (!one_wave || wave == 0) {
+    const int cnt = tid < E ? expert_routes(l, tid, W) : 0;
+    const int present = cnt > 0 ? 1 : 0, nj = expert_jobs(cnt, jr);
+    constexpr int kShift = 11;  // presence in bits 0..10, routes above
+    const int ipr = wave_prefix_sum(present | (cnt << kShift), lane), ij = wave_prefix_sum(nj, lane);
+    int base_pr = 0, base_j = 0, all_pr = 0, all_j = 0;
+    if (one_wave) {
+      all_pr = __builtin_amdgcn_readlane(ipr, kWave - 1);
+      all_j = __builtin_amdgcn_readlane(ij, kWave - 1);
+    } else {
+      if (lane == kWave - 1) {
+        l.totals[wave] = ipr;
+        l.totals[kWaves + wave] = ij;
+      }
+      __syncthreads();
+      const int4* t4 = reinterpret_cast<const int4*>(l.totals);
+      int tot[2 * kWaves];
 #pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int up_p = __shfl_up(inc_p, o, kWave);
-    const int up_r = __shfl_up(inc_r, o, kWave);
-    const int up_j = __shfl_up(inc_j, o, kWave);
-    if (lane >= o) {
-      inc_p += up_p;
-      inc_r += up_r;
-      inc_j += up_j;
+      for (int q = 0; q < 2 * kWaves / 4; ++q) {
+        const int4 v = t4[q];
+        tot[4 * q] = v.x;
+        tot[4 * q + 1] = v.y;
+        tot[4 * q + 2] = v.z;
+        tot[4 * q + 3] = v.w;
+      }
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        base_pr += w < wave ? tot[w] : 0;
+        base_j += w < wave ? tot[kWaves + w] : 0;
+        all_pr += tot[w];
+        all_j += tot[kWaves + w];
+      }
     }
-  }
-  if (lane == kWave - 1) {
-    l.scratch[wave] = inc_p;
-    l.scratch[kWaves + wave] = inc_r;
-    l.scratch[2 * kWaves + wave] = inc_j;
-  }
-  __syncthreads();
-  int base_p = 0, base_r = 0, base_j = 0, all_p = 0, all_j = 0;
-  for (int w = 0; w < kWaves; ++w) {
-    const int tp = l.scratch[w], tr = l.scratch[kWaves + w], tj = l.scratch[2 * kWaves + w];
-    if (w < wave) {
-      base_p += tp;
-      base_r += tr;
-      base_j += tj;
+    if (present) {
+      const int pr = base_pr + ipr;
+      const int u = (pr & ((1 << kShift) - 1)) - 1, o = (pr >> kShift) - cnt, jb = base_j + ij - nj;
+      if (u < ucap) {
+        a.b.uexp[u] = tid;
+        a.b.uoff[u] = o;
+        a.b.ucnt[u] = cnt;
+      }
+      l.first[tid] = o;
+      l.jbase[tid] = jb;
+      for (int q = 0; q < nj; ++q)
+        if (jb + q < R) a.b.jobs[jb + q] = make_int4(tid, o + q * jr, min(jr, cnt - q * jr), 0);
     }
-    all_p += tp;
-    all_j += tj;
-  }
-  if (present) {
-    const int u = base_p + inc_p - 1;
-    const int o = base_r + inc_r - cnt;
-    const int jb = base_j + inc_j - nj;
-    a.b.uexp[u] = tid;
-    a.b.uoff[u] = o;
-    a.b.ucnt[u] = cnt;
-    l.first[tid] = o;
-    l.jbase[tid] = jb;
-    for (int p = 0; p < nj; ++p) a.b.jobs[jb + p] = make_int4(tid, o + p * jr, min(jr, cnt - p * jr), 0);
-  }
-  if (tid == 0) {
-    a.b.ctrl[1] = all_p;
-    a.b.ctrl[2] = all_j;
+    if (tid == 0) {
+      a.b.ctrl[1] = min(all_pr & ((1 << kShift) - 1), ucap);
+      a.b.ctrl[2] = min(all_j, R);
+    }
   }
   __syncthreads();
   for (int r = tid; r < R; r += kThreads) {
@@ -227,7 +259,8 @@ __device__ void bucket_routes(const RouteQuantArgs& a, const Lds& l) {
     int before = 0;
     for (int w = 0; w < t / 64; ++w) before += __popcll(m[w]);
     before += __popcll(m[t / 64] & ((1ull << (t % 64)) - 1ull));
-    a.b.routes[l.first[e] + before] = r;
+    const int slot = l.first[e] + before;
+    if (slot < R) a.b.routes[slot] = r;
     if (jr > 0) a.b.rjob[r] = l.jbase[e] + before / jr;
   }
 }
@@ -252,6 +285,8 @@ __global__ __launch_bounds__(kThreads) void route_quant_kernel(RouteQuantArgs a)
   const int tpw = tokens_per_wg(a.M);
   const int gr = routing_wgs(a.M);
   const bool routing = (int)blockIdx.x < gr;
+  if (routing && a.M * a.k > kWave)  // the token masks of the grouping (read after a barrier)
+    for (int i = threadIdx.x; i < a.lc * a.words; i += kThreads) l.mask[i] = 0;
   // the routing waves (one per token) and the quantising waves run side by
   // side; the quantising waves of every workgroup share out the blocks
   if (routing && wave < tpw) {
@@ -305,7 +340,7 @@ __global__ void codec_check_kernel(const float* in, uint8_t* q, float* dq, int n
 }  // namespace
 
 size_t route_quant_lds_bytes(int E, int words, int routes) {
-  return (size_t)E * words * 8 + (size_t)routes * 4 + (size_t)E * 8 + 3 * kWaves * 4;
+  return (size_t)E * words * 8 + (size_t)routes * 4 + (size_t)E * 8 + 2 * kWaves * 4;
 }
 
 hipError_t launch_route_quant(const RouteQuantArgs& a, hipStream_t s, KernelEvents ev) {
