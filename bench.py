@@ -46,7 +46,7 @@ GEMM1_TRAFFIC = [
                  "fp8_block_scaled_moe_amd/csrc/route_device.h",
                  "fp8_block_scaled_moe_amd/csrc/kernels.h",
                  "fp8_block_scaled_moe_amd/csrc/capi.hip"],  # the plan (K parts, grids)
-     "sources_sha256_16": "5b2b8623fc872c38",
+     "sources_sha256_16": "48844a35fce297ae",
      "workload": "dsv3", "M": 4, "seed": 0, "unique_experts": 27,
      # medians per dispatch (KiB) and the copy kernel's reading of 256 MiB
      "fetch_kib": 387990.5, "write_kib": 512.0, "copy_fetch_kib": 131175.0, "copy_write_kib": 262144.0},
